@@ -1,0 +1,294 @@
+"""Seeded synthetic workloads for the block-draft round.
+
+This module only draws random inputs: it holds none of the projection,
+attention or verification arithmetic, so both the CPU oracle and the HIP path
+can consume its arrays without sharing any of the method's code.
+
+Every tensor comes from NumPy's PCG64 through ``SeedSequence(seed).spawn``;
+each named stream below is one child, in the fixed order of ``STREAMS``.
+bf16 tensors are drawn in fp32 and rounded to bf16 (round to nearest even);
+they are returned both as raw ``uint16`` bits and as the exactly equal fp32
+values.
+
+The shapes mirror the workloads on the pages: a block of 16 = 1 known anchor
+plus 15 drafted positions, five target layers concatenated into ``H_target``,
+an 8192-token sliding window for the 27B drafter (Tencent DSpine article,
+"what these weights are"), concurrency 32 for the 8B drafter (DFlash / Spec V2
+blog, A7) and temperature 1 / top-k 20 / top-p 0.95 sampling (DSpine article,
+"speed-up"). The pages' public evaluation sets and trained weights are not
+used: synthetic Gaussian data of the same shapes stands in for them.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from typing import Dict, Optional
+
+import numpy as np
+
+STREAMS = (
+    "ctx_len",      # per-request context lengths
+    "h_ctx",        # hidden states of the context (prefill fill of the caches)
+    "h_round",      # hidden states of the B*K rows injected this round
+    "w_kv",         # layer-batched projection weights
+    "k_norm_w",     # per-layer RMSNorm gains of K
+    "q",            # drafter queries of the block
+    "kv_blk",       # in-block keys and values
+    "z_draft",      # draft logits
+    "z_noise",      # target = draft + sigma * noise
+    "z_bonus",      # the extra target row (no draft counterpart)
+    "draft_pick",   # drafter's own sampling noise (Gumbel) for draft tokens
+    "uniforms",     # verification uniforms [B, G+1, 2]
+)
+
+
+@dataclass(frozen=True)
+class Config:
+    """One workload. K counts the anchor, so G = K - 1 drafted tokens."""
+
+    name: str
+    B: int
+    K: int
+    L: int
+    n_q: int
+    n_kv: int
+    hd: int
+    d_in: int
+    V: int
+    ctx_kind: str            # "fixed" | "uniform" | "lognormal"
+    ctx_a: int               # fixed length / lower bound / median
+    ctx_b: int = 0           # upper bound (uniform, lognormal clip)
+    ctx_lo: int = 0          # lower clip (lognormal)
+    ctx_logsigma: float = 1.0
+    window: int = 0          # 0 = whole context
+    temperature: float = 0.0  # 0 = greedy
+    top_k: int = 0
+    top_p: float = 1.0
+    sigma: float = 1.0        # target = draft + sigma * N(0, 1)
+    sigma_odd: Optional[float] = None  # second regime for odd requests
+    h_bf16: bool = True       # H drawn as bf16 (else fp32 rounded at the boundary)
+    rope_theta: float = 1e6
+    rms_eps: float = 1e-6
+    w_std: float = 0.02
+
+    @property
+    def G(self) -> int:
+        return self.K - 1
+
+    @property
+    def n_out(self) -> int:
+        return self.L * 2 * self.n_kv * self.hd
+
+    @property
+    def group(self) -> int:
+        return self.n_q // self.n_kv
+
+
+# sigma for the greedy 4B / 27B shapes: chosen so that the first-position
+# greedy agreement is about 0.84 at V = 151936, which gives a mean accepted
+# length of about 5 over 15 drafted positions (independent positions).
+SIGMA_TAU5 = 0.066
+
+CONFIGS: Dict[str, Config] = {
+    "tiny": Config("tiny", B=1, K=8, L=2, n_q=4, n_kv=2, hd=64, d_in=768, V=4096,
+                   ctx_kind="fixed", ctx_a=512, sigma=0.5, h_bf16=False),
+    "qwen3-4b": Config("qwen3-4b", B=1, K=16, L=5, n_q=32, n_kv=8, hd=128, d_in=12800,
+                       V=151936, ctx_kind="fixed", ctx_a=4096, sigma=SIGMA_TAU5),
+    "qwen3-8b": Config("qwen3-8b", B=32, K=16, L=5, n_q=32, n_kv=8, hd=128, d_in=20480,
+                       V=151936, ctx_kind="uniform", ctx_a=512, ctx_b=4096,
+                       temperature=1.0, sigma=1.0),
+    "27b-long": Config("27b-long", B=8, K=16, L=5, n_q=40, n_kv=8, hd=128, d_in=25600,
+                       V=151936, ctx_kind="fixed", ctx_a=32768, window=8192,
+                       sigma=SIGMA_TAU5),
+    "sweep-b128": Config("sweep-b128", B=128, K=16, L=5, n_q=32, n_kv=8, hd=128, d_in=20480,
+                         V=151936, ctx_kind="lognormal", ctx_a=2048, ctx_lo=256,
+                         ctx_b=16384, ctx_logsigma=1.0, temperature=1.0, top_k=20,
+                         top_p=0.95, sigma=0.3, sigma_odd=2.0),
+}
+CONFIG_ORDER = ("tiny", "qwen3-4b", "qwen3-8b", "27b-long", "sweep-b128")
+
+
+def streams(seed: int = 0) -> Dict[str, np.random.Generator]:
+    """One independent PCG64 generator per named stream."""
+    kids = np.random.SeedSequence(seed).spawn(len(STREAMS))
+    return {name: np.random.Generator(np.random.PCG64(k)) for name, k in zip(STREAMS, kids)}
+
+
+# ----------------------------------------------------------------------------
+# fp32 -> bf16 bits (round to nearest, ties to even) for drawing inputs.
+# ----------------------------------------------------------------------------
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (b >> np.uint32(16)) & np.uint32(1)
+    r = ((b + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(np.ascontiguousarray(x, dtype=np.float32))
+    if nan.any():
+        r[nan] = np.uint16(0x7FC0)
+    return r
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_normal(rng: np.random.Generator, shape, std: float = 1.0):
+    """(bits, values) of a bf16 tensor drawn from N(0, std^2)."""
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    bits = to_bf16_bits(x)
+    return bits, bf16_bits_to_f32(bits)
+
+
+# ----------------------------------------------------------------------------
+# Generators
+# ----------------------------------------------------------------------------
+def ctx_lengths(cfg: Config, rng: np.random.Generator) -> np.ndarray:
+    if cfg.ctx_kind == "fixed":
+        return np.full(cfg.B, cfg.ctx_a, dtype=np.int32)
+    if cfg.ctx_kind == "uniform":
+        return rng.integers(cfg.ctx_a, cfg.ctx_b + 1, size=cfg.B).astype(np.int32)
+    if cfg.ctx_kind == "lognormal":
+        x = rng.lognormal(mean=np.log(cfg.ctx_a), sigma=cfg.ctx_logsigma, size=cfg.B)
+        return np.clip(np.rint(x), cfg.ctx_lo, cfg.ctx_b).astype(np.int32)
+    raise ValueError(cfg.ctx_kind)
+
+
+def cache_layout(ctx_len: np.ndarray, K: int, window: int = 0):
+    """Ragged cache slots: request b owns ``ctx_len[b] + K`` consecutive slots
+    starting at ``cache_base[b]`` (position p lives at slot cache_base[b] + p).
+    Returns (cache_base int64 [B], T_cap)."""
+    span = ctx_len.astype(np.int64) + K
+    base = np.zeros(len(ctx_len), dtype=np.int64)
+    if len(ctx_len) > 1:
+        base[1:] = np.cumsum(span)[:-1]
+    return base, int(span.sum())
+
+
+@dataclass
+class RoundInputs:
+    """Everything one round consumes, as host arrays (bf16 as uint16 bits)."""
+
+    cfg: Config
+    ctx_len: np.ndarray            # int32 [B]
+    cache_base: np.ndarray         # int64 [B]
+    T_cap: int
+    h_round_bits: np.ndarray       # uint16 [B*K, d_in]
+    w_bits: np.ndarray             # uint16 [N_out, d_in]
+    k_norm_bits: np.ndarray        # uint16 [L, hd]
+    q_bits: np.ndarray             # uint16 [L, B, K, n_q, hd]
+    k_blk_bits: np.ndarray         # uint16 [L, B, K, n_kv, hd]
+    v_blk_bits: np.ndarray         # uint16 [L, B, K, n_kv, hd]
+    z_target: np.ndarray           # fp32 [B, G+1, V]
+    z_draft: Optional[np.ndarray]  # fp32 [B, G, V] or None (greedy)
+    draft_tokens: np.ndarray       # int32 [B, G]
+    uniforms: np.ndarray           # fp32 [B, G+1, 2]
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def row_cu(self) -> np.ndarray:
+        return (np.arange(self.cfg.B + 1, dtype=np.int32) * self.cfg.K).astype(np.int32)
+
+    @property
+    def row_pos0(self) -> np.ndarray:
+        """This round's rows sit at positions ctx_len .. ctx_len + K - 1."""
+        return self.ctx_len.astype(np.int32)
+
+
+def logits(cfg: Config, st, B: Optional[int] = None, V: Optional[int] = None):
+    """Draft logits N(0,1); target = draft + sigma_b * N(0,1) for the G drafted
+    positions; the extra (bonus) target row is a fresh N(0,1) row plus the same
+    noise. Returns (z_target [B,G+1,V], z_draft [B,G,V]) in fp32."""
+    B = cfg.B if B is None else B
+    V = cfg.V if V is None else V
+    G = cfg.G
+    zd = st["z_draft"].standard_normal((B, G, V), dtype=np.float32)
+    noise = st["z_noise"].standard_normal((B, G + 1, V), dtype=np.float32)
+    bonus = st["z_bonus"].standard_normal((B, 1, V), dtype=np.float32)
+    sig = np.full((B, 1, 1), cfg.sigma, dtype=np.float32)
+    if cfg.sigma_odd is not None:
+        sig[1::2] = np.float32(cfg.sigma_odd)
+    zt = np.empty((B, G + 1, V), dtype=np.float32)
+    zt[:, :G] = zd + sig * noise[:, :G]
+    zt[:, G:] = bonus + sig * noise[:, G:]
+    return zt, zd
+
+
+def draft_tokens(cfg: Config, zd: np.ndarray, st) -> np.ndarray:
+    """The drafter's own choice of tokens (outside the verified path).
+
+    Greedy drafters take the lowest-index maximum of their logits. Sampling
+    drafters draw with the Gumbel-max rule over their logits at the
+    temperature; with a top-k filter the draw is restricted to the k largest
+    logits (the drafter's filter; the verifier applies its own filters)."""
+    B, G, V = zd.shape
+    if cfg.temperature == 0.0:
+        return np.argmax(zd, axis=-1).astype(np.int32)
+    gum = st["draft_pick"].gumbel(size=(B, G, V)).astype(np.float32)
+    score = zd / np.float32(cfg.temperature) + gum
+    if cfg.top_k > 0 and cfg.top_k < V:
+        kth = np.partition(zd, V - cfg.top_k, axis=-1)[..., V - cfg.top_k][..., None]
+        score = np.where(zd >= kth, score, -np.inf)
+    return np.argmax(score, axis=-1).astype(np.int32)
+
+
+def uniforms(cfg: Config, st, B: Optional[int] = None) -> np.ndarray:
+    """[B, G+1, 2] fp32 in [0, 1): [..., i, 0] accepts drafted position i,
+    [..., i, 1] samples the correction / extra token at position i."""
+    B = cfg.B if B is None else B
+    return st["uniforms"].random((B, cfg.G + 1, 2), dtype=np.float32)
+
+
+def make_round(cfg: Config, seed: int = 0, with_logits: bool = True,
+               random_gains: bool = False) -> RoundInputs:
+    """All inputs of one round of ``cfg``. Context caches are not drawn here
+    (see ``context_hidden``)."""
+    st = streams(seed)
+    ctx = ctx_lengths(cfg, st["ctx_len"])
+    base, tcap = cache_layout(ctx, cfg.K, cfg.window)
+    rows = cfg.B * cfg.K
+    h_bits, _ = bf16_normal(st["h_round"], (rows, cfg.d_in))
+    w_bits, _ = bf16_normal(st["w_kv"], (cfg.n_out, cfg.d_in), std=cfg.w_std)
+    if random_gains:
+        g = 1.0 + 0.25 * st["k_norm_w"].standard_normal((cfg.L, cfg.hd), dtype=np.float32)
+        g_bits = to_bf16_bits(g)
+    else:
+        g_bits = to_bf16_bits(np.ones((cfg.L, cfg.hd), dtype=np.float32))
+    q_bits, _ = bf16_normal(st["q"], (cfg.L, cfg.B, cfg.K, cfg.n_q, cfg.hd))
+    kb_bits, _ = bf16_normal(st["kv_blk"], (cfg.L, cfg.B, cfg.K, cfg.n_kv, cfg.hd))
+    vb_bits, _ = bf16_normal(st["kv_blk"], (cfg.L, cfg.B, cfg.K, cfg.n_kv, cfg.hd))
+    if with_logits:
+        zt, zd = logits(cfg, st)
+        dt = draft_tokens(cfg, zd, st)
+        u = uniforms(cfg, st)
+        if cfg.temperature == 0.0:
+            zd_keep = None
+        else:
+            zd_keep = zd
+    else:
+        zt = np.zeros((cfg.B, cfg.G + 1, 0), np.float32)
+        zd_keep = None
+        dt = np.zeros((cfg.B, cfg.G), np.int32)
+        u = uniforms(cfg, st)
+    return RoundInputs(cfg, ctx, base, tcap, h_bits, w_bits, g_bits, q_bits, kb_bits, vb_bits,
+                       zt, zd_keep, dt, u)
+
+
+def context_hidden(cfg: Config, ctx_len: np.ndarray, seed: int = 0, window_only: bool = True):
+    """Hidden states of the context tokens, used to fill the caches before a
+    round (untimed). Returns (bits [R, d_in], row_cu [B+1], row_pos0 [B]).
+    With a window only the last ``window`` positions of each request are drawn
+    (earlier positions are never read)."""
+    st = streams(seed)
+    first = np.zeros(cfg.B, dtype=np.int64)
+    if window_only and cfg.window > 0:
+        first = np.maximum(0, ctx_len.astype(np.int64) - cfg.window)
+    n = ctx_len.astype(np.int64) - first
+    row_cu = np.zeros(cfg.B + 1, dtype=np.int32)
+    row_cu[1:] = np.cumsum(n)
+    bits, _ = bf16_normal(st["h_ctx"], (int(row_cu[-1]), cfg.d_in))
+    return bits, row_cu, first.astype(np.int32)
+
+
+def scaled(cfg: Config, **kw) -> Config:
+    """A copy of ``cfg`` with some fields replaced (smaller parity cases)."""
+    return replace(cfg, **kw)
