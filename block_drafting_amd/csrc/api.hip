@@ -1,0 +1,166 @@
+// C ABI of the block-draft library: argument checks on the host, workspace
+// sizing, and the launches (declared in include/blockdraft.h).
+//
+// Every check runs before any HIP call, so an invalid call returns without
+// touching the device and leaves the outputs as they were.
+#include "../../include/blockdraft.h"
+#include "bd_launch.hpp"
+
+#include <stdarg.h>
+#include <stdio.h>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return BD_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(BD_E_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* blockdraft_last_error(void) { return g_err; }
+
+// ------------------------------------------------------------------ inject_kv
+size_t inject_kv_workspace_size(int32_t M, int32_t d_in, int32_t L, int32_t n_kv, int32_t hd) {
+  if (M <= 0 || d_in <= 0 || L <= 0 || n_kv <= 0 || hd <= 0) return 0;
+  return bd::inject_ws_bytes(M, d_in, L * 2 * n_kv * hd);
+}
+
+int inject_kv(const uint16_t* h_target, const uint16_t* w_kv, const uint16_t* k_norm_w,
+              const int32_t* row_cu, const int32_t* row_pos0, const int64_t* cache_base,
+              uint16_t* k_cache, uint16_t* v_cache, int64_t T_cap,
+              int32_t B, int32_t M, int32_t d_in, int32_t L, int32_t n_kv, int32_t hd,
+              float rope_theta, float rms_eps,
+              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || M < 0 || d_in <= 0 || L <= 0 || n_kv <= 0 || hd <= 0 || T_cap < 0)
+    return fail(BD_E_SHAPE, "inject_kv: need B >= 0, M >= 0, T_cap >= 0 and positive d_in, L, n_kv, hd "
+                "(got B=%d M=%d d_in=%d L=%d n_kv=%d hd=%d T_cap=%lld)", B, M, d_in, L, n_kv, hd,
+                (long long)T_cap);
+  if (!(rope_theta > 0.f) || !(rms_eps >= 0.f))
+    return fail(BD_E_SHAPE, "inject_kv: need rope_theta > 0 and rms_eps >= 0");
+  if (hd != 64 && hd != 128) return fail(BD_E_UNSUPPORTED, "inject_kv: hd must be 64 or 128 (got %d)", hd);
+  if (d_in % 64 != 0) return fail(BD_E_UNSUPPORTED, "inject_kv: d_in must be a multiple of 64 (got %d)", d_in);
+  if (n_kv > 64) return fail(BD_E_UNSUPPORTED, "inject_kv: n_kv must be <= 64 (got %d)", n_kv);
+  if ((long long)L * 2 * n_kv * hd > (1 << 24))
+    return fail(BD_E_UNSUPPORTED, "inject_kv: L*2*n_kv*hd too large");
+  if (!h_target || !w_kv || !row_cu || !row_pos0 || !cache_base || !k_cache || !v_cache)
+    return fail(BD_E_NULL, "inject_kv: a required pointer is NULL");
+  if (!aligned16(h_target) || !aligned16(w_kv) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(BD_E_UNSUPPORTED, "inject_kv: H, W and the caches must be 16-byte aligned");
+  const size_t need = inject_kv_workspace_size(M, d_in, L, n_kv, hd);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(BD_E_WORKSPACE, "inject_kv: workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (need > 0 && !aligned16(workspace)) return fail(BD_E_UNSUPPORTED, "inject_kv: workspace must be 16-byte aligned");
+  if (M == 0 || B == 0) return ok();
+  return launched(bd::launch_inject(h_target, w_kv, k_norm_w, row_cu, row_pos0, cache_base, k_cache, v_cache,
+                                    T_cap, B, M, d_in, L, n_kv, hd, rope_theta, rms_eps, workspace, stream),
+                  "inject_kv");
+}
+
+// ------------------------------------------------------------ draft_block_attn
+size_t draft_block_attn_workspace_size(int32_t B, int32_t K, int32_t n_q, int32_t n_kv, int32_t hd,
+                                       int32_t max_ctx, int32_t window) {
+  if (B <= 0 || K <= 0 || n_q <= 0 || n_kv <= 0 || hd <= 0 || max_ctx < 0 || window < 0 || n_q % n_kv)
+    return 0;
+  return bd::attn_ws_bytes(B, K, n_q, n_kv, hd, max_ctx, window);
+}
+
+int draft_block_attn(const uint16_t* q, const uint16_t* k_blk, const uint16_t* v_blk,
+                     const uint16_t* k_cache, const uint16_t* v_cache,
+                     const int64_t* cache_base, const int32_t* ctx_len,
+                     int64_t T_cap, int32_t max_ctx,
+                     int32_t B, int32_t K, int32_t n_q, int32_t n_kv, int32_t hd,
+                     int32_t window, float scale,
+                     uint16_t* out, float* lse,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || K < 1 || n_q < 1 || n_kv < 1 || hd < 1 || max_ctx < 0 || window < 0 || T_cap < 0)
+    return fail(BD_E_SHAPE, "draft_block_attn: need B >= 0, K, n_q, n_kv, hd >= 1 and max_ctx, window, "
+                "T_cap >= 0 (got B=%d K=%d n_q=%d n_kv=%d hd=%d max_ctx=%d window=%d)",
+                B, K, n_q, n_kv, hd, max_ctx, window);
+  if (n_q % n_kv) return fail(BD_E_SHAPE, "draft_block_attn: n_q (%d) must be a multiple of n_kv (%d)", n_q, n_kv);
+  if (scale != scale) return fail(BD_E_SHAPE, "draft_block_attn: scale is NaN");
+  if (hd != 64 && hd != 128) return fail(BD_E_UNSUPPORTED, "draft_block_attn: hd must be 64 or 128 (got %d)", hd);
+  if (K > 64) return fail(BD_E_UNSUPPORTED, "draft_block_attn: K must be <= 64 (got %d)", K);
+  if ((n_q / n_kv) * K > 128)
+    return fail(BD_E_UNSUPPORTED, "draft_block_attn: (n_q/n_kv)*K must be <= 128 (got %d)", (n_q / n_kv) * K);
+  if (!q || !k_blk || !v_blk || !k_cache || !v_cache || !cache_base || !ctx_len || !out)
+    return fail(BD_E_NULL, "draft_block_attn: a required pointer is NULL");
+  if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(BD_E_UNSUPPORTED, "draft_block_attn: Q, block K/V and the caches must be 16-byte aligned");
+  const size_t need = draft_block_attn_workspace_size(B, K, n_q, n_kv, hd, max_ctx, window);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(BD_E_WORKSPACE, "draft_block_attn: workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (need > 0 && !aligned16(workspace))
+    return fail(BD_E_UNSUPPORTED, "draft_block_attn: workspace must be 16-byte aligned");
+  if (B == 0) return ok();
+  return launched(bd::launch_attn(q, k_blk, v_blk, k_cache, v_cache, cache_base, ctx_len, T_cap, max_ctx, B, K,
+                                  n_q, n_kv, hd, window, scale, out, lse, workspace, stream),
+                  "draft_block_attn");
+}
+
+// ---------------------------------------------------------------- verify_block
+size_t verify_block_workspace_size(int32_t B, int32_t G, int32_t V, int32_t top_k) {
+  if (B <= 0 || G < 0 || V <= 0 || top_k < 0) return 0;
+  return bd::verify_ws_bytes(B, G, V, top_k);
+}
+
+int verify_block(const float* target_logits, const float* draft_logits,
+                 const int32_t* draft_tokens, const float* uniforms,
+                 int32_t B, int32_t G, int32_t V,
+                 float temperature, int32_t top_k, float top_p,
+                 int32_t* tau, int32_t* out_tokens,
+                 float* target_probs, float* draft_probs,
+                 float* accept_ratio, float* sample_margin,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || G < 0 || V < 1 || top_k < 0)
+    return fail(BD_E_SHAPE, "verify_block: need B >= 0, G >= 0, V >= 1, top_k >= 0 (got B=%d G=%d V=%d top_k=%d)",
+                B, G, V, top_k);
+  if (!(temperature >= 0.f) || temperature == INFINITY || top_p != top_p)
+    return fail(BD_E_SHAPE, "verify_block: temperature must be finite and >= 0, top_p not NaN");
+  if (top_k > 64) return fail(BD_E_UNSUPPORTED, "verify_block: top_k must be <= 64 (got %d)", top_k);
+  if (G > 64) return fail(BD_E_UNSUPPORTED, "verify_block: G must be <= 64 (got %d)", G);
+  if ((long long)B * (2 * G + 1) * ((V + 8191) / 8192) > 0x7fffffffLL)
+    return fail(BD_E_UNSUPPORTED, "verify_block: too many (row, chunk) pairs");
+  const bool greedy = temperature == 0.f;
+  if (!target_logits || !tau || !out_tokens || (G > 0 && !draft_tokens))
+    return fail(BD_E_NULL, "verify_block: target_logits, draft_tokens, tau and out_tokens are required");
+  if (!greedy && (!uniforms || (G > 0 && !draft_logits)))
+    return fail(BD_E_NULL, "verify_block: sampling needs draft_logits and uniforms");
+  if (draft_probs && G > 0 && !draft_logits)
+    return fail(BD_E_NULL, "verify_block: draft_probs needs draft_logits");
+  if (!aligned16(target_logits) || (draft_logits && !aligned16(draft_logits)))
+    return fail(BD_E_UNSUPPORTED, "verify_block: logits must be 16-byte aligned");
+  const size_t need = verify_block_workspace_size(B, G, V, top_k);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(BD_E_WORKSPACE, "verify_block: workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (need > 0 && !aligned16(workspace)) return fail(BD_E_UNSUPPORTED, "verify_block: workspace must be 16-byte aligned");
+  if (B == 0) return ok();
+  return launched(bd::launch_verify(target_logits, draft_logits, draft_tokens, uniforms, B, G, V, temperature,
+                                    top_k, top_p, tau, out_tokens, target_probs, draft_probs, accept_ratio,
+                                    sample_margin, workspace, stream),
+                  "verify_block");
+}
+
+}  // extern "C"

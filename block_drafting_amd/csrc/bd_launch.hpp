@@ -1,0 +1,28 @@
+// Host launchers of the three kernel families (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bd {
+
+size_t inject_ws_bytes(int M, int d_in, int N);
+hipError_t launch_inject(const uint16_t* h, const uint16_t* w, const uint16_t* gain, const int32_t* row_cu,
+                         const int32_t* row_pos0, const int64_t* cache_base, uint16_t* kc, uint16_t* vc,
+                         int64_t T_cap, int B, int M, int d_in, int L, int n_kv, int hd, float theta,
+                         float eps, void* ws, hipStream_t stream);
+
+size_t attn_ws_bytes(int B, int K, int n_q, int n_kv, int hd, int max_ctx, int window);
+hipError_t launch_attn(const uint16_t* q, const uint16_t* kb, const uint16_t* vb, const uint16_t* kc,
+                       const uint16_t* vc, const int64_t* cache_base, const int32_t* ctx_len,
+                       int64_t T_cap, int max_ctx, int B, int K, int n_q, int n_kv, int hd, int window,
+                       float scale, uint16_t* out, float* lse, void* ws, hipStream_t stream);
+
+size_t verify_ws_bytes(int B, int G, int V, int top_k);
+hipError_t launch_verify(const float* zt, const float* zd, const int* dtok, const float* uni,
+                         int B, int G, int V, float temperature, int top_k, float top_p,
+                         int* tau, int* out, float* tprob, float* dprob, float* ratio, float* margin,
+                         void* ws, hipStream_t stream);
+
+}  // namespace bd

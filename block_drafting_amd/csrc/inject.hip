@@ -1,0 +1,279 @@
+// inject_kv kernels: the layer-batched projection of target hidden states
+// into every draft layer's K/V, with RMSNorm + RoPE + bf16 + cache scatter.
+//
+// DFlash/Spec V2 blog, summary and A2: KV_draft^(l) = Projection^(l)(H_target)
+// for every draft layer l.  A7: all layers' projections run as one batched
+// linear map, followed by a fused Norm + RoPE post-processing step, and the
+// result goes straight into the draft KV cache before the draft forward
+// (immediate materialization; the target latents are not kept).
+//
+// Stage 1 (ik_gemm): Y = H . W^T on the gfx950 32x32x16 bf16 MFMA, fp32
+// accumulation, tiles staged in LDS, optional split over d_in; fp32 partial
+// sums go to the workspace.
+// Stage 2 (ik_finish): one workgroup per (row, layer) sums the partials in a
+// fixed order, normalises each K head (RMS over hd, times the gain), rotates
+// the half-split pairs (i, i + hd/2) by pos * theta^(-2i/hd), rounds K and V
+// to bf16 and writes them to the request's cache slot.
+#include "bd_common.hpp"
+#include "bd_launch.hpp"
+
+#include <math.h>
+
+namespace bd {
+
+constexpr int GT = 256;  // threads per GEMM workgroup (2 x 2 waves)
+constexpr int BK = 64;   // d_in per LDS stage
+constexpr int GLS = BK + 8;  // LDS row stride (elements)
+
+struct GemmArgs {
+  const uint16_t* A;  // [M, Kd]
+  const uint16_t* Bw; // [N, Kd]
+  float* P;           // [S][M][N]
+  int M, N, Kd, S, steps_per_split, tiles_n;
+};
+
+template <int BM, int BN>
+__global__ __launch_bounds__(GT) void ik_gemm(GemmArgs g) {
+  constexpr int WM = BM / 2, WN = BN / 2;   // wave tile
+  constexpr int FM = WM / 32, FN = WN / 32; // 32x32 blocks per wave
+  constexpr int APT = BM * BK / 8 / GT;     // 16-byte pieces per thread
+  constexpr int BPT = BN * BK / 8 / GT;
+  __shared__ __attribute__((aligned(16))) uint16_t As[BM * GLS];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * GLS];
+
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int tile = blockIdx.x, split = blockIdx.y;
+  const int tm = tile / g.tiles_n, tn = tile - tm * g.tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int step0 = split * g.steps_per_split;
+  const int nsteps_all = g.Kd / BK;
+  const int nsteps = min(g.steps_per_split, nsteps_all - step0);
+
+  floatx16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  uint4 ra[APT], rb[BPT];
+  auto fetch = [&](int step) {
+    const int k0 = (step0 + step) * BK;
+#pragma unroll
+    for (int p = 0; p < APT; ++p) {
+      const int piece = t + p * GT;
+      const int row = piece / (BK / 8), kc = piece - row * (BK / 8);
+      const int m = m0 + row;
+      ra[p] = m < g.M ? *reinterpret_cast<const uint4*>(g.A + size_t(m) * g.Kd + k0 + kc * 8)
+                      : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int p = 0; p < BPT; ++p) {
+      const int piece = t + p * GT;
+      const int row = piece / (BK / 8), kc = piece - row * (BK / 8);
+      rb[p] = *reinterpret_cast<const uint4*>(g.Bw + size_t(n0 + row) * g.Kd + k0 + kc * 8);
+    }
+  };
+
+  if (nsteps > 0) fetch(0);
+  for (int step = 0; step < nsteps; ++step) {
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < APT; ++p) {
+      const int piece = t + p * GT;
+      const int row = piece / (BK / 8), kc = piece - row * (BK / 8);
+      *reinterpret_cast<uint4*>(&As[row * GLS + kc * 8]) = ra[p];
+    }
+#pragma unroll
+    for (int p = 0; p < BPT; ++p) {
+      const int piece = t + p * GT;
+      const int row = piece / (BK / 8), kc = piece - row * (BK / 8);
+      *reinterpret_cast<uint4*>(&Bs[row * GLS + kc * 8]) = rb[p];
+    }
+    __syncthreads();
+    if (step + 1 < nsteps) fetch(step + 1);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(
+            &As[(wm * WM + i * 32 + (lane & 31)) * GLS + kk * 16 + (lane >> 5) * 8]));
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = as_bf16x8(*reinterpret_cast<const uint4*>(
+            &Bs[(wn * WN + j * 32 + (lane & 31)) * GLS + kk * 16 + (lane >> 5) * 8]));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(af[i], bfr[j], acc[i][j]);
+    }
+  }
+
+  // C block layout: lane holds column (lane & 31), rows 8*jj + 4*(lane >> 5) + r
+  float* P = g.P + size_t(split) * g.M * g.N;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn * WN + j * 32 + (lane & 31);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + wm * WM + i * 32 + jj * 8 + (lane >> 5) * 4 + r;
+          if (m < g.M) P[size_t(m) * g.N + n] = acc[i][j][jj * 4 + r];
+        }
+    }
+}
+
+struct FinishArgs {
+  const float* P;  // [S][M][N]
+  const uint16_t* gain;  // [L][hd] or NULL
+  const int32_t* row_cu;
+  const int32_t* row_pos0;
+  const int64_t* cache_base;
+  uint16_t* kc;
+  uint16_t* vc;
+  int64_t T_cap;
+  int B, M, N, S, L, n_kv, hd;
+  float eps;
+  double inv_freq[64];
+};
+
+__global__ __launch_bounds__(256) void ik_finish(FinishArgs f) {
+  const int m = blockIdx.x, l = blockIdx.y, t = threadIdx.x;
+  // request of this row
+  if (f.B <= 0 || m >= f.row_cu[f.B]) return;
+  int lo = 0, hi = f.B - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (f.row_cu[mid] <= m) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo;
+  const int j = m - f.row_cu[b];
+  const int pos = f.row_pos0[b] + j;
+  const int64_t slot = f.cache_base[b] + pos;
+  if (j < 0 || slot < 0 || slot >= f.T_cap) return;
+
+  const int hd = f.hd, half = hd >> 1;
+  const int tph = hd / 8;  // threads per K head (4 + 4 dims each)
+  const int n_items_k = f.n_kv * tph;
+  const int n_items_v = f.n_kv * hd / 8;
+  const size_t kcol0 = size_t(l) * 2 * f.n_kv * hd;
+  const size_t vcol0 = kcol0 + size_t(f.n_kv) * hd;
+  const size_t MN = size_t(f.M) * f.N;
+  const float* prow = f.P + size_t(m) * f.N;
+
+  for (int it = t; it < n_items_k; it += 256) {
+    const int head = it / tph, jj = it - head * tph;
+    const int d0 = 4 * jj;  // dims d0..d0+3 and half+d0..half+d0+3
+    const float* p0 = prow + kcol0 + size_t(head) * hd;
+    float xa[4] = {0.f, 0.f, 0.f, 0.f}, xb[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < f.S; ++s) {
+      const float4 va = *reinterpret_cast<const float4*>(p0 + s * MN + d0);
+      const float4 vb = *reinterpret_cast<const float4*>(p0 + s * MN + half + d0);
+      xa[0] += va.x; xa[1] += va.y; xa[2] += va.z; xa[3] += va.w;
+      xb[0] += vb.x; xb[1] += vb.y; xb[2] += vb.z; xb[3] += vb.w;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ss += xa[c] * xa[c] + xb[c] * xb[c];
+    for (int o = tph >> 1; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    const float inv = 1.0f / sqrtf(ss / float(hd) + f.eps);
+    uint16_t oa[4], ob[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int i = d0 + c;
+      float ga = 1.f, gb = 1.f;
+      if (f.gain) {
+        ga = bf16_to_f32(f.gain[l * hd + i]);
+        gb = bf16_to_f32(f.gain[l * hd + half + i]);
+      }
+      const float a = xa[c] * inv * ga, bb = xb[c] * inv * gb;
+      // angle pos * theta^(-2i/hd) in fp64, reduced to [-pi, pi] before the
+      // fp32 sine / cosine
+      const double ang = double(pos) * f.inv_freq[i];
+      const double k = rint(ang * 0.15915494309189535);
+      double r = fma(-k, 6.283185307179586, ang);
+      r = fma(-k, 2.4492935982947064e-16, r);
+      float sn, cs;
+      sincosf(float(r), &sn, &cs);
+      oa[c] = f32_to_bf16(a * cs - bb * sn);
+      ob[c] = f32_to_bf16(bb * cs + a * sn);
+    }
+    uint16_t* kd = f.kc + ((size_t(l) * f.T_cap + slot) * f.n_kv + head) * hd;
+    *reinterpret_cast<uint2*>(kd + d0) = make_uint2(oa[0] | (uint32_t(oa[1]) << 16), oa[2] | (uint32_t(oa[3]) << 16));
+    *reinterpret_cast<uint2*>(kd + half + d0) = make_uint2(ob[0] | (uint32_t(ob[1]) << 16), ob[2] | (uint32_t(ob[3]) << 16));
+  }
+  for (int it = t; it < n_items_v; it += 256) {
+    const int c0 = it * 8;  // column within this layer's V block
+    const float* p0 = prow + vcol0 + c0;
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < f.S; ++s) {
+      const float4 va = *reinterpret_cast<const float4*>(p0 + s * MN);
+      const float4 vb = *reinterpret_cast<const float4*>(p0 + s * MN + 4);
+      x[0] += va.x; x[1] += va.y; x[2] += va.z; x[3] += va.w;
+      x[4] += vb.x; x[5] += vb.y; x[6] += vb.z; x[7] += vb.w;
+    }
+    uint16_t* vd = f.vc + (size_t(l) * f.T_cap + slot) * f.n_kv * hd + c0;
+    *reinterpret_cast<uint4*>(vd) = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                               pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+  }
+}
+
+// ---------------------------------------------------------------- host side
+static inline size_t al(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct GemmPlan {
+  int bm, bn, S, steps_per_split, tiles;
+};
+
+static GemmPlan gemm_plan(int M, int N, int Kd) {
+  GemmPlan p;
+  p.bm = M > 128 ? 256 : 64;
+  p.bn = 128;
+  const int tm = (M + p.bm - 1) / p.bm;
+  p.tiles = tm * (N / p.bn);
+  const int steps = Kd / BK;
+  int S = (512 + p.tiles - 1) / p.tiles;
+  if (S > steps) S = steps;
+  if (S < 1) S = 1;
+  p.steps_per_split = (steps + S - 1) / S;
+  p.S = (steps + p.steps_per_split - 1) / p.steps_per_split;
+  return p;
+}
+
+size_t inject_ws_bytes(int M, int d_in, int N) {
+  if (M <= 0) return 0;
+  GemmPlan p = gemm_plan(M, N, d_in);
+  return al(size_t(p.S) * M * N * 4);
+}
+
+hipError_t launch_inject(const uint16_t* h, const uint16_t* w, const uint16_t* gain, const int32_t* row_cu,
+                         const int32_t* row_pos0, const int64_t* cache_base, uint16_t* kc, uint16_t* vc,
+                         int64_t T_cap, int B, int M, int d_in, int L, int n_kv, int hd, float theta,
+                         float eps, void* ws, hipStream_t stream) {
+  if (M == 0 || B == 0) return hipSuccess;
+  const int N = L * 2 * n_kv * hd;
+  GemmPlan p = gemm_plan(M, N, d_in);
+  GemmArgs g;
+  g.A = h; g.Bw = w; g.P = static_cast<float*>(ws);
+  g.M = M; g.N = N; g.Kd = d_in; g.S = p.S; g.steps_per_split = p.steps_per_split;
+  g.tiles_n = N / p.bn;
+  dim3 grid(p.tiles, p.S);
+  if (p.bm == 256) hipLaunchKernelGGL((ik_gemm<256, 128>), grid, dim3(GT), 0, stream, g);
+  else hipLaunchKernelGGL((ik_gemm<64, 128>), grid, dim3(GT), 0, stream, g);
+
+  FinishArgs f{};
+  f.P = g.P; f.gain = gain; f.row_cu = row_cu; f.row_pos0 = row_pos0; f.cache_base = cache_base;
+  f.kc = kc; f.vc = vc; f.T_cap = T_cap;
+  f.B = B; f.M = M; f.N = N; f.S = p.S; f.L = L; f.n_kv = n_kv; f.hd = hd; f.eps = eps;
+  for (int i = 0; i < hd / 2; ++i) f.inv_freq[i] = pow(double(theta), -2.0 * i / double(hd));
+  hipLaunchKernelGGL(ik_finish, dim3(M, L), dim3(256), 0, stream, f);
+  return hipGetLastError();
+}
+
+}  // namespace bd

@@ -1,0 +1,812 @@
+// verify_block kernels: vocabulary-row statistics, the per-request decision
+// chain, and the residual / extra-token draw.
+//
+// DSpark tutorial, "speculative decoding basics": prefix acceptance, one
+// replacement at the first disagreement, one extra token per round, and the
+// losslessness of the rejection rule (accept with min(1, P/Q), else draw from
+// the normalised max(0, P - Q)).  DSpine article, "principle": greedy
+// matching; "speed-up": temperature / top-k / top-p; "tuning and memory":
+// batched verification can flip near-tied tokens, hence the fixed reduction
+// orders here and the ratio / margin diagnostics.
+//
+// Pass 1 (vb_stats) streams every logits row once, split in chunks of 8192:
+// per chunk the maximum and its lowest index, the sum of exp((z - max) / T)
+// (fp32 lanes, fp64 across lanes) and, under top-k, the chunk's k best
+// (value desc, index asc).  Pass 2 (vb_decide, one workgroup per request)
+// merges the chunks of its rows, applies the filters, runs the accept chain
+// and, where the draw needs only the filtered support, draws the token.
+// Without top-k the draw needs the whole row pair once more: vb_draw_sums
+// gives per-chunk sums of the draw weights and vb_draw_pick scans the one
+// chunk that holds the crossing.
+#include "bd_common.hpp"
+#include "bd_launch.hpp"
+
+#include <math.h>
+
+namespace bd {
+
+constexpr int VT = 256;        // threads of a stats / draw workgroup
+constexpr int VCH = 8192;      // logits per chunk (32 per thread)
+constexpr int VPT = VCH / VT;  // 32
+constexpr int TOPK_MAX = 64;
+constexpr int CAND_PER_WAVE = 64;
+
+enum { JOB_NONE = 0, JOB_RESID = 1, JOB_BONUS = 2 };
+
+// -------------------------------------------------------------------------
+// element access: thread t holds, for j = 0..7 and c = 0..3 (vector rows) the
+// logit at chunk offset 4 * (j * 256 + t) + c, or for j = 0..31 (scalar rows)
+// the logit at chunk offset j * 256 + t.  Both orders increase with the slot.
+// -------------------------------------------------------------------------
+template <bool VEC>
+__device__ __forceinline__ int slot_offset(int s, int t) {
+  if (VEC) return 4 * ((s >> 2) * VT + t) + (s & 3);
+  return s * VT + t;
+}
+
+template <bool VEC>
+__device__ __forceinline__ void load_chunk(const float* __restrict__ row, int start, int V, int t,
+                                           float (&x)[VPT]) {
+  if (VEC) {
+#pragma unroll
+    for (int j = 0; j < VPT / 4; ++j) {
+      int e = start + 4 * (j * VT + t);
+      if (e + 3 < V) {
+        float4 f = *reinterpret_cast<const float4*>(row + e);
+        x[4 * j] = f.x; x[4 * j + 1] = f.y; x[4 * j + 2] = f.z; x[4 * j + 3] = f.w;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[4 * j + c] = (e + c < V) ? row[e + c] : -INFINITY;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      int e = start + j * VT + t;
+      x[j] = (e < V) ? row[e] : -INFINITY;
+    }
+  }
+}
+
+// Block-wide (value, index) argmax; lds needs 2 * (VT / 64) words.
+__device__ __forceinline__ void block_argmax(float& v, int& i, float* lv, int* li) {
+  wave_argmax(v, i);
+  int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) { lv[w] = v; li[w] = i; }
+  __syncthreads();
+  v = lv[0]; i = li[0];
+#pragma unroll
+  for (int k = 1; k < VT / 64; ++k)
+    if (better(lv[k], li[k], v, i)) { v = lv[k]; i = li[k]; }
+}
+
+__device__ __forceinline__ double block_sum_f64(double s, double* ld) {
+  s = wave_sum(s);
+  int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) ld[w] = s;
+  __syncthreads();
+  double r = 0.0;
+#pragma unroll
+  for (int k = 0; k < VT / 64; ++k) r += ld[k];
+  return r;
+}
+
+// Descending bitonic sort of one float per lane across the wave.
+__device__ __forceinline__ float wave_sort_desc(float v) {
+  int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      float o = __shfl_xor(v, stride);
+      bool desc = (lane & size) == 0 || size == 64;
+      bool lower = (lane & stride) == 0;
+      v = (lower == desc) ? fmaxf(v, o) : fminf(v, o);
+    }
+  }
+  return v;
+}
+
+struct VerifyWs {
+  float* cmax;   // [rows][nch]
+  int* carg;     // [rows][nch]
+  double* csum;  // [rows][nch]
+  float* ctv;    // [rows][nch][k]
+  int* cti;      // [rows][nch][k]
+  float* rmax;   // [rows]
+  int* rarg;     // [rows]
+  double* rsum;  // [rows]
+  int* rkn;      // [rows]           kept count after filters
+  int* rki;      // [rows][TOPK_MAX] kept indices (value desc, index asc)
+  double* rkp;   // [rows][TOPK_MAX] kept probabilities
+  int* job;      // [B][2]           (position, kind)
+  double* jsum;  // [B][nch]
+};
+
+struct VerifyArgs {
+  const float* zt;
+  const float* zd;
+  const int* dtok;
+  const float* uni;
+  int B, G, V, nch;
+  int n_trows, n_rows;   // target rows B*(G+1); all rows with draft rows
+  float T;               // temperature used for probabilities (1 when greedy)
+  float c2;              // log2(e) / T
+  int greedy, topk, need_sum;
+  float top_p;
+  int* tau;
+  int* out;
+  float* tprob;
+  float* dprob;
+  float* ratio;
+  float* margin;
+  VerifyWs ws;
+};
+
+__device__ __forceinline__ const float* row_ptr(const VerifyArgs& a, int r) {
+  return r < a.n_trows ? a.zt + size_t(r) * a.V : a.zd + size_t(r - a.n_trows) * a.V;
+}
+
+// -------------------------------------------------------------------------
+// Pass 1: per (row, chunk) statistics.
+// -------------------------------------------------------------------------
+template <bool VEC>
+__global__ __launch_bounds__(VT) void vb_stats(VerifyArgs a) {
+  __shared__ float s_v[4];
+  __shared__ int s_i[4];
+  __shared__ double s_d[4];
+  __shared__ float s_cv[4 * CAND_PER_WAVE];
+  __shared__ int s_ci[4 * CAND_PER_WAVE];
+  __shared__ int s_cn[4];
+  __shared__ int s_over;
+
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int row = blockIdx.x / a.nch;
+  const int c = blockIdx.x - row * a.nch;
+  const int start = c * VCH;
+  const float* zr = row_ptr(a, row);
+
+  float x[VPT];
+  load_chunk<VEC>(zr, start, a.V, t, x);
+
+  float bv = -INFINITY;
+  int bi = INT32_MAX;
+#pragma unroll
+  for (int s = 0; s < VPT; ++s) {
+    int e = start + slot_offset<VEC>(s, t);
+    if (e < a.V && (x[s] > bv || bi == INT32_MAX)) { bv = x[s]; bi = e; }
+  }
+  float lane_best = bv;
+  block_argmax(bv, bi, s_v, s_i);
+  const size_t rc = size_t(row) * a.nch + c;
+  if (t == 0) { a.ws.cmax[rc] = bv; a.ws.carg[rc] = bi; }
+
+  if (a.need_sum) {
+    double sum = 0.0;
+    if (bi != INT32_MAX && bv != -INFINITY) {
+      float part = 0.f;
+#pragma unroll
+      for (int s = 0; s < VPT; ++s) part += exp2f((x[s] - bv) * a.c2);
+      sum = double(part);
+    }
+    sum = block_sum_f64(sum, s_d);
+    if (t == 0) a.ws.csum[rc] = sum;
+  }
+
+  if (a.topk > 0) {
+    const int k = a.topk;
+    // Per wave: the k-th largest lane maximum bounds the chunk's k best that
+    // live in this wave from below (the wave alone has k elements at least as
+    // large), so only elements >= it can be among them.
+    float srt = wave_sort_desc(lane_best);
+    float thr = __shfl(srt, k - 1);
+    int cnt = 0;
+#pragma unroll
+    for (int s = 0; s < VPT; ++s) {
+      int e = start + slot_offset<VEC>(s, t);
+      cnt += (e < a.V && x[s] >= thr) ? 1 : 0;
+    }
+    // exclusive prefix of cnt over the wave
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    int total = __shfl(incl, 63);
+    if (t == 0) s_over = 0;
+    __syncthreads();
+    if (total > CAND_PER_WAVE) {
+      if (lane == 0) s_over = 1;
+    } else {
+      int pos = incl - cnt;
+#pragma unroll
+      for (int s = 0; s < VPT; ++s) {
+        int e = start + slot_offset<VEC>(s, t);
+        if (e < a.V && x[s] >= thr) {
+          s_cv[w * CAND_PER_WAVE + pos] = x[s];
+          s_ci[w * CAND_PER_WAVE + pos] = e;
+          ++pos;
+        }
+      }
+      if (lane == 0) s_cn[w] = total;
+    }
+    __syncthreads();
+    float* ov = a.ws.ctv + rc * k;
+    int* oi = a.ws.cti + rc * k;
+    if (!s_over) {
+      // rank every candidate against all others (strict total order)
+      for (int cidx = t; cidx < 4 * CAND_PER_WAVE; cidx += VT) {
+        int cw = cidx / CAND_PER_WAVE, cj = cidx - cw * CAND_PER_WAVE;
+        if (cj >= s_cn[cw]) continue;
+        float v = s_cv[cidx];
+        int id = s_ci[cidx];
+        int rank = 0;
+        for (int w2 = 0; w2 < 4; ++w2)
+          for (int j2 = 0; j2 < s_cn[w2]; ++j2) {
+            int o = w2 * CAND_PER_WAVE + j2;
+            rank += better(s_cv[o], s_ci[o], v, id) ? 1 : 0;
+          }
+        if (rank < k) { ov[rank] = v; oi[rank] = id; }
+      }
+      int n_all = s_cn[0] + s_cn[1] + s_cn[2] + s_cn[3];
+      for (int r = n_all + t; r < k; r += VT) { ov[r] = -INFINITY; oi[r] = INT32_MAX; }
+    } else {
+      // exact fallback: k rounds, each taking the best element strictly
+      // after the previous pick in (value desc, index asc) order
+      float pv = INFINITY;
+      int pi = -1;
+      for (int r = 0; r < k; ++r) {
+        float cv = -INFINITY;
+        int ci = INT32_MAX;
+#pragma unroll
+        for (int s = 0; s < VPT; ++s) {
+          int e = start + slot_offset<VEC>(s, t);
+          if (e < a.V && (pi < 0 || better(pv, pi, x[s], e)) && better(x[s], e, cv, ci)) {
+            cv = x[s]; ci = e;
+          }
+        }
+        block_argmax(cv, ci, s_v, s_i);
+        if (t == 0) { ov[r] = cv; oi[r] = ci; }
+        if (ci == INT32_MAX) {
+          for (int r2 = r + 1 + t; r2 < k; r2 += VT) { ov[r2] = -INFINITY; oi[r2] = INT32_MAX; }
+          break;
+        }
+        pv = cv; pi = ci;
+      }
+    }
+  }
+}
+
+// -------------------------------------------------------------------------
+// Draw weights of the full-vocabulary draw: the residual max(0, p - q) or p.
+// p(x) = exp((z - max) / T) / S evaluated in fp32.
+// -------------------------------------------------------------------------
+struct DrawRow {
+  const float* zt;
+  const float* zd;  // NULL for the extra-token draw
+  float mt, md, st, sd;  // row maxima and 1 / sums
+};
+
+__device__ __forceinline__ float draw_weight(const DrawRow& r, float c2, float zt, float zd, bool resid) {
+  float p = exp2f((zt - r.mt) * c2) * r.st;
+  if (!resid) return p;
+  float q = exp2f((zd - r.md) * c2) * r.sd;
+  return fmaxf(0.f, p - q);
+}
+
+// -------------------------------------------------------------------------
+// Pass 2: one workgroup per request.
+// -------------------------------------------------------------------------
+__device__ void merge_row(const VerifyArgs& a, int row, int lane) {
+  // max / argmax over chunks
+  float v = -INFINITY;
+  int i = INT32_MAX;
+  for (int c = lane; c < a.nch; c += 64) {
+    size_t rc = size_t(row) * a.nch + c;
+    float cv = a.ws.cmax[rc];
+    int ci = a.ws.carg[rc];
+    if (better(cv, ci, v, i)) { v = cv; i = ci; }
+  }
+  wave_argmax(v, i);
+  double S = 0.0;
+  if (a.need_sum && v != -INFINITY) {
+    for (int c = lane; c < a.nch; c += 64) {
+      size_t rc = size_t(row) * a.nch + c;
+      float cm = a.ws.cmax[rc];
+      if (cm != -INFINITY) S += a.ws.csum[rc] * exp2(double(cm - v) * double(a.c2));
+    }
+    S = wave_sum(S);
+  }
+  if (lane == 0) {
+    a.ws.rmax[row] = v;
+    a.ws.rarg[row] = i;
+    a.ws.rsum[row] = S;
+  }
+  if (a.topk > 0) {
+    // k best of the chunk lists, then softmax over them and the top-p cut
+    const int k = a.topk;
+    const int ncand = a.nch * k;
+    const float* cv = a.ws.ctv + size_t(row) * a.nch * k;
+    const int* ci = a.ws.cti + size_t(row) * a.nch * k;
+    float pv = INFINITY;
+    int pi = -1;
+    int* ki = a.ws.rki + size_t(row) * TOPK_MAX;
+    double* kp = a.ws.rkp + size_t(row) * TOPK_MAX;
+    float kv_lane = -INFINITY;  // lane r keeps the r-th kept value
+    int kept = 0;
+    for (int r = 0; r < k; ++r) {
+      float bv = -INFINITY;
+      int bi = INT32_MAX;
+      for (int j = lane; j < ncand; j += 64) {
+        float x = cv[j];
+        int id = ci[j];
+        if (id == INT32_MAX) continue;
+        if ((pi < 0 || better(pv, pi, x, id)) && better(x, id, bv, bi)) { bv = x; bi = id; }
+      }
+      wave_argmax(bv, bi);
+      if (bi == INT32_MAX) break;
+      if (lane == r) { kv_lane = bv; ki[r] = bi; }
+      pv = bv; pi = bi;
+      ++kept;
+    }
+    // softmax over the kept set in fp64: x_j = z_j / T, e_j = exp(x_j - x_0)
+    double x0 = double(__shfl(kv_lane, 0)) / double(a.T);
+    double e = 0.0;
+    if (lane < kept) e = exp(double(kv_lane) / double(a.T) - x0);
+    // sum in kept order (lane 0 first), the same sequential order everywhere
+    double tot = 0.0;
+    for (int r = 0; r < kept; ++r) tot += __shfl(e, r);
+    double p = (lane < kept) ? e / tot : 0.0;
+    int n = kept;
+    if (a.top_p < 1.0f) {
+      double run = 0.0;
+      n = kept;
+      for (int r = 0; r < kept; ++r) {
+        run += __shfl(p, r);
+        if (run >= double(a.top_p)) { n = r + 1; break; }
+      }
+      if (n < 1) n = 1;
+      double tot2 = 0.0;
+      for (int r = 0; r < n; ++r) tot2 += __shfl(p, r);
+      p = (lane < n) ? p / tot2 : 0.0;
+    }
+    if (lane < n) kp[lane] = p;
+    if (lane == 0) a.ws.rkn[row] = n;
+  }
+}
+
+__device__ __forceinline__ double kept_prob(const VerifyArgs& a, int row, int tok) {
+  int n = a.ws.rkn[row];
+  const int* ki = a.ws.rki + size_t(row) * TOPK_MAX;
+  const double* kp = a.ws.rkp + size_t(row) * TOPK_MAX;
+  for (int j = 0; j < n; ++j)
+    if (ki[j] == tok) return kp[j];
+  return 0.0;
+}
+
+__global__ __launch_bounds__(256) void vb_decide(VerifyArgs a) {
+  const int b = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int G = a.G;
+  // rows of this request: G+1 target rows, then G draft rows when sampling
+  const int n_my = (G + 1) + ((a.n_rows > a.n_trows) ? G : 0);
+  for (int j = w; j < n_my; j += 4) {
+    int row = j <= G ? b * (G + 1) + j : a.n_trows + b * G + (j - G - 1);
+    merge_row(a, row, lane);
+  }
+  __threadfence_block();
+  __syncthreads();
+  if (w != 0) return;
+
+  // decisions, one lane per drafted position (G <= 64)
+  bool acc = false;
+  float ratio = 0.f;
+  int d = -1;
+  if (lane < G) {
+    d = a.dtok[b * G + lane];
+    const int trow = b * (G + 1) + lane;
+    if (a.greedy) {
+      acc = (d == a.ws.rarg[trow]);
+      ratio = acc ? 1.f : 0.f;
+    } else {
+      const int drow = a.n_trows + b * G + lane;
+      double p = 0.0, q = 0.0;
+      if (d >= 0 && d < a.V) {
+        if (a.topk > 0) {
+          p = kept_prob(a, trow, d);
+          q = kept_prob(a, drow, d);
+        } else {
+          float zt = a.zt[size_t(trow) * a.V + d];
+          float zd = a.zd[size_t(b * G + lane) * a.V + d];
+          double Tt = double(a.T);
+          p = exp(double(zt) / Tt - double(a.ws.rmax[trow]) / Tt) / a.ws.rsum[trow];
+          q = exp(double(zd) / Tt - double(a.ws.rmax[drow]) / Tt) / a.ws.rsum[drow];
+        }
+      }
+      float p32 = float(p), q32 = float(q);
+      ratio = p32 / q32;
+      float u = a.uni[(size_t(b) * (G + 1) + lane) * 2];
+      acc = u < ratio;
+    }
+    if (a.ratio) a.ratio[b * G + lane] = ratio;
+  }
+  unsigned long long rej = __ballot(lane < G && !acc);
+  int tau = rej ? __ffsll((long long)rej) - 1 : G;
+  if (lane == 0) a.tau[b] = tau;
+  for (int i = lane; i <= G; i += 64) {
+    if (i < tau) a.out[b * (G + 1) + i] = a.dtok[b * G + i];
+    else if (i > tau) a.out[b * (G + 1) + i] = -1;
+  }
+  const int trow = b * (G + 1) + tau;
+  if (a.greedy) {
+    if (lane == 0) {
+      a.out[b * (G + 1) + tau] = a.ws.rarg[trow];
+      if (a.margin) a.margin[b] = INFINITY;
+    }
+    return;
+  }
+  const float u2 = a.uni[(size_t(b) * (G + 1) + tau) * 2 + 1];
+  if (a.topk > 0) {
+    if (lane != 0) return;
+    // draw over P's kept support in vocabulary order
+    const int n = a.ws.rkn[trow];
+    const int* ki = a.ws.rki + size_t(trow) * TOPK_MAX;
+    const double* kp = a.ws.rkp + size_t(trow) * TOPK_MAX;
+    int idx[TOPK_MAX];
+    double wgt[TOPK_MAX];
+    for (int j = 0; j < n; ++j) { idx[j] = ki[j]; wgt[j] = kp[j]; }
+    // insertion sort by index
+    for (int j = 1; j < n; ++j) {
+      int ii = idx[j]; double ww = wgt[j]; int m = j - 1;
+      while (m >= 0 && idx[m] > ii) { idx[m + 1] = idx[m]; wgt[m + 1] = wgt[m]; --m; }
+      idx[m + 1] = ii; wgt[m + 1] = ww;
+    }
+    double Z = 0.0;
+    if (tau < G) {
+      const int drow = a.n_trows + b * G + tau;
+      for (int j = 0; j < n; ++j) {
+        double r = wgt[j] - kept_prob(a, drow, idx[j]);
+        wgt[j] = r > 0.0 ? r : 0.0;
+        Z += wgt[j];
+      }
+      if (Z == 0.0) {
+        for (int j = 0; j < n; ++j) { wgt[j] = kept_prob(a, trow, idx[j]); Z += wgt[j]; }
+      }
+    } else {
+      for (int j = 0; j < n; ++j) Z += wgt[j];
+    }
+    const double tgt = double(u2) * Z;
+    int pick = -1;
+    double run = 0.0, mg = 0.0;
+    for (int j = 0; j < n; ++j) {
+      double prev = run;
+      run += wgt[j];
+      if (run > tgt) { pick = j; mg = fmin(tgt - prev, run - tgt); break; }
+    }
+    if (pick < 0) {
+      for (int j = n - 1; j >= 0; --j)
+        if (wgt[j] > 0.0) { pick = j; break; }
+      if (pick < 0) pick = n - 1;
+      mg = 0.0;
+    }
+    a.out[b * (G + 1) + tau] = idx[pick];
+    if (a.margin) a.margin[b] = float(mg);
+    return;
+  }
+  if (lane == 0) {
+    a.ws.job[2 * b] = tau;
+    a.ws.job[2 * b + 1] = (tau < G) ? JOB_RESID : JOB_BONUS;
+  }
+}
+
+__device__ __forceinline__ DrawRow draw_row(const VerifyArgs& a, int b, int pos, bool resid) {
+  DrawRow r;
+  const int trow = b * (a.G + 1) + pos;
+  r.zt = a.zt + size_t(trow) * a.V;
+  r.mt = a.ws.rmax[trow];
+  r.st = float(1.0 / a.ws.rsum[trow]);
+  r.zd = nullptr;
+  r.md = 0.f;
+  r.sd = 0.f;
+  if (resid) {
+    const int drow = a.n_trows + b * a.G + pos;
+    r.zd = a.zd + size_t(b * a.G + pos) * a.V;
+    r.md = a.ws.rmax[drow];
+    r.sd = float(1.0 / a.ws.rsum[drow]);
+  }
+  return r;
+}
+
+// per-chunk sums of the draw weights (full-vocabulary draws only)
+__global__ __launch_bounds__(VT) void vb_draw_sums(VerifyArgs a) {
+  __shared__ double s_d[4];
+  const int b = blockIdx.y, c = blockIdx.x, t = threadIdx.x;
+  const int kind = a.ws.job[2 * b + 1];
+  if (kind == JOB_NONE) return;
+  const bool resid = kind == JOB_RESID;
+  const DrawRow r = draw_row(a, b, a.ws.job[2 * b], resid);
+  const int start = c * VCH;
+  double s = 0.0;
+  for (int j = 0; j < VPT; ++j) {
+    int e = start + t * VPT + j;
+    if (e < a.V) s += double(draw_weight(r, a.c2, r.zt[e], resid ? r.zd[e] : 0.f, resid));
+  }
+  s = block_sum_f64(s, s_d);
+  if (t == 0) a.ws.jsum[size_t(b) * a.nch + c] = s;
+}
+
+// Scan one chunk for the first running sum above tgt.  Returns the vocabulary
+// index (or INT32_MAX) and the margin through the shared outputs.
+__device__ void scan_chunk(const VerifyArgs& a, const DrawRow& r, bool resid, bool use_p, int c,
+                           double base, double tgt, int* s_pick, double* s_mg, double* s_ex) {
+  const int t = threadIdx.x;
+  const int start = c * VCH + t * VPT;
+  float wv[VPT];
+  double mine = 0.0;
+  for (int j = 0; j < VPT; ++j) {
+    int e = start + j;
+    float wgt = 0.f;
+    if (e < a.V) wgt = use_p ? draw_weight(r, a.c2, r.zt[e], 0.f, false)
+                             : draw_weight(r, a.c2, r.zt[e], resid ? r.zd[e] : 0.f, resid);
+    wv[j] = wgt;
+    mine += double(wgt);
+  }
+  // exclusive scan of the thread sums in thread order
+  s_ex[t] = mine;
+  __syncthreads();
+  if (t == 0) {
+    double run = 0.0;
+    for (int k = 0; k < VT; ++k) { double v = s_ex[k]; s_ex[k] = run; run += v; }
+  }
+  __syncthreads();
+  double run = base + s_ex[t];
+  int pick = INT32_MAX;
+  double mg = 0.0;
+  for (int j = 0; j < VPT; ++j) {
+    double prev = run;
+    run += double(wv[j]);
+    if (run > tgt) { pick = start + j; mg = fmin(tgt - prev, run - tgt); break; }
+  }
+  // lowest pick wins
+  int best = pick;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) best = min(best, __shfl_xor(best, o));
+  __syncthreads();
+  if (t == 0) *s_pick = INT32_MAX;
+  __syncthreads();
+  if ((t & 63) == 0) atomicMin(s_pick, best);
+  __syncthreads();
+  if (pick != INT32_MAX && pick == *s_pick) *s_mg = mg;
+  __syncthreads();
+}
+
+// last x in chunk c with a positive weight (INT32_MAX if none)
+__device__ int last_positive(const VerifyArgs& a, const DrawRow& r, bool resid, bool use_p, int c,
+                             int* s_pick) {
+  const int t = threadIdx.x;
+  int best = -1;
+  for (int j = 0; j < VPT; ++j) {
+    int e = c * VCH + t * VPT + j;
+    if (e < a.V) {
+      float wgt = use_p ? draw_weight(r, a.c2, r.zt[e], 0.f, false)
+                        : draw_weight(r, a.c2, r.zt[e], resid ? r.zd[e] : 0.f, resid);
+      if (wgt > 0.f) best = e;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) best = max(best, __shfl_xor(best, o));
+  __syncthreads();
+  if (t == 0) *s_pick = -1;
+  __syncthreads();
+  if ((t & 63) == 0) atomicMax(s_pick, best);
+  __syncthreads();
+  return *s_pick;
+}
+
+__global__ __launch_bounds__(VT) void vb_draw_pick(VerifyArgs a) {
+  __shared__ double s_ex[VT];
+  __shared__ double s_d[4];
+  __shared__ int s_pick;
+  __shared__ double s_mg;
+  __shared__ int s_chunk;
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int kind = a.ws.job[2 * b + 1];
+  if (kind == JOB_NONE) return;
+  const int pos = a.ws.job[2 * b];
+  bool resid = kind == JOB_RESID;
+  const DrawRow r = draw_row(a, b, pos, resid);
+  const float u2 = a.uni[(size_t(b) * (a.G + 1) + pos) * 2 + 1];
+  const double* cs = a.ws.jsum + size_t(b) * a.nch;
+
+  bool use_p = false;
+  double Z = 0.0;
+  for (int c = 0; c < a.nch; ++c) Z += cs[c];
+  double tot_p = 0.0;
+  if (resid && Z == 0.0) {
+    // every residual weight rounded to zero: draw from P instead
+    use_p = true;
+    for (int c = 0; c < a.nch; ++c) {
+      double s = 0.0;
+      for (int j = 0; j < VPT; ++j) {
+        int e = c * VCH + t * VPT + j;
+        if (e < a.V) s += double(draw_weight(r, a.c2, r.zt[e], 0.f, false));
+      }
+      tot_p += block_sum_f64(s, s_d);
+    }
+    Z = tot_p;
+  }
+  const double tgt = double(u2) * Z;
+  // chunk holding the crossing
+  if (t == 0) {
+    double run = 0.0;
+    int chunk = -1;
+    if (!use_p) {
+      for (int c = 0; c < a.nch; ++c) {
+        run += cs[c];
+        if (run > tgt) { chunk = c; break; }
+      }
+    }
+    s_chunk = chunk;
+  }
+  __syncthreads();
+  int chunk = s_chunk;
+  double base = 0.0;
+  int pick = INT32_MAX;
+  double mg = 0.0;
+  if (!use_p && chunk >= 0) {
+    for (int c = 0; c < chunk; ++c) base += cs[c];
+    scan_chunk(a, r, resid, false, chunk, base, tgt, &s_pick, &s_mg, s_ex);
+    pick = s_pick;
+    mg = s_mg;
+    if (pick == INT32_MAX) {
+      pick = last_positive(a, r, resid, false, chunk, &s_pick);
+      mg = 0.0;
+    }
+  } else if (use_p) {
+    // P-weights: walk chunk by chunk (rare path)
+    double run = 0.0;
+    for (int c = 0; c < a.nch && pick == INT32_MAX; ++c) {
+      scan_chunk(a, r, resid, true, c, run, tgt, &s_pick, &s_mg, s_ex);
+      if (s_pick != INT32_MAX) { pick = s_pick; mg = s_mg; break; }
+      double s = 0.0;
+      for (int j = 0; j < VPT; ++j) {
+        int e = c * VCH + t * VPT + j;
+        if (e < a.V) s += double(draw_weight(r, a.c2, r.zt[e], 0.f, false));
+      }
+      run += block_sum_f64(s, s_d);
+    }
+  }
+  if (pick == INT32_MAX || pick < 0) {
+    // no crossing anywhere: the last x with a positive weight
+    int last = -1;
+    for (int c = a.nch - 1; c >= 0 && last < 0; --c) last = last_positive(a, r, resid, use_p, c, &s_pick);
+    pick = last >= 0 ? last : a.V - 1;
+    mg = 0.0;
+  }
+  if (t == 0) {
+    a.out[b * (a.G + 1) + pos] = pick;
+    if (a.margin) a.margin[b] = float(mg);
+  }
+}
+
+// probabilities for the test path: full rows of the (filtered) P and Q
+__global__ __launch_bounds__(VT) void vb_write_probs(VerifyArgs a) {
+  const int row = blockIdx.x / a.nch;
+  const int c = blockIdx.x - row * a.nch;
+  const int t = threadIdx.x;
+  float* dst;
+  if (row < a.n_trows) {
+    if (!a.tprob) return;
+    dst = a.tprob + size_t(row) * a.V;
+  } else {
+    if (!a.dprob) return;
+    dst = a.dprob + size_t(row - a.n_trows) * a.V;
+  }
+  const float* z = row_ptr(a, row);
+  const float m = a.ws.rmax[row];
+  const bool filt = a.topk > 0 && !a.greedy;
+  const float inv = float(1.0 / a.ws.rsum[row]);
+  for (int j = 0; j < VPT; ++j) {
+    int e = c * VCH + j * VT + t;
+    if (e >= a.V) break;
+    float p;
+    if (filt) p = float(kept_prob(a, row, e));
+    else p = exp2f((z[e] - m) * a.c2) * inv;
+    dst[e] = p;
+  }
+}
+
+// -------------------------------------------------------------------------
+// host side
+// -------------------------------------------------------------------------
+static inline size_t al(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct VerifyLayout {
+  size_t cmax, carg, csum, ctv, cti, rmax, rarg, rsum, rkn, rki, rkp, job, jsum, total;
+};
+
+static VerifyLayout verify_layout(int B, int G, int V, int top_k) {
+  VerifyLayout L{};
+  const size_t nch = (size_t(V) + VCH - 1) / VCH;
+  const size_t rows = size_t(B) * (2 * G + 1);
+  const size_t rc = rows * nch;
+  const size_t k = top_k > 0 ? size_t(top_k) : 0;
+  size_t o = 0;
+  L.cmax = o; o += al(rc * 4);
+  L.carg = o; o += al(rc * 4);
+  L.csum = o; o += al(rc * 8);
+  L.ctv = o; o += al(rc * k * 4);
+  L.cti = o; o += al(rc * k * 4);
+  L.rmax = o; o += al(rows * 4);
+  L.rarg = o; o += al(rows * 4);
+  L.rsum = o; o += al(rows * 8);
+  L.rkn = o; o += al(rows * 4);
+  L.rki = o; o += al(k ? rows * TOPK_MAX * 4 : 0);
+  L.rkp = o; o += al(k ? rows * TOPK_MAX * 8 : 0);
+  L.job = o; o += al(size_t(B) * 2 * 4);
+  L.jsum = o; o += al(size_t(B) * nch * 8);
+  L.total = o;
+  return L;
+}
+
+size_t verify_ws_bytes(int B, int G, int V, int top_k) {
+  if (B <= 0) return 0;
+  return verify_layout(B, G, V, top_k).total;
+}
+
+hipError_t launch_verify(const float* zt, const float* zd, const int* dtok, const float* uni,
+                         int B, int G, int V, float temperature, int top_k, float top_p,
+                         int* tau, int* out, float* tprob, float* dprob, float* ratio, float* margin,
+                         void* ws, hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  const bool greedy = temperature == 0.0f;
+  const int k = (!greedy && top_k > 0 && top_k < V) ? top_k : 0;
+  VerifyLayout L = verify_layout(B, G, V, k);
+  char* w = static_cast<char*>(ws);
+  VerifyArgs a{};
+  a.zt = zt; a.zd = zd; a.dtok = dtok; a.uni = uni;
+  a.B = B; a.G = G; a.V = V;
+  a.nch = (V + VCH - 1) / VCH;
+  a.n_trows = B * (G + 1);
+  const bool draft_rows = !greedy || dprob != nullptr;
+  a.n_rows = a.n_trows + (draft_rows && zd ? B * G : 0);
+  a.T = greedy ? 1.0f : temperature;
+  a.c2 = float(1.4426950408889634 / double(a.T));
+  a.greedy = greedy;
+  a.topk = k;
+  a.top_p = greedy ? 1.0f : top_p;
+  a.need_sum = (!greedy && k == 0) || (greedy && (tprob || dprob));
+  a.tau = tau; a.out = out; a.tprob = tprob; a.dprob = dprob; a.ratio = ratio; a.margin = margin;
+  a.ws.cmax = reinterpret_cast<float*>(w + L.cmax);
+  a.ws.carg = reinterpret_cast<int*>(w + L.carg);
+  a.ws.csum = reinterpret_cast<double*>(w + L.csum);
+  a.ws.ctv = reinterpret_cast<float*>(w + L.ctv);
+  a.ws.cti = reinterpret_cast<int*>(w + L.cti);
+  a.ws.rmax = reinterpret_cast<float*>(w + L.rmax);
+  a.ws.rarg = reinterpret_cast<int*>(w + L.rarg);
+  a.ws.rsum = reinterpret_cast<double*>(w + L.rsum);
+  a.ws.rkn = reinterpret_cast<int*>(w + L.rkn);
+  a.ws.rki = reinterpret_cast<int*>(w + L.rki);
+  a.ws.rkp = reinterpret_cast<double*>(w + L.rkp);
+  a.ws.job = reinterpret_cast<int*>(w + L.job);
+  a.ws.jsum = reinterpret_cast<double*>(w + L.jsum);
+
+  const unsigned nblk = unsigned(a.n_rows) * unsigned(a.nch);
+  if ((V & 3) == 0)
+    hipLaunchKernelGGL(vb_stats<true>, dim3(nblk), dim3(VT), 0, stream, a);
+  else
+    hipLaunchKernelGGL(vb_stats<false>, dim3(nblk), dim3(VT), 0, stream, a);
+  hipLaunchKernelGGL(vb_decide, dim3(B), dim3(256), 0, stream, a);
+  if (!greedy && k == 0) {
+    hipLaunchKernelGGL(vb_draw_sums, dim3(a.nch, B), dim3(VT), 0, stream, a);
+    hipLaunchKernelGGL(vb_draw_pick, dim3(B), dim3(VT), 0, stream, a);
+  }
+  if (tprob || dprob)
+    hipLaunchKernelGGL(vb_write_probs, dim3(nblk), dim3(VT), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace bd

@@ -1,0 +1,186 @@
+/*
+ * blockdraft.h -- C ABI of the block-draft round on one MI355X (gfx950).
+ *
+ * Three calls make one round of block-parallel speculative decoding:
+ *   inject_kv         project the target's concatenated multi-layer hidden
+ *                     states into every draft layer's K/V cache;
+ *   draft_block_attn  attention of the K block positions over the injected
+ *                     context K/V plus the block's own K/V (one layer);
+ *   verify_block      greedy prefix matching or lossless rejection sampling
+ *                     of the drafted tokens against the target's logits.
+ *
+ * Sources (cited by page title and section):
+ *   "The Next Generation of Speculative Decoding: DFlash and Spec V2"
+ *     (lmsys.org blog; "DFlash/Spec V2 blog"): summary and A2 give the KV
+ *     injection KV_draft^(l) = Projection^(l)(H_target) into every draft
+ *     layer; A7 gives immediate materialization through one layer-batched
+ *     projection with fused Norm + RoPE post-processing.
+ *   "Tencent open-sources DSpine" ("DSpine article"): block 16 = 1 anchor +
+ *     15 drafted positions, 8192-token sliding window ("what these weights
+ *     are"); DFlash's in-block attention is bidirectional ("principle").
+ *   DeepSeek DSpark tutorial ("DSpark tutorial"), "speculative decoding
+ *     basics": prefix acceptance, a replacement token at the first
+ *     disagreement, one extra token per round, and losslessness.
+ *   "Didi EAGLE-3 training/inference practice", 5.3: partial attention
+ *     results merge exactly through their log-sum-exp.
+ *
+ * Conventions shared by every call
+ *   - Pointers named as device memory are owned by the caller; the library
+ *     never allocates, frees or keeps them.  Scratch space comes in through
+ *     (workspace, workspace_bytes); the *_workspace_size functions give the
+ *     size needed.
+ *   - Calls are asynchronous on the caller's stream and never synchronise.
+ *   - Arrays are dense and row-major; bf16 values are passed as uint16_t bit
+ *     patterns; bf16 results are rounded to nearest, ties to even.
+ *   - Every call checks its arguments on the host first and returns a status
+ *     without launching anything (outputs untouched) when they are invalid;
+ *     blockdraft_last_error() then gives a text for the calling thread.
+ *     Per-request values that live on the device (context lengths, slots,
+ *     token ids) cannot be checked on the host: the kernels never read or
+ *     write outside [0, T_cap) or [0, V) because of them, and the affected
+ *     request's outputs are undefined (attention writes NaN).
+ *   - Results are deterministic: fixed reduction orders, no float atomics.
+ *   - NaN inputs give undefined results.
+ */
+#ifndef BLOCKDRAFT_H
+#define BLOCKDRAFT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  BD_OK = 0,
+  BD_E_NULL = -1,        /* a required pointer is NULL                      */
+  BD_E_SHAPE = -2,       /* inconsistent or negative sizes                  */
+  BD_E_UNSUPPORTED = -3, /* valid but outside the supported shapes          */
+  BD_E_WORKSPACE = -4,   /* workspace smaller than *_workspace_size says    */
+  BD_E_LAUNCH = -5       /* the HIP runtime reported an error at launch     */
+};
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* blockdraft_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * inject_kv -- KV injection (DFlash/Spec V2 blog, summary, A2 and A7).
+ *
+ * For every row m of H (one token) and every draft layer l:
+ *   y = H[m] . W^T  (fp32 accumulation of bf16 products), all layers at once;
+ *   K head g = y[l][K][g] / sqrt(mean over hd of y^2 + rms_eps) * k_norm_w[l],
+ *   then the half-split rotary embedding at the row's absolute position:
+ *   dims (i, i + hd/2) turn by pos * rope_theta^(-2i/hd);
+ *   V head g = y[l][V][g] unchanged;
+ *   both rounded to bf16 and written to slot cache_base[b] + row_pos0[b] + j,
+ *   where row m is the j-th row of request b (row_cu[b] <= m < row_cu[b+1]).
+ *
+ * h_target    device bf16 [M, d_in]: concatenated target-layer hidden states.
+ * w_kv        device bf16 [L*2*n_kv*hd, d_in]: rows ordered [l][K|V][head][dim].
+ * k_norm_w    device bf16 [L, hd] RMSNorm gains of K, or NULL for ones.
+ * row_cu      device int32 [B+1]: request row offsets, row_cu[0] = 0,
+ *             nondecreasing, row_cu[B] <= M (rows past row_cu[B] are not
+ *             written).
+ * row_pos0    device int32 [B]: absolute position of each request's first row.
+ * cache_base  device int64 [B]: slot of position 0 of each request.
+ * k_cache, v_cache  device bf16 [L, T_cap, n_kv, hd], updated in place; a row
+ *             whose slot falls outside [0, T_cap) is skipped.
+ * Supported: hd in {64, 128}; d_in a positive multiple of 64; 1 <= n_kv <= 64.
+ * ------------------------------------------------------------------------ */
+size_t inject_kv_workspace_size(int32_t M, int32_t d_in, int32_t L, int32_t n_kv, int32_t hd);
+
+int inject_kv(const uint16_t* h_target, const uint16_t* w_kv, const uint16_t* k_norm_w,
+              const int32_t* row_cu, const int32_t* row_pos0, const int64_t* cache_base,
+              uint16_t* k_cache, uint16_t* v_cache, int64_t T_cap,
+              int32_t B, int32_t M, int32_t d_in, int32_t L, int32_t n_kv, int32_t hd,
+              float rope_theta, float rms_eps,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * draft_block_attn -- block-draft attention of one layer (DFlash/Spec V2
+ * blog, A2; DSpine article, "principle" and "what these weights are";
+ * Didi EAGLE-3 article, 5.3 for the exact split-and-merge).
+ *
+ * For request b, query head h (KV head g = h / (n_q / n_kv)) and block
+ * position i, the keys are the context positions [lo, ctx_len[b]) with
+ * lo = max(0, ctx_len[b] - window) (lo = 0 when window == 0), read from slots
+ * cache_base[b] + p, followed by the K in-block keys k_blk[b, :, g]; every
+ * block position sees all of them (no mask).
+ *   out[b, i, h] = softmax(q . keys^T * scale) . values   (bf16)
+ *   lse[b, i, h] = log sum exp(q . keys^T * scale)          (fp32, natural log)
+ *
+ * q           device bf16 [B, K, n_q, hd] (already normalised / rotated).
+ * k_blk, v_blk device bf16 [B, K, n_kv, hd].
+ * k_cache, v_cache device bf16 [T_cap, n_kv, hd]: this layer's caches.
+ * cache_base  device int64 [B]; ctx_len device int32 [B], 0 <= ctx_len <= max_ctx.
+ * max_ctx     host upper bound of ctx_len (sizes the grid).
+ * window      0 = whole context, else the sliding-window length.
+ * scale       <= 0 selects 1/sqrt(hd).
+ * out         device bf16 [B, K, n_q, hd]; lse device fp32 [B, K, n_q] or NULL.
+ * Supported: hd in {64, 128}; 1 <= K <= 64; (n_q / n_kv) * K <= 128.
+ * ------------------------------------------------------------------------ */
+size_t draft_block_attn_workspace_size(int32_t B, int32_t K, int32_t n_q, int32_t n_kv, int32_t hd,
+                                       int32_t max_ctx, int32_t window);
+
+int draft_block_attn(const uint16_t* q, const uint16_t* k_blk, const uint16_t* v_blk,
+                     const uint16_t* k_cache, const uint16_t* v_cache,
+                     const int64_t* cache_base, const int32_t* ctx_len,
+                     int64_t T_cap, int32_t max_ctx,
+                     int32_t B, int32_t K, int32_t n_q, int32_t n_kv, int32_t hd,
+                     int32_t window, float scale,
+                     uint16_t* out, float* lse,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * verify_block -- verification of G drafted tokens per request (DSpark
+ * tutorial, "speculative decoding basics"; DSpine article, "principle" for
+ * greedy matching and "speed-up" for the sampling filters).
+ *
+ * Greedy (temperature == 0): d_i is kept while it equals the lowest-index
+ * maximum of the target's raw logits at position i; the emitted token at the
+ * first mismatch (or after G matches) is that maximum.
+ * Sampling (temperature > 0): P_i = filt(softmax(z_t,i / T)),
+ * Q_i = filt(softmax(z_d,i / T)); filt = keep the top_k largest raw logits
+ * (value desc, index asc; off when top_k == 0), softmax over them, keep the
+ * shortest prefix in probability order whose mass reaches top_p (off when
+ * top_p >= 1), renormalise.  d_i is kept while u_i < fp32(P_i(d_i)) /
+ * fp32(Q_i(d_i)) (IEEE fp32 division).  At the first rejection i the token is
+ * the smallest x (vocab order) whose running sum of max(0, P_i - Q_i) exceeds
+ * u'_i times its total (P_i itself if that total is 0); with every draft kept
+ * the same draw runs over P_{G+1} with u'_{G+1}.
+ *
+ * target_logits device fp32 [B, G+1, V]; draft_logits device fp32 [B, G, V]
+ *             (may be NULL when greedy and draft_probs is NULL).
+ * draft_tokens device int32 [B, G]; a token outside [0, V) is rejected.
+ * uniforms    device fp32 [B, G+1, 2] in [0, 1): [b, i, 0] accepts position i,
+ *             [b, i, 1] draws the replacement / extra token at position i;
+ *             may be NULL when greedy.
+ * tau         device int32 [B]: accepted drafted tokens, 0..G.
+ * out_tokens  device int32 [B, G+1]: d_1..d_tau, then the replacement or
+ *             extra token, then -1.
+ * target_probs, draft_probs  optional device fp32 [B, G+1, V] / [B, G, V]:
+ *             the (filtered) P and Q; with temperature 0 the plain softmax.
+ * accept_ratio optional device fp32 [B, G]: the ratio each accept test used
+ *             (greedy: 1 on a match, else 0).
+ * sample_margin optional device fp32 [B]: distance of u' * total to the
+ *             nearer running-sum boundary of the drawn token (greedy: +inf).
+ * Supported: 0 <= top_k <= 64; G <= 64; V >= 1.
+ * ------------------------------------------------------------------------ */
+size_t verify_block_workspace_size(int32_t B, int32_t G, int32_t V, int32_t top_k);
+
+int verify_block(const float* target_logits, const float* draft_logits,
+                 const int32_t* draft_tokens, const float* uniforms,
+                 int32_t B, int32_t G, int32_t V,
+                 float temperature, int32_t top_k, float top_p,
+                 int32_t* tau, int32_t* out_tokens,
+                 float* target_probs, float* draft_probs,
+                 float* accept_ratio, float* sample_margin,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLOCKDRAFT_H */

@@ -1,0 +1,170 @@
+"""GPU parity of draft_block_attn against the oracle (called through the C ABI).
+
+Bar: per (request, layer) slice, max |gpu - oracle| / max |oracle| <= 2e-2 for
+the bf16 output (bf16 inputs, fp32 accumulation); lse within 1e-3 absolute.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import attention as oa
+from tests.helpers import bits_to_f64, cuda_bits, host_bits, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def case(B, K, n_q, n_kv, hd, ctx, seed, extra_slots=0):
+    rng = np.random.default_rng(seed)
+    ctx = np.asarray(ctx, dtype=np.int32)
+    base, T = wl.cache_layout(ctx, K)
+    T += extra_slots
+    q, _ = wl.bf16_normal(rng, (B, K, n_q, hd))
+    kb, _ = wl.bf16_normal(rng, (B, K, n_kv, hd))
+    vb, _ = wl.bf16_normal(rng, (B, K, n_kv, hd))
+    kc, _ = wl.bf16_normal(rng, (T, n_kv, hd))
+    vc, _ = wl.bf16_normal(rng, (T, n_kv, hd))
+    return q, kb, vb, kc, vc, base, ctx, T
+
+
+def run_gpu(q, kb, vb, kc, vc, base, ctx, window, scale=0.0, max_ctx=None, with_lse=True):
+    import block_drafting_amd as bd
+    B, K, n_q, hd = q.shape
+    max_ctx = int(ctx.max()) if max_ctx is None else max_ctx
+    lse = torch.full((B, K, n_q), -7.0, dtype=torch.float32, device="cuda") if with_lse else None
+    out, lse = bd.draft_block_attn(cuda_bits(q), cuda_bits(kb), cuda_bits(vb), cuda_bits(kc), cuda_bits(vc),
+                                   torch.from_numpy(base).cuda(), torch.from_numpy(ctx).cuda(), max_ctx,
+                                   window, scale, lse=lse)
+    torch.cuda.synchronize()
+    return bits_to_f64(host_bits(out)), (lse.cpu().numpy() if with_lse else None)
+
+
+def check(q, kb, vb, kc, vc, base, ctx, window, scale=0.0, label="", **kw):
+    say(f"attention {label} q={q.shape} ctx={list(ctx)[:6]} window={window}")
+    go, gl = run_gpu(q, kb, vb, kc, vc, base, ctx, window, scale, **kw)
+    oo, ol = oa.block_attn(bits_to_f64(q), bits_to_f64(kb), bits_to_f64(vb), bits_to_f64(kc), bits_to_f64(vc),
+                           base, ctx, window, scale)
+    worst = max(rel_err(go[b], oo[b]) for b in range(q.shape[0]))
+    say(f"  worst relative error {worst:.2e}, lse max abs err {np.abs(gl - ol).max():.2e}")
+    assert worst <= TOL
+    assert np.abs(gl - ol).max() <= 1e-3
+    return worst
+
+
+@pytest.mark.parametrize("window", [0, 100])
+def test_tiny_config_shape(window):
+    cfg = wl.CONFIGS["tiny"]
+    check(*case(1, cfg.K, cfg.n_q, cfg.n_kv, cfg.hd, [512], 0)[:7], window, label="tiny")
+
+
+@pytest.mark.parametrize("window", [0, 100, 64])
+def test_ragged_contexts(window):
+    check(*case(6, 16, 32, 8, 128, [0, 1, 63, 64, 1000, 130], 1)[:7], window, label="ragged")
+
+
+def test_group5_two_row_blocks():
+    # 40 query heads over 8 KV heads, K = 16: 80 query rows per item
+    check(*case(2, 16, 40, 8, 128, [3000, 17], 2)[:7], 1024, label="group5")
+
+
+def test_hd64_128_rows():
+    check(*case(3, 64, 4, 2, 64, [700, 5, 129], 3)[:7], 0, label="hd64 K64")
+
+
+def test_custom_scale_and_no_lse():
+    q, kb, vb, kc, vc, base, ctx, _ = case(2, 8, 8, 2, 128, [300, 40], 4)
+    check(q, kb, vb, kc, vc, base, ctx, 0, scale=0.05, label="scale")
+    go, _ = run_gpu(q, kb, vb, kc, vc, base, ctx, 0, with_lse=False)
+    oo, _ = oa.block_attn(bits_to_f64(q), bits_to_f64(kb), bits_to_f64(vb), bits_to_f64(kc), bits_to_f64(vc),
+                          base, ctx, 0)
+    assert max(rel_err(go[b], oo[b]) for b in range(2)) <= TOL
+
+
+def test_max_ctx_larger_than_needed():
+    q, kb, vb, kc, vc, base, ctx, _ = case(2, 16, 32, 8, 128, [200, 900], 5)
+    check(q, kb, vb, kc, vc, base, ctx, 0, label="max_ctx slack", max_ctx=5000)
+
+
+def test_window_never_reads_outside():
+    """Slots outside the window hold NaN: any read of them would poison the output."""
+    q, kb, vb, kc, vc, base, ctx, _ = case(3, 16, 32, 8, 128, [5000, 2100, 300], 6)
+    W = 2048
+    kc2, vc2 = kc.copy(), vc.copy()
+    for b in range(3):
+        lo = max(0, ctx[b] - W)
+        kc2[base[b]: base[b] + lo] = 0x7FC0
+        vc2[base[b]: base[b] + lo] = 0x7FC0
+    go, gl = run_gpu(q, kb, vb, kc2, vc2, base, ctx, W)
+    assert np.isfinite(go).all() and np.isfinite(gl).all()
+    check(q, kb, vb, kc, vc, base, ctx, W, label="window")
+
+
+def test_invalid_request_metadata_gives_nan_not_fault():
+    q, kb, vb, kc, vc, base, ctx, T = case(3, 16, 32, 8, 128, [100, 200, 300], 7)
+    bad = ctx.copy()
+    bad[1] = 10_000  # beyond max_ctx and beyond the cache
+    go, _ = run_gpu(q, kb, vb, kc, vc, base, bad, 0, max_ctx=400)
+    assert np.isnan(go[1]).all()
+    assert np.isfinite(go[0]).all() and np.isfinite(go[2]).all()
+
+
+def test_deterministic_run_to_run():
+    args = case(4, 16, 32, 8, 128, [1500, 77, 3000, 640], 8)[:7]
+    a = run_gpu(*args, 0)
+    b = run_gpu(*args, 0)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_full_size_8b_layer_sampled_requests():
+    """The batch-32 ragged workload (U[512, 4096] contexts) at full size on the
+    GPU; the oracle checks four requests."""
+    cfg = wl.CONFIGS["qwen3-8b"]
+    r = wl.make_round(cfg, parts=("attn",))
+    rng = np.random.default_rng(9)
+    kc, _ = wl.bf16_normal(rng, (r.T_cap, cfg.n_kv, cfg.hd))
+    vc, _ = wl.bf16_normal(rng, (r.T_cap, cfg.n_kv, cfg.hd))
+    q, kb, vb = r.q_bits[0], r.k_blk_bits[0], r.v_blk_bits[0]
+    say(f"full-size qwen3-8b layer, T_cap={r.T_cap}")
+    go, gl = run_gpu(q, kb, vb, kc, vc, r.cache_base, r.ctx_len, 0, max_ctx=cfg.ctx_b)
+    for b in (0, 7, 19, 31):
+        sub = slice(b, b + 1)
+        s0, s1 = int(r.cache_base[b]), int(r.cache_base[b] + r.ctx_len[b])
+        oo, ol = oa.block_attn(bits_to_f64(q[sub]), bits_to_f64(kb[sub]), bits_to_f64(vb[sub]),
+                               bits_to_f64(kc[s0:s1]), bits_to_f64(vc[s0:s1]), np.array([0]), r.ctx_len[sub], 0)
+        e = rel_err(go[b], oo[0])
+        say(f"  request {b} ctx={r.ctx_len[b]} rel err {e:.2e}")
+        assert e <= TOL
+        assert np.abs(gl[b] - ol[0]).max() <= 1e-3
+
+
+def test_full_size_27b_window_sampled_requests():
+    """Batch 8, 32768-token contexts, 8192-token window, 40 query heads."""
+    cfg = wl.CONFIGS["27b-long"]
+    r = wl.make_round(cfg, parts=("attn",))
+    rng = np.random.default_rng(10)
+    n_kv, hd = cfg.n_kv, cfg.hd
+    # only the window (plus a NaN guard just below it) is materialised
+    kc = np.full((r.T_cap, n_kv, hd), 0x7FC0, np.uint16)
+    vc = np.full((r.T_cap, n_kv, hd), 0x7FC0, np.uint16)
+    for b in range(cfg.B):
+        lo = r.cache_base[b] + r.ctx_len[b] - cfg.window
+        kc[lo: lo + cfg.window], _ = wl.bf16_normal(rng, (cfg.window, n_kv, hd))
+        vc[lo: lo + cfg.window], _ = wl.bf16_normal(rng, (cfg.window, n_kv, hd))
+    q, kb, vb = r.q_bits[0], r.k_blk_bits[0], r.v_blk_bits[0]
+    say("full-size 27b-long layer")
+    go, gl = run_gpu(q, kb, vb, kc, vc, r.cache_base, r.ctx_len, cfg.window, max_ctx=cfg.ctx_a)
+    assert np.isfinite(go).all()
+    for b in (0, 5):
+        sub = slice(b, b + 1)
+        lo = r.cache_base[b] + r.ctx_len[b] - cfg.window
+        # the oracle sees a compact cache holding only the window
+        oo, ol = oa.block_attn(bits_to_f64(q[sub]), bits_to_f64(kb[sub]), bits_to_f64(vb[sub]),
+                               bits_to_f64(kc[lo: lo + cfg.window]), bits_to_f64(vc[lo: lo + cfg.window]),
+                               np.array([0]), np.array([cfg.window]), 0)
+        e = rel_err(go[b], oo[0])
+        say(f"  request {b} rel err {e:.2e}")
+        assert e <= TOL
+        assert np.abs(gl[b] - ol[0]).max() <= 1e-3

@@ -1,0 +1,137 @@
+"""GPU parity of inject_kv against the oracle (called through the C ABI).
+
+Bar: for every written slot, per layer, max |gpu - oracle| / max |oracle|
+<= 2e-2 for K and for V (bf16 inputs, fp32 accumulation, bf16 outputs); every
+slot the call must not write keeps its old bits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import inject as oi
+from tests.helpers import bits_to_f64, cuda_bits, host_bits, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+SENTINEL = 0x3F80  # bf16 1.0
+
+
+def run_case(L, n_kv, hd, d_in, rows_per_req, pos0, seed, gains=True, theta=1e6, eps=1e-6, extra=7,
+             w_std=0.02):
+    rng = np.random.default_rng(seed)
+    B = len(rows_per_req)
+    row_cu = np.zeros(B + 1, np.int32)
+    row_cu[1:] = np.cumsum(rows_per_req)
+    M = int(row_cu[-1])
+    pos0 = np.asarray(pos0, np.int32)
+    span = pos0.astype(np.int64) + np.asarray(rows_per_req) + extra
+    base = np.zeros(B, np.int64)
+    base[1:] = np.cumsum(span)[:-1]
+    T_cap = int(span.sum())
+    h, _ = wl.bf16_normal(rng, (M, d_in))
+    w, _ = wl.bf16_normal(rng, (L * 2 * n_kv * hd, d_in), std=w_std)
+    g = wl.to_bf16_bits((1.0 + 0.3 * rng.standard_normal((L, hd))).astype(np.float32)) if gains else None
+    import block_drafting_amd as bd
+    kc = torch.full((L, T_cap, n_kv, hd), SENTINEL, dtype=torch.int16, device="cuda")
+    vc = torch.full((L, T_cap, n_kv, hd), SENTINEL, dtype=torch.int16, device="cuda")
+    say(f"inject L={L} n_kv={n_kv} hd={hd} d_in={d_in} M={M} rows={list(rows_per_req)[:6]}")
+    bd.inject_kv(cuda_bits(h), cuda_bits(w), cuda_bits(g) if gains else None,
+                 torch.from_numpy(row_cu).cuda(), torch.from_numpy(pos0).cuda(), torch.from_numpy(base).cuda(),
+                 kc, vc, theta, eps)
+    torch.cuda.synchronize()
+    gk, gv = host_bits(kc), host_bits(vc)
+    ok = np.full((L, T_cap, n_kv, hd), 1.0)
+    ov_ = np.full((L, T_cap, n_kv, hd), 1.0)
+    oi.inject_kv(bits_to_f64(h), bits_to_f64(w), bits_to_f64(g) if gains else None, row_cu, pos0, base,
+                 ok, ov_, L, n_kv, hd, theta, eps)
+    written = np.zeros(T_cap, bool)
+    for b in range(B):
+        s0 = base[b] + pos0[b]
+        written[s0: s0 + rows_per_req[b]] = True
+    worst = 0.0
+    for l in range(L):
+        if written.any():
+            worst = max(worst, rel_err(bits_to_f64(gk[l, written]), ok[l, written]),
+                        rel_err(bits_to_f64(gv[l, written]), ov_[l, written]))
+    assert (gk[:, ~written] == SENTINEL).all() and (gv[:, ~written] == SENTINEL).all()
+    say(f"  worst relative error {worst:.2e}")
+    assert worst <= TOL
+    return worst
+
+
+def test_tiny_config_round_and_prefill():
+    cfg = wl.CONFIGS["tiny"]
+    run_case(cfg.L, cfg.n_kv, cfg.hd, cfg.d_in, [cfg.K], [512], 0)        # one round: 8 rows at 512..519
+    run_case(cfg.L, cfg.n_kv, cfg.hd, cfg.d_in, [512], [0], 1)            # prefill of the context
+
+
+def test_ragged_requests_large_positions():
+    run_case(3, 4, 128, 1024, [5, 0, 70, 1], [0, 3, 32000, 32767 - 1], 2)
+
+
+def test_m_above_128_uses_big_tiles():
+    run_case(2, 8, 128, 512, [150, 150], [100, 0], 3)
+
+
+def test_no_gains_hd64():
+    run_case(2, 3, 64, 640, [40, 9], [7, 1000], 4, gains=False)
+
+
+def test_rows_past_row_cu_end_are_not_written():
+    """row_cu[B] < M: trailing rows of H are ignored."""
+    import block_drafting_amd as bd
+    rng = np.random.default_rng(5)
+    L, n_kv, hd, d_in, M = 1, 2, 64, 256, 20
+    h, _ = wl.bf16_normal(rng, (M, d_in))
+    w, _ = wl.bf16_normal(rng, (L * 2 * n_kv * hd, d_in), std=0.02)
+    kc = torch.full((L, 40, n_kv, hd), SENTINEL, dtype=torch.int16, device="cuda")
+    vc = torch.full((L, 40, n_kv, hd), SENTINEL, dtype=torch.int16, device="cuda")
+    bd.inject_kv(cuda_bits(h), cuda_bits(w), None, torch.tensor([0, 12], dtype=torch.int32, device="cuda"),
+                 torch.tensor([0], dtype=torch.int32, device="cuda"),
+                 torch.tensor([0], dtype=torch.int64, device="cuda"), kc, vc)
+    torch.cuda.synchronize()
+    gk = host_bits(kc)
+    assert (gk[:, 12:] == SENTINEL).all() and (gk[:, :12] != SENTINEL).any()
+
+
+def test_deterministic_run_to_run():
+    a = run_case(2, 8, 128, 2048, [64, 64], [10, 4000], 6)
+    b = run_case(2, 8, 128, 2048, [64, 64], [10, 4000], 6)
+    assert a == b
+
+
+def test_full_size_8b_round_sampled_rows():
+    """M = 512 rows (B = 32, K = 16), d_in = 20480, 5 layers x 8 heads x 128:
+    the full-size projection on the GPU; the oracle checks 8 rows."""
+    import block_drafting_amd as bd
+    cfg = wl.CONFIGS["qwen3-8b"]
+    r = wl.make_round(cfg, parts=("inject",), random_gains=True)
+    say(f"full-size qwen3-8b inject M={cfg.B * cfg.K}")
+    T_cap = r.T_cap
+    kc = torch.full((cfg.L, T_cap, cfg.n_kv, cfg.hd), SENTINEL, dtype=torch.int16, device="cuda")
+    vc = torch.full((cfg.L, T_cap, cfg.n_kv, cfg.hd), SENTINEL, dtype=torch.int16, device="cuda")
+    bd.inject_kv(cuda_bits(r.h_round_bits), cuda_bits(r.w_bits), cuda_bits(r.k_norm_bits),
+                 torch.from_numpy(r.row_cu).cuda(), torch.from_numpy(r.row_pos0).cuda(),
+                 torch.from_numpy(r.cache_base).cuda(), kc, vc, cfg.rope_theta, cfg.rms_eps)
+    torch.cuda.synchronize()
+    gk, gv = host_bits(kc), host_bits(vc)
+    rows = np.array([0, 15, 16, 100, 257, 300, 498, 511])
+    w = bits_to_f64(r.w_bits)
+    h = bits_to_f64(r.h_round_bits[rows])
+    g = bits_to_f64(r.k_norm_bits)
+    b_of = rows // cfg.K
+    j_of = rows % cfg.K
+    row_cu = np.arange(len(rows) + 1, dtype=np.int32)
+    pos0 = (r.row_pos0[b_of] + j_of).astype(np.int32)
+    slots = r.cache_base[b_of] + pos0
+    ok = np.zeros((cfg.L, len(rows), cfg.n_kv, cfg.hd))
+    ov_ = np.zeros((cfg.L, len(rows), cfg.n_kv, cfg.hd))
+    oi.inject_kv(h, w, g, row_cu, pos0, np.arange(len(rows)) - pos0, ok, ov_, cfg.L, cfg.n_kv, cfg.hd,
+                 cfg.rope_theta, cfg.rms_eps)
+    for l in range(cfg.L):
+        ek = rel_err(bits_to_f64(gk[l, slots]), ok[l])
+        ev = rel_err(bits_to_f64(gv[l, slots]), ov_[l])
+        say(f"  layer {l}: K rel err {ek:.2e}  V rel err {ev:.2e}")
+        assert ek <= TOL and ev <= TOL

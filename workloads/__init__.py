@@ -238,37 +238,38 @@ def uniforms(cfg: Config, st, B: Optional[int] = None) -> np.ndarray:
     return st["uniforms"].random((B, cfg.G + 1, 2), dtype=np.float32)
 
 
-def make_round(cfg: Config, seed: int = 0, with_logits: bool = True,
+def make_round(cfg: Config, seed: int = 0, parts=("inject", "attn", "verify"),
                random_gains: bool = False) -> RoundInputs:
-    """All inputs of one round of ``cfg``. Context caches are not drawn here
-    (see ``context_hidden``)."""
+    """Inputs of one round of ``cfg``; ``parts`` selects which tensors to draw
+    (each tensor has its own stream, so skipping one changes no other).
+    Context caches are not drawn here (see ``context_hidden``)."""
     st = streams(seed)
     ctx = ctx_lengths(cfg, st["ctx_len"])
     base, tcap = cache_layout(ctx, cfg.K, cfg.window)
     rows = cfg.B * cfg.K
-    h_bits, _ = bf16_normal(st["h_round"], (rows, cfg.d_in))
-    w_bits, _ = bf16_normal(st["w_kv"], (cfg.n_out, cfg.d_in), std=cfg.w_std)
-    if random_gains:
-        g = 1.0 + 0.25 * st["k_norm_w"].standard_normal((cfg.L, cfg.hd), dtype=np.float32)
-        g_bits = to_bf16_bits(g)
-    else:
-        g_bits = to_bf16_bits(np.ones((cfg.L, cfg.hd), dtype=np.float32))
-    q_bits, _ = bf16_normal(st["q"], (cfg.L, cfg.B, cfg.K, cfg.n_q, cfg.hd))
-    kb_bits, _ = bf16_normal(st["kv_blk"], (cfg.L, cfg.B, cfg.K, cfg.n_kv, cfg.hd))
-    vb_bits, _ = bf16_normal(st["kv_blk"], (cfg.L, cfg.B, cfg.K, cfg.n_kv, cfg.hd))
-    if with_logits:
+    empty16 = np.zeros(0, np.uint16)
+    h_bits = w_bits = g_bits = q_bits = kb_bits = vb_bits = empty16
+    if "inject" in parts:
+        h_bits, _ = bf16_normal(st["h_round"], (rows, cfg.d_in))
+        w_bits, _ = bf16_normal(st["w_kv"], (cfg.n_out, cfg.d_in), std=cfg.w_std)
+        if random_gains:
+            g = 1.0 + 0.25 * st["k_norm_w"].standard_normal((cfg.L, cfg.hd), dtype=np.float32)
+            g_bits = to_bf16_bits(g)
+        else:
+            g_bits = to_bf16_bits(np.ones((cfg.L, cfg.hd), dtype=np.float32))
+    if "attn" in parts:
+        q_bits, _ = bf16_normal(st["q"], (cfg.L, cfg.B, cfg.K, cfg.n_q, cfg.hd))
+        kb_bits, _ = bf16_normal(st["kv_blk"], (cfg.L, cfg.B, cfg.K, cfg.n_kv, cfg.hd))
+        vb_bits, _ = bf16_normal(st["kv_blk"], (cfg.L, cfg.B, cfg.K, cfg.n_kv, cfg.hd))
+    if "verify" in parts:
         zt, zd = logits(cfg, st)
         dt = draft_tokens(cfg, zd, st)
-        u = uniforms(cfg, st)
-        if cfg.temperature == 0.0:
-            zd_keep = None
-        else:
-            zd_keep = zd
+        zd_keep = None if cfg.temperature == 0.0 else zd
     else:
         zt = np.zeros((cfg.B, cfg.G + 1, 0), np.float32)
         zd_keep = None
         dt = np.zeros((cfg.B, cfg.G), np.int32)
-        u = uniforms(cfg, st)
+    u = uniforms(cfg, st)
     return RoundInputs(cfg, ctx, base, tcap, h_bits, w_bits, g_bits, q_bits, kb_bits, vb_bits,
                        zt, zd_keep, dt, u)
 
