@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of one block-draft round on one MI355X.
+
+A step is one whole round over one batch: inject_kv for the B*K new rows, the
+block attention of every draft layer, and verify_block.  The workload is the
+batch-32 Qwen3-8B-shaped drafter (K = 16, contexts ~ U[512, 4096], 5 layers,
+32 query / 8 KV heads x 128, H_target 5 x 4096, vocab 151936, temperature-1
+rejection sampling).  All inputs are seeded synthetic data already resident in
+HBM when timing starts; the context caches are filled beforehand (untimed) by
+running inject_kv over synthetic context hidden states.
+
+Prints one JSON line.  ``value`` is rounds/s; ``accepted_tok_s`` is rounds/s
+times the tokens a round commits (sum of tau + 1).  ``roofline`` covers the
+call that dominates the round; ``stages`` has all three.  ``cpu_baseline``
+times the CPU oracle on one full round of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+KERNEL_SOURCES = {
+    "inject_kv": "block_drafting_amd/csrc/inject.hip",
+    "draft_block_attn": "block_drafting_amd/csrc/attn.hip",
+    "verify_block": "block_drafting_amd/csrc/verify.hip",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="qwen3-8b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (for HBM counter scaling)")
+    return ap.parse_args()
+
+
+def source_sha(path: str) -> str:
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(call: str):
+    """HBM bytes per launch of ``call`` measured with rocprofv3 counters, if the
+    committed measurement was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "traffic_qwen3-8b.txt")
+    if not os.path.exists(p):
+        return None
+    rec = {}
+    for line in open(p):
+        if line.startswith(call + " "):
+            for kv in line.split()[1:]:
+                k, _, v = kv.partition("=")
+                rec[k] = v
+    if not rec or rec.get("source_sha") != source_sha(KERNEL_SOURCES[call]):
+        return None
+    return float(rec["bytes_per_call"])
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {a.gpus} is not supported "
+              "(the path shards by request, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as wl
+    import block_drafting_amd as bd
+
+    bd.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = wl.CONFIGS[a.config]
+    B, K, G, L, n_q, n_kv, hd, V = cfg.B, cfg.K, cfg.G, cfg.L, cfg.n_q, cfg.n_kv, cfg.hd, cfg.V
+    sampling = cfg.temperature > 0
+
+    # ---------------------------------------------------------------- inputs
+    r = wl.make_round(cfg, seed=0)
+    i16 = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev)
+    h = i16(r.h_round_bits)
+    w = i16(r.w_bits)
+    gains = i16(r.k_norm_bits)
+    q = i16(r.q_bits)
+    kb = i16(r.k_blk_bits)
+    vb = i16(r.v_blk_bits)
+    zt = torch.from_numpy(r.z_target).to(dev)
+    zd = torch.from_numpy(r.z_draft).to(dev) if sampling else None
+    dtok = torch.from_numpy(r.draft_tokens).to(dev)
+    uni = torch.from_numpy(r.uniforms).to(dev)
+    row_cu = torch.from_numpy(r.row_cu).to(dev)
+    row_pos0 = torch.from_numpy(r.row_pos0).to(dev)
+    cache_base = torch.from_numpy(r.cache_base).to(dev)
+    ctx_len = torch.from_numpy(r.ctx_len).to(dev)
+    T_cap = r.T_cap
+    kc = torch.zeros((L, T_cap, n_kv, hd), dtype=torch.int16, device=dev)
+    vc = torch.zeros((L, T_cap, n_kv, hd), dtype=torch.int16, device=dev)
+    max_ctx = int(r.ctx_len.max())
+
+    # context fill (untimed): inject_kv over synthetic context hidden states,
+    # drawn on the device in slices
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1)
+    lo = np.maximum(0, r.ctx_len - cfg.window) if cfg.window > 0 else np.zeros(B, np.int64)
+    rows_b = (r.ctx_len - lo).astype(np.int64)
+    slice_rows = 8192
+    fill_ws = torch.empty(bd.inject_kv_workspace_size(slice_rows, cfg.d_in, L, n_kv, hd), dtype=torch.uint8,
+                          device=dev)
+    for b in range(B):
+        done = 0
+        while done < rows_b[b]:
+            n = int(min(slice_rows, rows_b[b] - done))
+            hc = torch.randn((n, cfg.d_in), generator=gen, device=dev).to(torch.bfloat16)
+            bd.inject_kv(hc, w, gains, torch.tensor([0, n], dtype=torch.int32, device=dev),
+                         torch.tensor([int(lo[b]) + done], dtype=torch.int32, device=dev),
+                         cache_base[b:b + 1].contiguous(), kc, vc, cfg.rope_theta, cfg.rms_eps, workspace=fill_ws)
+            done += n
+    torch.cuda.synchronize()
+    del fill_ws
+
+    # workspaces and outputs, allocated once
+    ws_inj = torch.empty(max(1, bd.inject_kv_workspace_size(B * K, cfg.d_in, L, n_kv, hd)), dtype=torch.uint8,
+                         device=dev)
+    ws_att = torch.empty(max(1, bd.draft_block_attn_workspace_size(B, K, n_q, n_kv, hd, max_ctx, cfg.window)),
+                         dtype=torch.uint8, device=dev)
+    ws_ver = torch.empty(max(1, bd.verify_block_workspace_size(B, G, V, cfg.top_k)), dtype=torch.uint8,
+                         device=dev)
+    attn_out = torch.empty((L, B, K, n_q, hd), dtype=torch.int16, device=dev)
+    tau = torch.empty(B, dtype=torch.int32, device=dev)
+    out_tok = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def round_(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        bd.inject_kv(h, w, gains, row_cu, row_pos0, cache_base, kc, vc, cfg.rope_theta, cfg.rms_eps,
+                     workspace=ws_inj)
+        if ev is not None:
+            ev[1].record(stream)
+        for l in range(L):
+            bd.draft_block_attn(q[l], kb[l], vb[l], kc[l], vc[l], cache_base, ctx_len, max_ctx, cfg.window,
+                                0.0, out=attn_out[l], workspace=ws_att)
+        if ev is not None:
+            ev[2].record(stream)
+        bd.verify_block(zt, zd, dtok, uni, cfg.temperature, cfg.top_k, cfg.top_p, tau=tau, out_tokens=out_tok,
+                        workspace=ws_ver)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(a.warmup):
+        round_()
+    torch.cuda.synchronize()
+
+    # timed region: whole rounds, bracketed by device synchronisation
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(a.steps):
+        round_(evs[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stage_ms = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in evs]).mean(axis=0)
+
+    tau_h = tau.cpu().numpy()
+    committed = int((tau_h + 1).sum())
+    rounds_s = a.steps / elapsed
+    ms_step = 1e3 * elapsed / a.steps
+
+    # ---------------------------------------------------------------- rooflines
+    M = B * K
+    N_out = cfg.n_out
+    inj_flops = 2.0 * M * cfg.d_in * N_out
+    inj_bytes = 2.0 * cfg.d_in * N_out + 2.0 * M * (cfg.d_in + N_out)
+    vis = np.minimum(r.ctx_len, cfg.window) if cfg.window > 0 else r.ctx_len
+    att_bytes = float(vis.sum()) * n_kv * hd * 2 * 2 + 2.0 * B * K * n_q * hd * 2 + 2.0 * B * K * n_kv * hd * 2
+    ver_rows = B * (G + 1) + (B * G if sampling else 0)
+    ver_bytes = 4.0 * V * ver_rows
+    stages = []
+    t_inj, t_att, t_ver = stage_ms[0] / 1e3, stage_ms[1] / L / 1e3, stage_ms[2] / 1e3
+    stages.append(dict(call="inject_kv", bound="mfma", per_call_us=t_inj * 1e6, calls_per_round=1,
+                       achieved=inj_flops / t_inj / 1e12, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                       frac=inj_flops / t_inj / 1e12 / BF16_PEAK_TFLOPS, algorithmic_flops=inj_flops,
+                       algorithmic_bytes=inj_bytes, hbm_gbs=inj_bytes / t_inj / 1e9))
+    stages.append(dict(call="draft_block_attn", bound="hbm", per_call_us=t_att * 1e6, calls_per_round=L,
+                       achieved=att_bytes / t_att / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
+                       frac=att_bytes / t_att / 1e9 / HBM_PEAK_GBS, algorithmic_bytes=att_bytes))
+    stages.append(dict(call="verify_block", bound="hbm", per_call_us=t_ver * 1e6, calls_per_round=1,
+                       achieved=ver_bytes / t_ver / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
+                       frac=ver_bytes / t_ver / 1e9 / HBM_PEAK_GBS, algorithmic_bytes=ver_bytes))
+    for s in stages:
+        s["traffic"] = read_traffic(s["call"])
+    dom = max(stages, key=lambda s: s["per_call_us"] * s["calls_per_round"])
+    roofline = dict(kernel=dom["call"], bound=dom["bound"], achieved=round(dom["achieved"], 2),
+                    peak=dom["peak"], unit=dom["unit"], frac=round(dom["frac"], 4),
+                    traffic=dom["traffic"])
+
+    # ---------------------------------------------------------------- CPU baseline
+    cpu = None
+    if not a.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, r, kc, vc, h, w)
+
+    line = {
+        "metric": "rounds/s + accepted tok/s at B=32, K=16 (8B shape); % of HBM/MFMA roofline",
+        "value": round(rounds_s, 2),
+        "unit": "rounds/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 (MFMA, fp32 accumulate) + fp32 (verify)",
+        "data": "synthetic (seeded; random-init projection weights)",
+        "config": {"workload": f"{cfg.name}: B={B} K={K} contexts {cfg.ctx_kind}[{cfg.ctx_a},{cfg.ctx_b}] "
+                               f"L={L} n_q={n_q} n_kv={n_kv} hd={hd} d_in={cfg.d_in} V={V} "
+                               f"T={cfg.temperature} top_k={cfg.top_k}",
+                   "global_batch": B, "block": K, "parallelism": "none (1 GPU)"},
+        "accepted_tok_s": round(rounds_s * committed, 1),
+        "drafted_accepted_tok_s": round(rounds_s * int(tau_h.sum()), 1),
+        "tokens_per_round": committed,
+        "roofline": roofline,
+        "stages": [{k: (round(v, 4) if isinstance(v, float) and k != "traffic" else v) for k, v in s.items()}
+                   for s in stages],
+        "cpu_baseline": cpu,
+    }
+    if a.copy_calibration:
+        line["copy_calibration"] = copy_calibration(torch, dev)
+    print(json.dumps(line), flush=True)
+
+
+def copy_calibration(torch, dev):
+    """A plain device-to-device copy of known size, for scaling HBM counters."""
+    n = 256 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 5}
+
+
+def cpu_baseline(cfg, r, kc, vc, h, w):
+    """The oracle, untuned, on one full round of the same workload on the host
+    cores: projection of the B*K rows, every layer's attention for every
+    request, and the verification of the batch."""
+    import oracle
+    from oracle import attention as oa, inject as oi, verify as ov
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    B, K, L = cfg.B, cfg.K, cfg.L
+    f64 = lambda bits: (np.ascontiguousarray(bits).view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    hh = f64(r.h_round_bits)
+    ww = f64(r.w_bits)
+    gg = f64(r.k_norm_bits)
+    # context caches of the sampled round, copied back once (not timed)
+    kc_h = kc.cpu().numpy().view(np.uint16)
+    vc_h = vc.cpu().numpy().view(np.uint16)
+    caches = [(f64(kc_h[l]), f64(vc_h[l])) for l in range(L)]
+    q = [f64(r.q_bits[l]) for l in range(L)]
+    kb = [f64(r.k_blk_bits[l]) for l in range(L)]
+    vb = [f64(r.v_blk_bits[l]) for l in range(L)]
+    k_o = np.zeros((L, r.T_cap, cfg.n_kv, cfg.hd))
+    v_o = np.zeros((L, r.T_cap, cfg.n_kv, cfg.hd))
+    t0 = time.perf_counter()
+    oi.inject_kv(hh, ww, gg, r.row_cu, r.row_pos0, r.cache_base, k_o, v_o, L, cfg.n_kv, cfg.hd,
+                 cfg.rope_theta, cfg.rms_eps)
+    t1 = time.perf_counter()
+    for l in range(L):
+        oa.block_attn(q[l], kb[l], vb[l], caches[l][0], caches[l][1], r.cache_base, r.ctx_len, cfg.window)
+    t2 = time.perf_counter()
+    ov.verify(r.z_target, r.z_draft, r.draft_tokens, r.uniforms, cfg.temperature, cfg.top_k, cfg.top_p)
+    t3 = time.perf_counter()
+    total = t3 - t0
+    return {"value": round(1.0 / total, 5), "unit": "rounds/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one full {cfg.name} round (inject M={B * K}, {L} attention layers x {B} requests, "
+                      f"verify of {B} requests)",
+            "seconds": {"inject_kv": round(t1 - t0, 3), "draft_block_attn": round(t2 - t1, 3),
+                        "verify_block": round(t3 - t2, 3), "round": round(total, 3)}}
+
+
+if __name__ == "__main__":
+    main()

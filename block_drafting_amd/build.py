@@ -38,29 +38,32 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libblockdraft.so)")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(os.path.basename(src))[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(PKG, "..", "include"), "-c", src, "-o", obj]
+def _compile(src: str, build_dir: str = BUILD, defines=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(os.path.basename(src))[0] + ".o")
+    cmd = [hipcc(), *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-I", os.path.join(PKG, "..", "include"),
+           "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
     return obj
 
 
-def build(jobs: int = 4, verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int = 4, verbose: bool = True, out: str = LIB, build_dir: str = BUILD, defines=()) -> str:
+    """Compile every source and link ``out``; ``defines`` override the
+    kernels' compile-time tuning constants (NAME=VALUE)."""
+    os.makedirs(build_dir, exist_ok=True)
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, build_dir, defines), srcs))
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
-    return LIB
+        print(f"built {out}", file=sys.stderr)
+    return out
 
 
 if __name__ == "__main__":

@@ -32,6 +32,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// ---------------------------------------------------------------- streaming loads
+// Non-temporal 16-byte loads for data read once per call (logits, K/V tiles,
+// projection weights): they stream through the caches at low priority.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const uint16_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ u32x4 ld_stream_v(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ float4 ld_stream(const float* p) {
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// 2^x with the hardware instruction (no denormal-result handling): used for
+// softmax terms exp((z - max) / T), where a result below 2^-126 is negligible
+// next to the term 1 of the maximum itself.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ---------------------------------------------------------------- MFMA
 // D = A(32x16) * B(16x32) + C, bf16 inputs, fp32 accumulators (gfx950).
 __device__ __forceinline__ floatx16 mfma32x32x16(bf16x8 a, bf16x8 b, floatx16 c) {

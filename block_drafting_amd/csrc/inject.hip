@@ -22,8 +22,7 @@
 namespace bd {
 
 constexpr int GT = 256;  // threads per GEMM workgroup (2 x 2 waves)
-constexpr int BK = 64;   // d_in per LDS stage
-constexpr int GLS = BK + 8;  // LDS row stride (elements)
+constexpr int KALIGN = 64;  // d_in must be a multiple of this
 
 struct GemmArgs {
   const uint16_t* A;  // [M, Kd]
@@ -32,8 +31,9 @@ struct GemmArgs {
   int M, N, Kd, S, steps_per_split, tiles_n;
 };
 
-template <int BM, int BN>
+template <int BM, int BN, int BK>
 __global__ __launch_bounds__(GT) void ik_gemm(GemmArgs g) {
+  constexpr int GLS = BK + 8;               // LDS row stride (elements)
   constexpr int WM = BM / 2, WN = BN / 2;   // wave tile
   constexpr int FM = WM / 32, FN = WN / 32; // 32x32 blocks per wave
   constexpr int APT = BM * BK / 8 / GT;     // 16-byte pieces per thread
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(GT) void ik_gemm(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  uint4 ra[APT], rb[BPT];
+  u32x4 ra[APT], rb[BPT];
   auto fetch = [&](int step) {
     const int k0 = (step0 + step) * BK;
 #pragma unroll
@@ -66,14 +66,13 @@ __global__ __launch_bounds__(GT) void ik_gemm(GemmArgs g) {
       const int piece = t + p * GT;
       const int row = piece / (BK / 8), kc = piece - row * (BK / 8);
       const int m = m0 + row;
-      ra[p] = m < g.M ? *reinterpret_cast<const uint4*>(g.A + size_t(m) * g.Kd + k0 + kc * 8)
-                      : make_uint4(0, 0, 0, 0);
+      ra[p] = *reinterpret_cast<const u32x4*>(g.A + size_t(m < g.M ? m : g.M - 1) * g.Kd + k0 + kc * 8);
     }
 #pragma unroll
     for (int p = 0; p < BPT; ++p) {
       const int piece = t + p * GT;
       const int row = piece / (BK / 8), kc = piece - row * (BK / 8);
-      rb[p] = *reinterpret_cast<const uint4*>(g.Bw + size_t(n0 + row) * g.Kd + k0 + kc * 8);
+      rb[p] = *reinterpret_cast<const u32x4*>(g.Bw + size_t(n0 + row) * g.Kd + k0 + kc * 8);
     }
   };
 
@@ -82,15 +81,18 @@ __global__ __launch_bounds__(GT) void ik_gemm(GemmArgs g) {
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < APT; ++p) {
+      // rows past M were loaded from row M - 1 (unconditional loads); they
+      // are zeroed here, where the data is consumed
       const int piece = t + p * GT;
       const int row = piece / (BK / 8), kc = piece - row * (BK / 8);
-      *reinterpret_cast<uint4*>(&As[row * GLS + kc * 8]) = ra[p];
+      const u32x4 z4 = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(&As[row * GLS + kc * 8]) = m0 + row < g.M ? ra[p] : z4;
     }
 #pragma unroll
     for (int p = 0; p < BPT; ++p) {
       const int piece = t + p * GT;
       const int row = piece / (BK / 8), kc = piece - row * (BK / 8);
-      *reinterpret_cast<uint4*>(&Bs[row * GLS + kc * 8]) = rb[p];
+      *reinterpret_cast<u32x4*>(&Bs[row * GLS + kc * 8]) = rb[p];
     }
     __syncthreads();
     if (step + 1 < nsteps) fetch(step + 1);
@@ -227,18 +229,33 @@ __global__ __launch_bounds__(256) void ik_finish(FinishArgs f) {
 // ---------------------------------------------------------------- host side
 static inline size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 
+#ifndef BD_GEMM_BN
+#define BD_GEMM_BN 128
+#endif
+#ifndef BD_GEMM_BK
+#define BD_GEMM_BK 64
+#endif
+#ifndef BD_GEMM_WGS
+#define BD_GEMM_WGS 512
+#endif
+
 struct GemmPlan {
-  int bm, bn, S, steps_per_split, tiles;
+  int bm, bn, bk, S, steps_per_split, tiles;
 };
 
+// Large M: 256 x BD_GEMM_BN tiles; small M (weight-bound): 64 x 128 tiles.
+// Split d_in until about BD_GEMM_WGS workgroups run.
 static GemmPlan gemm_plan(int M, int N, int Kd) {
   GemmPlan p;
-  p.bm = M > 128 ? 256 : 64;
-  p.bn = 128;
+  const bool big = M > 128 && N % BD_GEMM_BN == 0;
+  p.bm = big ? 256 : 64;
+  p.bn = big ? BD_GEMM_BN : 128;
+  p.bk = big ? BD_GEMM_BK : 64;
+  const int target = big ? BD_GEMM_WGS : 512;
   const int tm = (M + p.bm - 1) / p.bm;
   p.tiles = tm * (N / p.bn);
-  const int steps = Kd / BK;
-  int S = (512 + p.tiles - 1) / p.tiles;
+  const int steps = Kd / p.bk;
+  int S = (target + p.tiles / 2) / p.tiles;
   if (S > steps) S = steps;
   if (S < 1) S = 1;
   p.steps_per_split = (steps + S - 1) / S;
@@ -264,8 +281,8 @@ hipError_t launch_inject(const uint16_t* h, const uint16_t* w, const uint16_t* g
   g.M = M; g.N = N; g.Kd = d_in; g.S = p.S; g.steps_per_split = p.steps_per_split;
   g.tiles_n = N / p.bn;
   dim3 grid(p.tiles, p.S);
-  if (p.bm == 256) hipLaunchKernelGGL((ik_gemm<256, 128>), grid, dim3(GT), 0, stream, g);
-  else hipLaunchKernelGGL((ik_gemm<64, 128>), grid, dim3(GT), 0, stream, g);
+  if (p.bm == 256) hipLaunchKernelGGL((ik_gemm<256, BD_GEMM_BN, BD_GEMM_BK>), grid, dim3(GT), 0, stream, g);
+  else hipLaunchKernelGGL((ik_gemm<64, 128, 64>), grid, dim3(GT), 0, stream, g);
 
   FinishArgs f{};
   f.P = g.P; f.gain = gain; f.row_cu = row_cu; f.row_pos0 = row_pos0; f.cache_base = cache_base;

@@ -29,6 +29,16 @@ constexpr int VT = 256;        // threads of a stats / draw workgroup
 constexpr int VCH = 8192;      // logits per chunk (32 per thread)
 constexpr int VPT = VCH / VT;  // 32
 constexpr int TOPK_MAX = 64;
+// Target workgroups of the streaming statistics pass and its register budget
+// (waves per SIMD) so that they are all resident at once.
+#ifndef BD_STATS_GRID
+#define BD_STATS_GRID 1024
+#endif
+#ifndef BD_STATS_WPE
+#define BD_STATS_WPE 4
+#endif
+#define BD_STATS_OCC __attribute__((amdgpu_waves_per_eu(BD_STATS_WPE)))
+constexpr int STATS_GRID = BD_STATS_GRID;
 constexpr int CAND_PER_WAVE = 64;
 
 enum { JOB_NONE = 0, JOB_RESID = 1, JOB_BONUS = 2 };
@@ -47,23 +57,22 @@ __device__ __forceinline__ int slot_offset(int s, int t) {
 template <bool VEC>
 __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int start, int V, int t,
                                            float (&x)[VPT]) {
+  // Every lane loads unconditionally (slots past the row end re-read the row
+  // start) and the values are used raw: callers mask slots with index >= V at
+  // the point of use.  Keeping selects off the loaded registers lets the
+  // loads stay in flight until the data is consumed.
   if (VEC) {
 #pragma unroll
     for (int j = 0; j < VPT / 4; ++j) {
-      int e = start + 4 * (j * VT + t);
-      if (e + 3 < V) {
-        float4 f = *reinterpret_cast<const float4*>(row + e);
-        x[4 * j] = f.x; x[4 * j + 1] = f.y; x[4 * j + 2] = f.z; x[4 * j + 3] = f.w;
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) x[4 * j + c] = (e + c < V) ? row[e + c] : -INFINITY;
-      }
+      const int e = start + 4 * (j * VT + t);
+      const float4 f = *reinterpret_cast<const float4*>(row + (e < V ? e : 0));
+      x[4 * j] = f.x; x[4 * j + 1] = f.y; x[4 * j + 2] = f.z; x[4 * j + 3] = f.w;
     }
   } else {
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-      int e = start + j * VT + t;
-      x[j] = (e < V) ? row[e] : -INFINITY;
+      const int e = start + j * VT + t;
+      x[j] = row[e < V ? e : 0];
     }
   }
 }
@@ -109,12 +118,16 @@ __device__ __forceinline__ float wave_sort_desc(float v) {
   return v;
 }
 
+// Statistics records: workgroup w of pass 1 takes the global chunks
+// [w * cpw, (w + 1) * cpw) of the row-major (row, chunk) sequence and writes
+// one record per row it touches, at slot row + w (unique: a later row starts
+// in a workgroup at or after the last one of an earlier row).
 struct VerifyWs {
-  float* cmax;   // [rows][nch]
-  int* carg;     // [rows][nch]
-  double* csum;  // [rows][nch]
-  float* ctv;    // [rows][nch][k]
-  int* cti;      // [rows][nch][k]
+  float* cmax;   // [slots]
+  int* carg;     // [slots]
+  double* csum;  // [slots]
+  float* ctv;    // [slots][k]
+  int* cti;      // [slots][k]
   float* rmax;   // [rows]
   int* rarg;     // [rows]
   double* rsum;  // [rows]
@@ -131,6 +144,7 @@ struct VerifyArgs {
   const int* dtok;
   const float* uni;
   int B, G, V, nch;
+  int cpw;               // consecutive (row, chunk) pairs per statistics workgroup
   int n_trows, n_rows;   // target rows B*(G+1); all rows with draft rows
   float T;               // temperature used for probabilities (1 when greedy)
   float c2;              // log2(e) / T
@@ -150,7 +164,118 @@ __device__ __forceinline__ const float* row_ptr(const VerifyArgs& a, int r) {
 }
 
 // -------------------------------------------------------------------------
-// Pass 1: per (row, chunk) statistics.
+// Pass 1, streaming form (no top-k): a persistent workgroup walks its run of
+// (row, chunk) pairs, keeping the next chunk's non-temporal loads in flight
+// while it reduces the current one.  Every thread keeps its own running
+// maximum (lowest index on ties) and sum of exp((z - max) / T) in fp64,
+// rescaled when its maximum grows; at the end of each row (or of the run) the
+// workgroup combines its threads into one record.
+// -------------------------------------------------------------------------
+template <bool VEC>
+__device__ __forceinline__ void load_stream_chunk(const float* __restrict__ row, int start, int V, int t,
+                                                  float (&x)[VPT]) {
+  if (VEC) {
+#pragma unroll
+    for (int j = 0; j < VPT / 4; ++j) {
+      const int e = start + 4 * (j * VT + t);
+      const float4 f = ld_stream(row + (e < V ? e : 0));
+      x[4 * j] = f.x; x[4 * j + 1] = f.y; x[4 * j + 2] = f.z; x[4 * j + 3] = f.w;
+    }
+  } else {
+    load_chunk<false>(row, start, V, t, x);
+  }
+}
+
+template <bool VEC>
+__device__ __forceinline__ void consume_chunk(const VerifyArgs& a, const float (&x)[VPT], int start, int t,
+                                              float& mt, int& it, double& st) {
+  float cm = -INFINITY;
+  int ci = INT32_MAX;
+#pragma unroll
+  for (int s = 0; s < VPT; ++s) {
+    const int e = start + slot_offset<VEC>(s, t);
+    if (e < a.V && (x[s] > cm || ci == INT32_MAX)) { cm = x[s]; ci = e; }
+  }
+  if (ci == INT32_MAX) return;
+  const bool first = it == INT32_MAX;
+  const float mn = first ? cm : fmaxf(mt, cm);
+  if (a.need_sum && mn != -INFINITY) {
+    if (!first && mn > mt && st != 0.0) st *= exp2(double(mt - mn) * double(a.c2));
+    float part = 0.f;
+#pragma unroll
+    for (int s = 0; s < VPT; ++s) {
+      const float p = exp2_hw((x[s] - mn) * a.c2);
+      part += (start + slot_offset<VEC>(s, t) < a.V) ? p : 0.f;
+    }
+    st += double(part);
+  }
+  if (first || cm > mt) { mt = cm; it = ci; }
+}
+
+// one record of (row, workgroup) from the threads' running statistics
+__device__ __forceinline__ void flush_row(const VerifyArgs& a, size_t slot, float& mt, int& it, double& st,
+                                          float* s_v, int* s_i, double* s_d) {
+  float bv = mt;
+  int bi = it;
+  block_argmax(bv, bi, s_v, s_i);
+  if (threadIdx.x == 0) { a.ws.cmax[slot] = bv; a.ws.carg[slot] = bi; }
+  if (a.need_sum) {
+    double contrib = 0.0;
+    if (it != INT32_MAX && st != 0.0) contrib = st * exp2(double(mt - bv) * double(a.c2));
+    const double S = block_sum_f64(contrib, s_d);
+    if (threadIdx.x == 0) a.ws.csum[slot] = S;
+  }
+  mt = -INFINITY;
+  it = INT32_MAX;
+  st = 0.0;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(VT) BD_STATS_OCC void vb_stats_stream(VerifyArgs a) {
+  __shared__ float s_v[4];
+  __shared__ int s_i[4];
+  __shared__ double s_d[4];
+  const int t = threadIdx.x, w = blockIdx.x;
+  const long long total = (long long)a.n_rows * a.nch;
+  const long long x0 = (long long)w * a.cpw;
+  const long long x1 = min(total, x0 + a.cpw);
+  if (x0 >= x1) return;
+  float mt = -INFINITY;
+  int it = INT32_MAX;
+  double st = 0.0;
+  float xa[VPT], xb[VPT];
+  auto rowp = [&](long long x) { return row_ptr(a, int(x / a.nch)); };
+  auto cstart = [&](long long x) { return int(x % a.nch) * VCH; };
+  auto row_ends = [&](long long x) { return x + 1 == x1 || (x + 1) % a.nch == 0; };
+  load_stream_chunk<VEC>(rowp(x0), cstart(x0), a.V, t, xa);
+  long long x = x0;
+  // steady state: both look-ahead loads are unconditional, so the compiler
+  // can wait for exactly the chunk it consumes
+  while (x + 2 < x1) {
+    load_stream_chunk<VEC>(rowp(x + 1), cstart(x + 1), a.V, t, xb);
+    consume_chunk<VEC>(a, xa, cstart(x), t, mt, it, st);
+    if (row_ends(x)) flush_row(a, size_t(x / a.nch) + w, mt, it, st, s_v, s_i, s_d);
+    load_stream_chunk<VEC>(rowp(x + 2), cstart(x + 2), a.V, t, xa);
+    consume_chunk<VEC>(a, xb, cstart(x + 1), t, mt, it, st);
+    if (row_ends(x + 1)) flush_row(a, size_t((x + 1) / a.nch) + w, mt, it, st, s_v, s_i, s_d);
+    x += 2;
+  }
+  // the last one or two chunks
+  if (x + 1 < x1) {
+    load_stream_chunk<VEC>(rowp(x + 1), cstart(x + 1), a.V, t, xb);
+    consume_chunk<VEC>(a, xa, cstart(x), t, mt, it, st);
+    if (row_ends(x)) flush_row(a, size_t(x / a.nch) + w, mt, it, st, s_v, s_i, s_d);
+    consume_chunk<VEC>(a, xb, cstart(x + 1), t, mt, it, st);
+    flush_row(a, size_t((x + 1) / a.nch) + w, mt, it, st, s_v, s_i, s_d);
+  } else {
+    consume_chunk<VEC>(a, xa, cstart(x), t, mt, it, st);
+    flush_row(a, size_t(x / a.nch) + w, mt, it, st, s_v, s_i, s_d);
+  }
+}
+
+// -------------------------------------------------------------------------
+// Pass 1, top-k form: one chunk per workgroup; besides the maximum (and the
+// sum when asked) it finds the chunk's k best (value desc, index asc).
 // -------------------------------------------------------------------------
 template <bool VEC>
 __global__ __launch_bounds__(VT) void vb_stats(VerifyArgs a) {
@@ -180,7 +305,7 @@ __global__ __launch_bounds__(VT) void vb_stats(VerifyArgs a) {
   }
   float lane_best = bv;
   block_argmax(bv, bi, s_v, s_i);
-  const size_t rc = size_t(row) * a.nch + c;
+  const size_t rc = size_t(row) + blockIdx.x;  // record slot (cpw = 1)
   if (t == 0) { a.ws.cmax[rc] = bv; a.ws.carg[rc] = bi; }
 
   if (a.need_sum) {
@@ -188,7 +313,10 @@ __global__ __launch_bounds__(VT) void vb_stats(VerifyArgs a) {
     if (bi != INT32_MAX && bv != -INFINITY) {
       float part = 0.f;
 #pragma unroll
-      for (int s = 0; s < VPT; ++s) part += exp2f((x[s] - bv) * a.c2);
+      for (int s = 0; s < VPT; ++s) {
+        const float p = exp2_hw((x[s] - bv) * a.c2);
+        part += (start + slot_offset<VEC>(s, t) < a.V) ? p : 0.f;
+      }
       sum = double(part);
     }
     sum = block_sum_f64(sum, s_d);
@@ -291,9 +419,9 @@ struct DrawRow {
 };
 
 __device__ __forceinline__ float draw_weight(const DrawRow& r, float c2, float zt, float zd, bool resid) {
-  float p = exp2f((zt - r.mt) * c2) * r.st;
+  float p = exp2_hw((zt - r.mt) * c2) * r.st;
   if (!resid) return p;
-  float q = exp2f((zd - r.md) * c2) * r.sd;
+  float q = exp2_hw((zd - r.md) * c2) * r.sd;
   return fmaxf(0.f, p - q);
 }
 
@@ -301,11 +429,15 @@ __device__ __forceinline__ float draw_weight(const DrawRow& r, float c2, float z
 // Pass 2: one workgroup per request.
 // -------------------------------------------------------------------------
 __device__ void merge_row(const VerifyArgs& a, int row, int lane) {
-  // max / argmax over chunks
+  // records of this row: slots row + w for the workgroups w that covered it
+  const long long w0 = (long long)row * a.nch / a.cpw;
+  const long long w1 = ((long long)row * a.nch + a.nch - 1) / a.cpw;
+  const int nrec = int(w1 - w0 + 1);
+  const size_t slot0 = size_t(row) + size_t(w0);
   float v = -INFINITY;
   int i = INT32_MAX;
-  for (int c = lane; c < a.nch; c += 64) {
-    size_t rc = size_t(row) * a.nch + c;
+  for (int c = lane; c < nrec; c += 64) {
+    size_t rc = slot0 + c;
     float cv = a.ws.cmax[rc];
     int ci = a.ws.carg[rc];
     if (better(cv, ci, v, i)) { v = cv; i = ci; }
@@ -313,8 +445,8 @@ __device__ void merge_row(const VerifyArgs& a, int row, int lane) {
   wave_argmax(v, i);
   double S = 0.0;
   if (a.need_sum && v != -INFINITY) {
-    for (int c = lane; c < a.nch; c += 64) {
-      size_t rc = size_t(row) * a.nch + c;
+    for (int c = lane; c < nrec; c += 64) {
+      size_t rc = slot0 + c;
       float cm = a.ws.cmax[rc];
       if (cm != -INFINITY) S += a.ws.csum[rc] * exp2(double(cm - v) * double(a.c2));
     }
@@ -328,9 +460,9 @@ __device__ void merge_row(const VerifyArgs& a, int row, int lane) {
   if (a.topk > 0) {
     // k best of the chunk lists, then softmax over them and the top-p cut
     const int k = a.topk;
-    const int ncand = a.nch * k;
-    const float* cv = a.ws.ctv + size_t(row) * a.nch * k;
-    const int* ci = a.ws.cti + size_t(row) * a.nch * k;
+    const int ncand = nrec * k;
+    const float* cv = a.ws.ctv + slot0 * k;
+    const int* ci = a.ws.cti + slot0 * k;
     float pv = INFINITY;
     int pi = -1;
     int* ki = a.ws.rki + size_t(row) * TOPK_MAX;
@@ -387,13 +519,15 @@ __device__ __forceinline__ double kept_prob(const VerifyArgs& a, int row, int to
   return 0.0;
 }
 
-__global__ __launch_bounds__(256) void vb_decide(VerifyArgs a) {
+constexpr int DT = 1024;  // threads of the decision workgroup (16 waves)
+
+__global__ __launch_bounds__(DT) void vb_decide(VerifyArgs a) {
   const int b = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int G = a.G;
   // rows of this request: G+1 target rows, then G draft rows when sampling
   const int n_my = (G + 1) + ((a.n_rows > a.n_trows) ? G : 0);
-  for (int j = w; j < n_my; j += 4) {
+  for (int j = w; j < n_my; j += DT / 64) {
     int row = j <= G ? b * (G + 1) + j : a.n_trows + b * G + (j - G - 1);
     merge_row(a, row, lane);
   }
@@ -521,6 +655,7 @@ __device__ __forceinline__ DrawRow draw_row(const VerifyArgs& a, int b, int pos,
 }
 
 // per-chunk sums of the draw weights (full-vocabulary draws only)
+template <bool VEC>
 __global__ __launch_bounds__(VT) void vb_draw_sums(VerifyArgs a) {
   __shared__ double s_d[4];
   const int b = blockIdx.y, c = blockIdx.x, t = threadIdx.x;
@@ -529,44 +664,75 @@ __global__ __launch_bounds__(VT) void vb_draw_sums(VerifyArgs a) {
   const bool resid = kind == JOB_RESID;
   const DrawRow r = draw_row(a, b, a.ws.job[2 * b], resid);
   const int start = c * VCH;
+  float xt[VPT], xd[VPT];
+  load_chunk<VEC>(r.zt, start, a.V, t, xt);
+  if (resid) load_chunk<VEC>(r.zd, start, a.V, t, xd);
   double s = 0.0;
+#pragma unroll
   for (int j = 0; j < VPT; ++j) {
-    int e = start + t * VPT + j;
-    if (e < a.V) s += double(draw_weight(r, a.c2, r.zt[e], resid ? r.zd[e] : 0.f, resid));
+    const int e = start + slot_offset<VEC>(j, t);
+    if (e < a.V) s += double(draw_weight(r, a.c2, xt[j], resid ? xd[j] : 0.f, resid));
   }
   s = block_sum_f64(s, s_d);
   if (t == 0) a.ws.jsum[size_t(b) * a.nch + c] = s;
 }
 
+// The thread's 32 consecutive logits of a row, starting at element e0.
+__device__ __forceinline__ void load_run(const float* __restrict__ row, int e0, int V, bool vec, float (&x)[VPT]) {
+  if (vec && e0 + VPT <= V) {
+#pragma unroll
+    for (int j = 0; j < VPT / 4; ++j) {
+      const float4 f = *reinterpret_cast<const float4*>(row + e0 + 4 * j);
+      x[4 * j] = f.x; x[4 * j + 1] = f.y; x[4 * j + 2] = f.z; x[4 * j + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) x[j] = (e0 + j < V) ? row[e0 + j] : -INFINITY;
+  }
+}
+
+// Exclusive prefix sum over the workgroup's threads (thread order), fp64.
+__device__ __forceinline__ double block_exclusive_scan(double v, double* s_w /* [4] */) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  double inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  __syncthreads();
+  if (lane == 63) s_w[w] = inc;
+  __syncthreads();
+  double base = 0.0;
+  for (int k = 0; k < w; ++k) base += s_w[k];
+  return base + inc - v;
+}
+
 // Scan one chunk for the first running sum above tgt.  Returns the vocabulary
 // index (or INT32_MAX) and the margin through the shared outputs.
 __device__ void scan_chunk(const VerifyArgs& a, const DrawRow& r, bool resid, bool use_p, int c,
-                           double base, double tgt, int* s_pick, double* s_mg, double* s_ex) {
+                           double base, double tgt, int* s_pick, double* s_mg, double* s_w) {
   const int t = threadIdx.x;
   const int start = c * VCH + t * VPT;
+  const bool vec = (a.V & 3) == 0;
+  float xt[VPT], xd[VPT];
+  load_run(r.zt, start, a.V, vec, xt);
+  if (resid && !use_p) load_run(r.zd, start, a.V, vec, xd);
   float wv[VPT];
   double mine = 0.0;
+#pragma unroll
   for (int j = 0; j < VPT; ++j) {
-    int e = start + j;
     float wgt = 0.f;
-    if (e < a.V) wgt = use_p ? draw_weight(r, a.c2, r.zt[e], 0.f, false)
-                             : draw_weight(r, a.c2, r.zt[e], resid ? r.zd[e] : 0.f, resid);
+    if (start + j < a.V) wgt = use_p ? draw_weight(r, a.c2, xt[j], 0.f, false)
+                                     : draw_weight(r, a.c2, xt[j], resid ? xd[j] : 0.f, resid);
     wv[j] = wgt;
     mine += double(wgt);
   }
-  // exclusive scan of the thread sums in thread order
-  s_ex[t] = mine;
-  __syncthreads();
-  if (t == 0) {
-    double run = 0.0;
-    for (int k = 0; k < VT; ++k) { double v = s_ex[k]; s_ex[k] = run; run += v; }
-  }
-  __syncthreads();
-  double run = base + s_ex[t];
+  double run = base + block_exclusive_scan(mine, s_w);
   int pick = INT32_MAX;
   double mg = 0.0;
   for (int j = 0; j < VPT; ++j) {
-    double prev = run;
+    const double prev = run;
     run += double(wv[j]);
     if (run > tgt) { pick = start + j; mg = fmin(tgt - prev, run - tgt); break; }
   }
@@ -607,7 +773,7 @@ __device__ int last_positive(const VerifyArgs& a, const DrawRow& r, bool resid, 
 }
 
 __global__ __launch_bounds__(VT) void vb_draw_pick(VerifyArgs a) {
-  __shared__ double s_ex[VT];
+  __shared__ double s_ex[4];
   __shared__ double s_d[4];
   __shared__ int s_pick;
   __shared__ double s_mg;
@@ -714,7 +880,7 @@ __global__ __launch_bounds__(VT) void vb_write_probs(VerifyArgs a) {
     if (e >= a.V) break;
     float p;
     if (filt) p = float(kept_prob(a, row, e));
-    else p = exp2f((z[e] - m) * a.c2) * inv;
+    else p = exp2_hw((z[e] - m) * a.c2) * inv;
     dst[e] = p;
   }
 }
@@ -732,7 +898,9 @@ static VerifyLayout verify_layout(int B, int G, int V, int top_k) {
   VerifyLayout L{};
   const size_t nch = (size_t(V) + VCH - 1) / VCH;
   const size_t rows = size_t(B) * (2 * G + 1);
-  const size_t rc = rows * nch;
+  // record slots: row + workgroup; the top-k pass uses rows * nch workgroups,
+  // the streaming pass at most max(rows * nch, STATS_GRID)
+  const size_t rc = rows + (rows * nch > size_t(STATS_GRID) ? rows * nch : size_t(STATS_GRID));
   const size_t k = top_k > 0 ? size_t(top_k) : 0;
   size_t o = 0;
   L.cmax = o; o += al(rc * 4);
@@ -794,18 +962,30 @@ hipError_t launch_verify(const float* zt, const float* zd, const int* dtok, cons
   a.ws.job = reinterpret_cast<int*>(w + L.job);
   a.ws.jsum = reinterpret_cast<double*>(w + L.jsum);
 
-  const unsigned nblk = unsigned(a.n_rows) * unsigned(a.nch);
-  if ((V & 3) == 0)
-    hipLaunchKernelGGL(vb_stats<true>, dim3(nblk), dim3(VT), 0, stream, a);
-  else
-    hipLaunchKernelGGL(vb_stats<false>, dim3(nblk), dim3(VT), 0, stream, a);
-  hipLaunchKernelGGL(vb_decide, dim3(B), dim3(256), 0, stream, a);
+  const bool vec = (V & 3) == 0;
+  const long long work = (long long)a.n_rows * a.nch;
+  if (k > 0) {
+    // top-k: one chunk per workgroup
+    a.cpw = 1;
+    if (vec) hipLaunchKernelGGL(vb_stats<true>, dim3(unsigned(work)), dim3(VT), 0, stream, a);
+    else hipLaunchKernelGGL(vb_stats<false>, dim3(unsigned(work)), dim3(VT), 0, stream, a);
+  } else {
+    // at most STATS_GRID persistent workgroups with equal runs of chunks
+    long long cpw = (work + STATS_GRID - 1) / STATS_GRID;
+    if (cpw < 1) cpw = 1;
+    a.cpw = int(cpw);
+    const unsigned grid = unsigned((work + cpw - 1) / cpw);
+    if (vec) hipLaunchKernelGGL(vb_stats_stream<true>, dim3(grid), dim3(VT), 0, stream, a);
+    else hipLaunchKernelGGL(vb_stats_stream<false>, dim3(grid), dim3(VT), 0, stream, a);
+  }
+  hipLaunchKernelGGL(vb_decide, dim3(B), dim3(DT), 0, stream, a);
   if (!greedy && k == 0) {
-    hipLaunchKernelGGL(vb_draw_sums, dim3(a.nch, B), dim3(VT), 0, stream, a);
+    if (vec) hipLaunchKernelGGL(vb_draw_sums<true>, dim3(a.nch, B), dim3(VT), 0, stream, a);
+    else hipLaunchKernelGGL(vb_draw_sums<false>, dim3(a.nch, B), dim3(VT), 0, stream, a);
     hipLaunchKernelGGL(vb_draw_pick, dim3(B), dim3(VT), 0, stream, a);
   }
   if (tprob || dprob)
-    hipLaunchKernelGGL(vb_write_probs, dim3(nblk), dim3(VT), 0, stream, a);
+    hipLaunchKernelGGL(vb_write_probs, dim3(unsigned(a.n_rows) * unsigned(a.nch)), dim3(VT), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -168,3 +168,14 @@ def test_full_size_27b_window_sampled_requests():
         say(f"  request {b} rel err {e:.2e}")
         assert e <= TOL
         assert np.abs(gl[b] - ol[0]).max() <= 1e-3
+
+
+def test_one_long_item_many_partials():
+    """One request, one KV head, 20000-token context: the item spans many
+    workgroups, so the merge combines many partial records."""
+    check(*case(1, 16, 4, 1, 64, [20000], 11)[:7], 0, label="long item")
+
+
+def test_batch1_4b_shape():
+    cfg = wl.CONFIGS["qwen3-4b"]
+    check(*case(1, cfg.K, cfg.n_q, cfg.n_kv, cfg.hd, [cfg.ctx_a], 12)[:7], 0, label="qwen3-4b")
