@@ -10,24 +10,24 @@
 // softmax), which is what lets the context be cut into chunks that run on
 // different compute units.
 //
-// Item = (request b, KV head g): its visible context in 64-key tiles plus one
-// tile holding the K in-block keys.  The item's query rows are the group's
-// (n_q / n_kv) heads at all K block positions (row r = i * group + hh).  The
-// partial kernel is persistent and balanced: all tiles of all items form one
-// sequence and each workgroup takes an equal run of it (the schedule is
-// rebuilt on the device from ctx_len, so ragged batches need no host copy of
-// the lengths); it writes one partial (O, max, normaliser) per item it
-// touches, and the merge kernel combines an item's partials exactly.  Each
-// wave owns 16-row blocks; the key tile is staged once in LDS and shared by
-// the four waves.
+// Item = (request b, KV head g): its visible context in 32-key tiles plus
+// ceil(K/32) tiles holding the K in-block keys.  The item's query rows are the
+// group's (n_q / n_kv) heads at all K block positions (row r = i * group + hh);
+// each wave owns 32 of them.  The partial kernel is persistent and balanced:
+// all tiles of all items form one sequence and each workgroup takes an equal
+// run of it (the schedule is rebuilt on the device from ctx_len, so ragged
+// batches need no host copy of the lengths); it writes one partial (O, max,
+// normaliser) per item it touches, and the merge kernel combines an item's
+// partials exactly.  A key tile is staged once in LDS and shared by the waves.
 //
-// Per 64-key tile and 16-row block, with the gfx950 16x16x32 bf16 MFMA:
+// Per 32-key tile and 32-row wave, with the gfx950 32x32x16 bf16 MFMA:
 //   S^T[key][row] = K[key][:] . Q[row][:]          (A = K from LDS, B = Q regs)
 //   online softmax per row in the exp2 domain
 //   O^T[dim][row] += V^T[dim][key] . P^T[key][row]  (A = V from LDS, B = P regs)
-// Keeping keys on the M side of S^T puts one row per lane column, so P leaves
-// the accumulators already in the B-operand layout (with a fixed permutation
-// of the 32 keys of a k-step that V's fragment reproduces).
+// Keys on the M side of S^T put one query row per lane column, so the score
+// accumulators already hold the B operand of the P.V product: within each 16
+// keys a lane holds keys 4h..4h+3 and 8+4h..8+4h+3 (h = lane / 32), and V^T is
+// staged with exactly that key order so its fragment is one 16-byte LDS read.
 #include "bd_common.hpp"
 #include "bd_launch.hpp"
 
@@ -35,19 +35,19 @@
 
 namespace bd {
 
-constexpr int AT = 256;  // threads per workgroup (4 waves)
+constexpr int TK = 32;   // keys per tile
+constexpr int MT = 256;  // threads of a merge workgroup
 
 // Register budget of the persistent partial kernel (waves per SIMD it must
-// allow); its grid is the number of workgroups that are resident at once
-// (CUs x workgroups per CU from the occupancy query), at most BD_ATTN_GRID.
+// allow); its grid is the number of workgroups resident at once (CUs x
+// workgroups per CU from the occupancy query), at most BD_ATTN_GRID.
 #ifndef BD_ATTN_GRID
-#define BD_ATTN_GRID 1024
+#define BD_ATTN_GRID 2048
 #endif
 #ifndef BD_ATTN_WPE
 #define BD_ATTN_WPE 2
 #endif
-#define BD_ATTN_OCC __attribute__((amdgpu_waves_per_eu(BD_ATTN_WPE)))
-constexpr int TK = 64;   // keys per tile
+#define BD_ATTN_OCC(NW) __attribute__((amdgpu_waves_per_eu(NW == 1 ? 1 : BD_ATTN_WPE)))
 
 struct AttnArgs {
   const uint16_t* q;
@@ -60,6 +60,7 @@ struct AttnArgs {
   int64_t T_cap;
   int B, K, n_q, n_kv, group, R;  // R = K * group query rows per item
   int window, max_ctx;
+  int nbt;                        // tiles of block keys per item, ceil(K / 32)
   int grid;                       // workgroups of the partial kernel
   int tmin;                       // fewest tiles a workgroup takes
   float sl2;                      // scale * log2(e)
@@ -79,13 +80,13 @@ __device__ __forceinline__ bool visible(const AttnArgs& a, int b, int64_t& base,
   return true;
 }
 
-// Tiles of request b: its visible context in 64-key tiles, then one tile for
-// the block keys.  Invalid requests get the block tile only.
+// Tiles of request b: its visible context in 32-key tiles, then the block
+// keys.  Invalid requests get the block tiles only.
 __device__ __forceinline__ int req_tiles(const AttnArgs& a, int b) {
   int64_t base;
   int lo, hi;
-  if (!visible(a, b, base, lo, hi)) return 1;
-  return (hi - lo + TK - 1) / TK + 1;
+  if (!visible(a, b, base, lo, hi)) return a.nbt;
+  return (hi - lo + TK - 1) / TK + a.nbt;
 }
 
 constexpr int TMIN = 4;     // fewest tiles a workgroup takes
@@ -102,8 +103,8 @@ struct Sched {
 
 __device__ Sched build_sched(const AttnArgs& a, int* s_pref /* [B + 1] */) {
   const int t = threadIdx.x;
-  // per-request tile counts, prefix by one thread per 256 requests (B <= 4096)
-  for (int b = t; b < a.B; b += AT) s_pref[b + 1] = req_tiles(a, b);
+  // per-request tile counts, prefix by thread 0
+  for (int b = t; b < a.B; b += blockDim.x) s_pref[b + 1] = req_tiles(a, b);
   __syncthreads();
   if (t == 0) {
     s_pref[0] = 0;
@@ -127,26 +128,41 @@ __device__ __forceinline__ int find_req(const AttnArgs& a, const int* s_pref, in
   return lo;
 }
 
-// Loads of one tile into registers: K as 16-byte pieces t + p * AT (key =
-// piece / (HD/8)); V as keys 4 kg .. 4 kg + 3 of column piece vd for threads
-// t < (HD/8) * 16 (kg = t % 16, vd = t / 16).  Loads are unconditional (keys
-// past the tile's end re-read key 0) so they stay in flight until used; the
-// caller masks keys >= the returned count.
-template <int HD>
-__device__ __forceinline__ int fetch_tile(const AttnArgs& a, int ti, int nt, int b, int g, int64_t cbase, int lo,
-                                          int nctx, int t, u32x4 (&pk)[TK * HD / 8 / AT], u32x4 (&pv)[4]) {
-  constexpr int PPT = TK * HD / 8 / AT;
-  constexpr int NDC = HD / 8;
-  constexpr int VTH = NDC * (TK / 4);
+// Staging of one 32-key tile by NT threads: K as 16-byte pieces
+// t + p * NT (key = piece / (HD/8)); V as units u = t + i * NT < 8 * (HD/8),
+// each four keys 4 kg .. 4 kg + 3 (kg = u % 8) of one 16-byte dim piece
+// vd = u / 8.  Loads are unconditional (keys past the tile end re-read a
+// valid line) so they stay in flight until used; the stager masks keys >=
+// the returned count.
+template <int HD, int NT>
+struct TileRegs {
+  static constexpr int KPIECES = TK * HD / 8;
+  static constexpr int KP = (KPIECES + NT - 1) / NT;
+  static constexpr int VUNITS = (TK / 4) * (HD / 8);
+  static constexpr int VU = (VUNITS + NT - 1) / NT;
+  u32x4 k[KP];
+  u32x4 v[VU][4];
+};
+
+template <int HD, int NT>
+__device__ __forceinline__ int fetch_tile(const AttnArgs& a, int ti, int nct, int nt, int b, int g,
+                                          int64_t cbase, int lo, int nctx, int t, TileRegs<HD, NT>& r) {
+  using TR = TileRegs<HD, NT>;
   const size_t kstride = size_t(a.n_kv) * HD;
-  const int kg = t & 15, vd = t >> 4;
   const uint16_t* kp;
   const uint16_t* vp;
   int nkeys;
-  if (ti == nt - 1) {
+  if (ti >= nt) {
+    // past the segment: the same number of loads from one valid line, so the
+    // count of loads in flight does not depend on the path
     kp = a.kb + (size_t(b) * a.K * a.n_kv + g) * HD;
-    vp = a.vb + (size_t(b) * a.K * a.n_kv + g) * HD;
-    nkeys = a.K;
+    vp = kp;
+    nkeys = 0;
+  } else if (ti >= nct) {
+    const int k0 = (ti - nct) * TK;
+    kp = a.kb + ((size_t(b) * a.K + k0) * a.n_kv + g) * HD;
+    vp = a.vb + ((size_t(b) * a.K + k0) * a.n_kv + g) * HD;
+    nkeys = min(TK, a.K - k0);
   } else {
     const int k0 = ti * TK;
     kp = a.kc + (size_t(cbase + lo + k0) * a.n_kv + g) * HD;
@@ -154,117 +170,135 @@ __device__ __forceinline__ int fetch_tile(const AttnArgs& a, int ti, int nt, int
     nkeys = min(TK, nctx - k0);
   }
 #pragma unroll
-  for (int p = 0; p < PPT; ++p) {
-    const int piece = t + p * AT;
-    const int key = piece / NDC, dc = piece - key * NDC;
-    pk[p] = ld_stream_v(kp + size_t(key < nkeys ? key : 0) * kstride + dc * 8);
+  for (int p = 0; p < TR::KP; ++p) {
+    const int piece = t + p * NT;
+    const int key = piece / (HD / 8), dc = piece - key * (HD / 8);
+    const bool in = piece < TR::KPIECES && key < nkeys;
+    r.k[p] = ld_stream_v(kp + (in ? size_t(key) * kstride + dc * 8 : 0));
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = 4 * kg + i;
-    const bool in = t < VTH && key < nkeys;
-    pv[i] = ld_stream_v(vp + (in ? size_t(key) * kstride + vd * 8 : 0));
+  for (int i = 0; i < TR::VU; ++i) {
+    const int u = t + i * NT;
+    const int kg = u & 7, vd = u >> 3;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int key = 4 * kg + c;
+      const bool in = u < TR::VUNITS && key < nkeys;
+      r.v[i][c] = ld_stream_v(vp + (in ? size_t(key) * kstride + vd * 8 : 0));
+    }
   }
   return nkeys;
 }
 
-// One key tile (in LDS) against the wave's 16-row blocks: scores, online
-// softmax in the exp2 domain, and the P.V accumulation.
-template <int HD, int RB>
-__device__ __forceinline__ void tile_math(const AttnArgs& a, const uint16_t* Ks, const uint16_t* Vt, int nvalid,
-                                          int w, int lr, int q4, const bf16x8 (&qf)[RB][HD / 32],
-                                          floatx4 (&acc)[RB][HD / 16], float (&m_run)[RB], float (&l_run)[RB]) {
+// LDS column of key 4 kg within a tile's V^T rows (see the header comment)
+__device__ __forceinline__ int vcol(int kg) { return 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1); }
+
+template <int HD, int NT>
+__device__ __forceinline__ void stage_tile(const TileRegs<HD, NT>& r, int nvalid, int t, uint16_t* Ks, uint16_t* Vt) {
+  using TR = TileRegs<HD, NT>;
   constexpr int LS = HD + 8;
   constexpr int LV = TK + 8;
-  constexpr int NKS = HD / 32;
-  constexpr int NDB = HD / 16;
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int j = 0; j < RB; ++j) {
-    if ((w + 4 * j) * 16 >= a.R) continue;
-    floatx4 s[4];
+  for (int p = 0; p < TR::KP; ++p) {
+    const int piece = t + p * NT;
+    const int key = piece / (HD / 8), dc = piece - key * (HD / 8);
+    if (piece < TR::KPIECES) *reinterpret_cast<u32x4*>(&Ks[key * LS + dc * 8]) = key < nvalid ? r.k[p] : z4;
+  }
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < TR::VU; ++i) {
+    const int u = t + i * NT;
+    if (u < TR::VUNITS) {
+      const int kg = u & 7, vd = u >> 3;
+      const int col = vcol(kg);
+      const u32x4 a0 = 4 * kg + 0 < nvalid ? r.v[i][0] : z4;
+      const u32x4 a1 = 4 * kg + 1 < nvalid ? r.v[i][1] : z4;
+      const u32x4 a2 = 4 * kg + 2 < nvalid ? r.v[i][2] : z4;
+      const u32x4 a3 = 4 * kg + 3 < nvalid ? r.v[i][3] : z4;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(&Ks[(kb * 16 + lr) * LS + ks * 32 + q4 * 8]);
-        s[kb] = mfma16x16x32(as_bf16x8(kv), qf[j][ks], s[kb]);
-      }
-    }
-    // lane holds keys kb*16 + 4*q4 + r for row lr
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kb * 16 + q4 * 4 + r;
-        float v = s[kb][r] * a.sl2;
-        v = key < nvalid ? v : -INFINITY;
-        s[kb][r] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run[j], tmax);
-    const float alpha = exp2f(m_run[j] - m_new);
-    m_run[j] = m_new;
-    float psum = 0.f;
-    uint32_t pw[8];  // P^T fragments: two k-steps of 32 keys, 4 dwords each
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      float pe[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pe[r] = exp2f(s[2 * ks2][r] - m_new);
-        pe[4 + r] = exp2f(s[2 * ks2 + 1][r] - m_new);
-      }
-#pragma unroll
-      for (int r = 0; r < 8; ++r) psum += pe[r];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pw[ks2 * 4 + r] = pack_bf16x2(pe[2 * r], pe[2 * r + 1]);
-    }
-    l_run[j] = l_run[j] * alpha + psum;
-#pragma unroll
-    for (int d = 0; d < NDB; ++d) acc[j][d] *= alpha;
-    // O^T += V^T P^T; the V fragment of lane (dim = 16d + lr) holds the
-    // same 8 keys of the k-step, in the same order, as its P fragment
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pw[ks2 * 4], pw[ks2 * 4 + 1], pw[ks2 * 4 + 2], pw[ks2 * 4 + 3]));
-#pragma unroll
-      for (int d = 0; d < NDB; ++d) {
-        const uint4 vf = *reinterpret_cast<const uint4*>(&Vt[(d * 16 + lr) * LV + ks2 * 32 + q4 * 8]);
-        acc[j][d] = mfma16x16x32(as_bf16x8(vf), pb, acc[j][d]);
+      for (int m = 0; m < 4; ++m) {
+        // dims 2m and 2m + 1 of the piece, keys 4 kg .. 4 kg + 3
+        const uint2 even = make_uint2((a0[m] & 0xffffu) | (a1[m] << 16), (a2[m] & 0xffffu) | (a3[m] << 16));
+        const uint2 odd = make_uint2((a0[m] >> 16) | (a1[m] & 0xffff0000u), (a2[m] >> 16) | (a3[m] & 0xffff0000u));
+        *reinterpret_cast<uint2*>(&Vt[(vd * 8 + 2 * m) * LV + col]) = even;
+        *reinterpret_cast<uint2*>(&Vt[(vd * 8 + 2 * m + 1) * LV + col]) = odd;
       }
     }
   }
 }
 
-template <int HD, int RB>
-__global__ __launch_bounds__(AT) BD_ATTN_OCC void attn_partial(AttnArgs a) {
-  constexpr int LS = HD + 8;          // K tile row stride (elements)
-  constexpr int LV = TK + 8;          // V^T tile row stride (elements)
-  constexpr int PIECES = TK * HD / 8;  // 16-byte pieces per tile
-  constexpr int PPT = PIECES / AT;     // K pieces per thread
-  constexpr int NDC = HD / 8;          // 16-byte pieces per key row
-  constexpr int VTH = NDC * (TK / 4);  // threads staging V (4 keys x 16 bytes each)
-  constexpr int NKS = HD / 32;         // k-steps of the score MFMA
-  constexpr int NDB = HD / 16;         // dim blocks of the output MFMA
-  // K tile row-major [key][dim]; V tile transposed [dim][column] with key k at
-  // column vcol(k): within each 32 keys, keys 4q..4q+3 and 16+4q..16+4q+3 sit
-  // side by side at columns 8q..8q+7, which is the order in which a lane's P
-  // fragment holds them, so a V fragment is one 16-byte LDS read.
+// One key tile (in LDS) against the wave's 32 query rows: scores, online
+// softmax in the exp2 domain, and the P.V accumulation.
+template <int HD>
+__device__ __forceinline__ void tile_math(const AttnArgs& a, const uint16_t* Ks, const uint16_t* Vt, int nvalid,
+                                          int lane, const bf16x8 (&qf)[HD / 16], floatx16 (&acc)[HD / 32],
+                                          float& m_run, float& l_run) {
+  constexpr int LS = HD + 8;
+  constexpr int LV = TK + 8;
+  const int lr = lane & 31, h = lane >> 5;
+  floatx16 s = {};
+#pragma unroll
+  for (int ks = 0; ks < HD / 16; ++ks) {
+    const u32x4 kf = *reinterpret_cast<const u32x4*>(&Ks[lr * LS + ks * 16 + h * 8]);
+    s = mfma32x32x16(__builtin_bit_cast(bf16x8, kf), qf[ks], s);
+  }
+  // lane holds keys 8 (r / 4) + 4 h + r % 4 of row lr
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = 8 * (r >> 2) + 4 * h + (r & 3);
+    const float v = key < nvalid ? s[r] * a.sl2 : -INFINITY;
+    s[r] = v;
+    tmax = fmaxf(tmax, v);
+  }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  const float m_new = fmaxf(m_run, tmax);
+  const float alpha = exp2_hw(m_run - m_new);
+  m_run = m_new;
+  float psum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s[r] = exp2_hw(s[r] - m_new);
+    psum += s[r];
+  }
+  l_run = l_run * alpha + psum;
+  if (__ballot(alpha != 1.f)) {
+#pragma unroll
+    for (int d = 0; d < HD / 32; ++d) acc[d] *= alpha;
+  }
+  // P^T fragments of the two 16-key steps: registers 8 s2 .. 8 s2 + 7
+  bf16x8 pb[2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+    pb[s2] = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(s[8 * s2 + 0], s[8 * s2 + 1]),
+                                                   pack_bf16x2(s[8 * s2 + 2], s[8 * s2 + 3]),
+                                                   pack_bf16x2(s[8 * s2 + 4], s[8 * s2 + 5]),
+                                                   pack_bf16x2(s[8 * s2 + 6], s[8 * s2 + 7])));
+#pragma unroll
+  for (int d = 0; d < HD / 32; ++d)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const u32x4 vf = *reinterpret_cast<const u32x4*>(&Vt[(d * 32 + lr) * LV + s2 * 16 + h * 8]);
+      acc[d] = mfma32x32x16(__builtin_bit_cast(bf16x8, vf), pb[s2], acc[d]);
+    }
+}
+
+template <int HD, int NW>
+__global__ __launch_bounds__(64 * NW) BD_ATTN_OCC(NW) void attn_partial(AttnArgs a) {
+  constexpr int NT = 64 * NW;
+  constexpr int LS = HD + 8;
+  constexpr int LV = TK + 8;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[TK * LS];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[HD * LV];
   extern __shared__ int s_pref[];
 
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int lr = lane & 15, q4 = lane >> 4;
+  const int lr = lane & 31, h = lane >> 5;
   const Sched sc = build_sched(a, s_pref);
   const int wg = blockIdx.x;
   int x = wg * sc.tpw;
   const int x_end = min(x + sc.tpw, sc.total);
-  const size_t kstride = size_t(a.n_kv) * HD;
+  const int row = w * 32 + lr;  // this lane's query row
 
   while (x < x_end) {
     // the segment of this workgroup inside one item
@@ -275,111 +309,69 @@ __global__ __launch_bounds__(AT) BD_ATTN_OCC void attn_partial(AttnArgs a) {
     const int t0 = x - item_s;                      // first tile of the item we take
     const int t1 = min(nt, x_end - item_s);         // one past the last
     const int item = b * a.n_kv + g;
-    int64_t cbase;
-    int lo, hi;
+    const int nct = nt - a.nbt;                     // context tiles of the item
+    int64_t cbase = 0;
+    int lo = 0, hi = 0;
     const bool ok = visible(a, b, cbase, lo, hi);
-    const int nctx = ok ? hi - lo : 0;              // context keys of the item
+    const int nctx = ok ? hi - lo : 0;
 
-    // query fragments: B operand of S^T, lane holds Q[row][32ks + 8q4 .. +8]
-    bf16x8 qf[RB][NKS];
+    // query fragments: B operand of S^T, lane holds Q[row][16 ks + 8 h .. +8]
+    bf16x8 qf[HD / 16];
 #pragma unroll
-    for (int j = 0; j < RB; ++j) {
-      const int row = (w + 4 * j) * 16 + lr;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (row < a.R) {
-          const int i = row / a.group, hh = row - i * a.group;
-          const uint16_t* qp = a.q + ((size_t(b) * a.K + i) * a.n_q + g * a.group + hh) * HD + ks * 32 + q4 * 8;
-          v = *reinterpret_cast<const uint4*>(qp);
-        }
-        qf[j][ks] = as_bf16x8(v);
+    for (int ks = 0; ks < HD / 16; ++ks) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row < a.R) {
+        const int i = row / a.group, hh = row - i * a.group;
+        v = *reinterpret_cast<const uint4*>(a.q + ((size_t(b) * a.K + i) * a.n_q + g * a.group + hh) * HD + ks * 16 + h * 8);
       }
+      qf[ks] = as_bf16x8(v);
     }
-    floatx4 acc[RB][NDB];
-    float m_run[RB], l_run[RB];
+    floatx16 acc[HD / 32];
 #pragma unroll
-    for (int j = 0; j < RB; ++j) {
-      m_run[j] = -INFINITY;
-      l_run[j] = 0.f;
-#pragma unroll
-      for (int d = 0; d < NDB; ++d) acc[j][d] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int d = 0; d < HD / 32; ++d) acc[d] = floatx16{};
+    float m_run = -INFINITY, l_run = 0.f;
 
-    // tile ti < nt - 1: context keys [lo + 64 ti, ...); tile nt - 1: block keys
-    // K: thread loads pieces t + p * AT (key = piece / NDC, 16-byte column
-    // piece % NDC); V: thread t < VTH loads keys 4 kg .. 4 kg + 3 of 16-byte
-    // column vd, kg = t % 16, vd = t / 16.
-    const int kg = t & 15, vd = t >> 4;
-    u32x4 pk[PPT], pv[4];
-    int nvalid_next = fetch_tile<HD>(a, t0, nt, b, g, cbase, lo, nctx, t, pk, pv);
-    // all tiles but the last: the look-ahead fetch is unconditional
+    TileRegs<HD, NT> regs;
+    int nvalid_next = fetch_tile<HD, NT>(a, t0, nct, nt, b, g, cbase, lo, nctx, t, regs);
     for (int ti = t0; ti < t1; ++ti) {
       const int nvalid = nvalid_next;
       __syncthreads();
-      // the loads were unconditional: keys past the tile's valid count are
-      // zeroed here, where the data is consumed
-      const u32x4 z4 = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int p = 0; p < PPT; ++p) {
-        const int piece = t + p * AT;
-        const int key = piece / NDC, dc = piece - key * NDC;
-        *reinterpret_cast<u32x4*>(&Ks[key * LS + dc * 8]) = key < nvalid ? pk[p] : z4;
-      }
-      if (t < VTH) {
-        // transpose 4 keys x 8 dims into 8 dims x 4 keys (bf16 pairs)
-        const int col = 32 * (kg >> 3) + 8 * (kg & 3) + 4 * ((kg >> 2) & 1);
-        const u32x4 a0 = 4 * kg + 0 < nvalid ? pv[0] : z4;
-        const u32x4 a1 = 4 * kg + 1 < nvalid ? pv[1] : z4;
-        const u32x4 a2 = 4 * kg + 2 < nvalid ? pv[2] : z4;
-        const u32x4 a3 = 4 * kg + 3 < nvalid ? pv[3] : z4;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint2 even = make_uint2((a0[m] & 0xffffu) | (a1[m] << 16), (a2[m] & 0xffffu) | (a3[m] << 16));
-          const uint2 odd = make_uint2((a0[m] >> 16) | (a1[m] & 0xffff0000u), (a2[m] >> 16) | (a3[m] & 0xffff0000u));
-          *reinterpret_cast<uint2*>(&Vt[(vd * 8 + 2 * m) * LV + col]) = even;
-          *reinterpret_cast<uint2*>(&Vt[(vd * 8 + 2 * m + 1) * LV + col]) = odd;
-        }
-      }
+      stage_tile<HD, NT>(regs, nvalid, t, Ks, Vt);
       __syncthreads();
-      if (ti + 1 == t1) {
-        tile_math<HD, RB>(a, Ks, Vt, nvalid, w, lr, q4, qf, acc, m_run, l_run);
-        break;
-      }
-      nvalid_next = fetch_tile<HD>(a, ti + 1, nt, b, g, cbase, lo, nctx, t, pk, pv);
-      tile_math<HD, RB>(a, Ks, Vt, nvalid, w, lr, q4, qf, acc, m_run, l_run);
+      // look-ahead for the next tile (past the segment end: a dummy fetch of
+      // one line), in flight during this tile's MFMAs
+      nvalid_next = fetch_tile<HD, NT>(a, ti + 1 < t1 ? ti + 1 : nt, nct, nt, b, g, cbase, lo, nctx, t, regs);
+      tile_math<HD>(a, Ks, Vt, nvalid, lane, qf, acc, m_run, l_run);
     }
 
     // partial result of (item, workgroup): slot item + wg is unique because a
     // later item only starts in a workgroup at or after this one's last
     const size_t slot = size_t(item) + wg;
+    const float l = l_run + __shfl_xor(l_run, 32);
+    if (row < a.R) {
+      float* o = a.wo + (slot * a.R + row) * HD;
 #pragma unroll
-    for (int j = 0; j < RB; ++j) {
-      const int row = (w + 4 * j) * 16 + lr;
-      float l = l_run[j];
-      l += __shfl_xor(l, 16);
-      l += __shfl_xor(l, 32);
-      if (row < a.R) {
-        float* o = a.wo + (slot * a.R + row) * HD;
+      for (int d = 0; d < HD / 32; ++d)
 #pragma unroll
-        for (int d = 0; d < NDB; ++d)
-          *reinterpret_cast<floatx4*>(o + d * 16 + q4 * 4) = acc[j][d];
-        if (q4 == 0) {
-          a.wml[(slot * a.R + row) * 2] = m_run[j];
-          a.wml[(slot * a.R + row) * 2 + 1] = l;
-        }
+        for (int r4 = 0; r4 < 4; ++r4)
+          *reinterpret_cast<float4*>(o + d * 32 + 8 * r4 + 4 * h) =
+              make_float4(acc[d][4 * r4], acc[d][4 * r4 + 1], acc[d][4 * r4 + 2], acc[d][4 * r4 + 3]);
+      if (h == 0) {
+        a.wml[(slot * a.R + row) * 2] = m_run;
+        a.wml[(slot * a.R + row) * 2 + 1] = l;
       }
     }
     x = item_s + t1;
   }
 }
 
+constexpr int MRS = 16;  // query rows per merge workgroup
+
 template <int HD>
-__global__ __launch_bounds__(AT) void attn_merge(AttnArgs a) {
+__global__ __launch_bounds__(MT) void attn_merge(AttnArgs a) {
   extern __shared__ int s_pref[];
-  __shared__ float s_f[MAXSEG * 128];  // per record and row: 2^(m - M) / L
-  __shared__ int s_ns;
-  const int item = blockIdx.x, t = threadIdx.x;
+  __shared__ float s_f[MAXSEG * MRS];  // per record and row: 2^(m - M) / L
+  const int item = blockIdx.x, r0 = blockIdx.y * MRS, t = threadIdx.x;
   const int b = item / a.n_kv, g = item - b * a.n_kv;
   const Sched sc = build_sched(a, s_pref);
   const int nt = s_pref[b + 1] - s_pref[b];
@@ -390,8 +382,10 @@ __global__ __launch_bounds__(AT) void attn_merge(AttnArgs a) {
   int lo, hi;
   const bool ok = visible(a, b, cbase, lo, hi) && ns <= MAXSEG;
   const size_t slot0 = size_t(item) + w0;
-  if (t < a.R) {
-    const int row = t;
+  const int nr = min(MRS, a.R - r0);
+  if (nr <= 0) return;
+  if (t < nr) {
+    const int row = r0 + t;
     float M = -INFINITY;
     for (int s = 0; s < ns; ++s) M = fmaxf(M, a.wml[((slot0 + s) * a.R + row) * 2]);
     float L = 0.f;
@@ -401,15 +395,16 @@ __global__ __launch_bounds__(AT) void attn_merge(AttnArgs a) {
     }
     const float inv = 1.f / L;
     if (ok)
-      for (int s = 0; s < ns; ++s) s_f[s * 128 + row] = exp2f(a.wml[((slot0 + s) * a.R + row) * 2] - M) * inv;
+      for (int s = 0; s < ns; ++s) s_f[s * MRS + t] = exp2f(a.wml[((slot0 + s) * a.R + row) * 2] - M) * inv;
     const int i = row / a.group, hh = row - i * a.group;
     const size_t oidx = (size_t(b) * a.K + i) * a.n_q + g * a.group + hh;
     if (a.lse) a.lse[oidx] = ok ? (M + log2f(L)) * 0.6931471805599453f : NAN;
   }
   __syncthreads();
   // outputs four dims at a time; the records of one float4 load independently
-  for (int e4 = t; e4 < a.R * HD / 4; e4 += AT) {
-    const int row = e4 / (HD / 4), d4 = (e4 - row * (HD / 4)) * 4;
+  for (int e4 = t; e4 < nr * HD / 4; e4 += MT) {
+    const int rr = e4 / (HD / 4), d4 = (e4 - rr * (HD / 4)) * 4;
+    const int row = r0 + rr;
     const int i = row / a.group, hh = row - i * a.group;
     const size_t oidx = (size_t(b) * a.K + i) * a.n_q + g * a.group + hh;
     uint2 packed;
@@ -418,7 +413,7 @@ __global__ __launch_bounds__(AT) void attn_merge(AttnArgs a) {
     } else {
       float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int s = 0; s < ns; ++s) {
-        const float f = s_f[s * 128 + row];
+        const float f = s_f[s * MRS + rr];
         const float4 v = *reinterpret_cast<const float4*>(a.wo + ((slot0 + s) * a.R + row) * HD + d4);
         o.x += v.x * f; o.y += v.y * f; o.z += v.z * f; o.w += v.w * f;
       }
@@ -434,10 +429,10 @@ static inline size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr int PARTIAL_GRID = BD_ATTN_GRID;
 
 // At least TMIN tiles per workgroup, and enough that one item (at most
-// vis/64 + 1 tiles) spans no more than MAXSEG workgroups.
+// ceil(vis/32) + 2 tiles) spans no more than MAXSEG workgroups.
 static int attn_tmin(int max_ctx, int window) {
   const int vis = (window > 0 && max_ctx > window) ? window : max_ctx;
-  const int nt_max = (vis + TK - 1) / TK + 1;
+  const int nt_max = (vis + TK - 1) / TK + 2;
   const int t = (nt_max + MAXSEG - 3) / (MAXSEG - 2);
   return t > TMIN ? t : TMIN;
 }
@@ -445,7 +440,7 @@ static int attn_tmin(int max_ctx, int window) {
 // upper bound of the grid (sizes the workspace)
 static int attn_grid(int B, int n_kv, int max_ctx, int window) {
   const int vis = (window > 0 && max_ctx > window) ? window : max_ctx;
-  const long long tiles = (long long)B * n_kv * ((vis + TK - 1) / TK + 1);  // upper bound
+  const long long tiles = (long long)B * n_kv * ((vis + TK - 1) / TK + 2);  // upper bound
   const int tmin = attn_tmin(max_ctx, window);
   long long g = (tiles + tmin - 1) / tmin;
   if (g > PARTIAL_GRID) g = PARTIAL_GRID;
@@ -453,16 +448,17 @@ static int attn_grid(int B, int n_kv, int max_ctx, int window) {
   return int(g);
 }
 
-// Workgroups of attn_partial<HD, RB> that fit on the device at once (queried
+// Workgroups of attn_partial<HD, NW> that fit on the device at once (queried
 // once per variant; falls back to two per CU on 256 CUs).
-template <int HD, int RB>
+template <int HD, int NW>
 static int resident_partial() {
   static const int n = [] {
     int dev = 0, cus = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, attn_partial<HD, RB>, AT, 4096) != hipSuccess || per < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, attn_partial<HD, NW>, 64 * NW, 4096) != hipSuccess ||
+        per < 1)
       per = 2;
     return cus * per;
   }();
@@ -476,6 +472,25 @@ size_t attn_ws_bytes(int B, int K, int n_q, int n_kv, int hd, int max_ctx, int w
   return al(slots * R * hd * 4) + al(slots * R * 2 * 4);
 }
 
+// one partial-kernel variant: NW = ceil(R / 32) waves of 32 query rows
+template <int HD, int NW>
+static void run_partial(AttnArgs& a, size_t pref_bytes, hipStream_t stream) {
+  const int resident = resident_partial<HD, NW>();
+  if (a.grid > resident) a.grid = resident;
+  hipLaunchKernelGGL((attn_partial<HD, NW>), dim3(a.grid), dim3(64 * NW), pref_bytes, stream, a);
+}
+
+template <int HD>
+static void run_attn(AttnArgs& a, size_t pref_bytes, hipStream_t stream) {
+  switch ((a.R + 31) / 32) {
+    case 1: run_partial<HD, 1>(a, pref_bytes, stream); break;
+    case 2: run_partial<HD, 2>(a, pref_bytes, stream); break;
+    case 3: run_partial<HD, 3>(a, pref_bytes, stream); break;
+    default: run_partial<HD, 4>(a, pref_bytes, stream); break;
+  }
+  hipLaunchKernelGGL(attn_merge<HD>, dim3(a.B * a.n_kv, (a.R + MRS - 1) / MRS), dim3(MT), pref_bytes, stream, a);
+}
+
 hipError_t launch_attn(const uint16_t* q, const uint16_t* kb, const uint16_t* vb, const uint16_t* kc,
                        const uint16_t* vc, const int64_t* cache_base, const int32_t* ctx_len,
                        int64_t T_cap, int max_ctx, int B, int K, int n_q, int n_kv, int hd, int window,
@@ -486,12 +501,10 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* kb, const uint16_t* vb
   a.cache_base = cache_base; a.ctx_len = ctx_len; a.T_cap = T_cap;
   a.B = B; a.K = K; a.n_q = n_q; a.n_kv = n_kv; a.group = n_q / n_kv; a.R = K * a.group;
   a.window = window; a.max_ctx = max_ctx;
+  a.nbt = (K + TK - 1) / TK;
   a.tmin = attn_tmin(max_ctx, window);
-  const bool two = a.R > 64;
-  const int resident = hd == 128 ? (two ? resident_partial<128, 2>() : resident_partial<128, 1>())
-                                 : (two ? resident_partial<64, 2>() : resident_partial<64, 1>());
+  // the workspace holds items + attn_grid() partial slots; the launch may use fewer
   a.grid = attn_grid(B, n_kv, max_ctx, window);
-  if (a.grid > resident) a.grid = resident;
   const float sc = scale > 0.f ? scale : float(1.0 / sqrt(double(hd)));
   a.sl2 = float(double(sc) * 1.4426950408889634);
   a.out = out; a.lse = lse;
@@ -500,15 +513,8 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* kb, const uint16_t* vb
   a.wo = static_cast<float*>(ws);
   a.wml = reinterpret_cast<float*>(static_cast<char*>(ws) + al(slots * R * hd * 4));
   const size_t pref_bytes = size_t(B + 1) * sizeof(int);
-  if (hd == 128) {
-    if (two) hipLaunchKernelGGL((attn_partial<128, 2>), dim3(a.grid), dim3(AT), pref_bytes, stream, a);
-    else hipLaunchKernelGGL((attn_partial<128, 1>), dim3(a.grid), dim3(AT), pref_bytes, stream, a);
-    hipLaunchKernelGGL(attn_merge<128>, dim3(B * n_kv), dim3(AT), pref_bytes, stream, a);
-  } else {
-    if (two) hipLaunchKernelGGL((attn_partial<64, 2>), dim3(a.grid), dim3(AT), pref_bytes, stream, a);
-    else hipLaunchKernelGGL((attn_partial<64, 1>), dim3(a.grid), dim3(AT), pref_bytes, stream, a);
-    hipLaunchKernelGGL(attn_merge<64>, dim3(B * n_kv), dim3(AT), pref_bytes, stream, a);
-  }
+  if (hd == 128) run_attn<128>(a, pref_bytes, stream);
+  else run_attn<64>(a, pref_bytes, stream);
   return hipGetLastError();
 }
 
