@@ -47,6 +47,10 @@ constexpr int MT = 256;  // threads of a merge workgroup
 #ifndef BD_ATTN_WPE
 #define BD_ATTN_WPE 2
 #endif
+// stages of the partial kernel's LDS tile ring (S - 1 tiles in flight)
+#ifndef BD_ATTN_STAGES
+#define BD_ATTN_STAGES 3
+#endif
 #define BD_ATTN_OCC(NW) __attribute__((amdgpu_waves_per_eu(NW == 1 ? 1 : BD_ATTN_WPE)))
 
 struct AttnArgs {
@@ -59,6 +63,7 @@ struct AttnArgs {
   const int32_t* ctx_len;
   int64_t T_cap;
   int B, K, n_q, n_kv, group, R;  // R = K * group query rows per item
+  int Rp;                         // R rounded up to whole 32-row wave blocks
   int window, max_ctx;
   int nbt;                        // tiles of block keys per item, ceil(K / 32)
   int grid;                       // workgroups of the partial kernel
@@ -66,14 +71,18 @@ struct AttnArgs {
   float sl2;                      // scale * log2(e)
   uint16_t* out;
   float* lse;
-  float* wo;   // [items + grid][R][HD] partial outputs
-  float* wml;  // [items + grid][R][2]  running max (exp2 domain), normaliser
+  float* wo;   // [items + grid][Rp / 32][HD / 32][4][64 lanes][4] partial outputs
+  float* wml;  // [items + grid][Rp][2]  running max (exp2 domain), normaliser
 };
 
 // visible context of request b, or ok = false when its metadata is invalid
+// (cache_base and ctx_len are read through the constant address space: they do
+// not change during a call, so uniform reads become scalar loads)
+typedef const __attribute__((address_space(4))) int64_t c_int64;
+typedef const __attribute__((address_space(4))) int32_t c_int32;
 __device__ __forceinline__ bool visible(const AttnArgs& a, int b, int64_t& base, int& lo, int& hi) {
-  base = a.cache_base[b];
-  int ctx = a.ctx_len[b];
+  base = ((c_int64*)a.cache_base)[b];
+  int ctx = ((c_int32*)a.ctx_len)[b];
   if (ctx < 0 || ctx > a.max_ctx || base < 0 || base + ctx > a.T_cap) return false;
   lo = (a.window > 0 && ctx > a.window) ? ctx - a.window : 0;
   hi = ctx;
@@ -112,7 +121,8 @@ __device__ Sched build_sched(const AttnArgs& a, int* s_pref /* [B + 1] */) {
   }
   __syncthreads();
   Sched s;
-  s.total = a.n_kv * s_pref[a.B];
+  // values read from LDS are the same in every lane: keep them in scalar registers
+  s.total = __builtin_amdgcn_readfirstlane(a.n_kv * s_pref[a.B]);
   int tpw = (s.total + a.grid - 1) / a.grid;
   s.tpw = tpw < a.tmin ? a.tmin : tpw;
   return s;
@@ -128,137 +138,231 @@ __device__ __forceinline__ int find_req(const AttnArgs& a, const int* s_pref, in
   return lo;
 }
 
-// Staging of one 32-key tile by NT threads: K as 16-byte pieces
-// t + p * NT (key = piece / (HD/8)); V as units u = t + i * NT < 8 * (HD/8),
-// each four keys 4 kg .. 4 kg + 3 (kg = u % 8) of one 16-byte dim piece
-// vd = u / 8.  Loads are unconditional (keys past the tile end re-read a
-// valid line) so they stay in flight until used; the stager masks keys >=
-// the returned count.
-template <int HD, int NT>
-struct TileRegs {
-  static constexpr int KPIECES = TK * HD / 8;
-  static constexpr int KP = (KPIECES + NT - 1) / NT;
-  static constexpr int VUNITS = (TK / 4) * (HD / 8);
-  static constexpr int VU = (VUNITS + NT - 1) / NT;
-  u32x4 k[KP];
-  u32x4 v[VU][4];
+// ---------------------------------------------------------------- tile ring
+// A stage of the LDS ring holds one 32-key tile: K, then V, each [32 keys][HD]
+// bf16 as 16-byte pieces, 16 pieces to a 256-byte line (HD = 128: one key per
+// line, HD = 64: two).  Tiles arrive straight from HBM (global_load_lds, 16
+// bytes per lane, a wave filling 1 KB of consecutive pieces), so the pieces of
+// a line are XOR-permuted by swz(line) instead of padded.  swz makes both MFMA
+// operand reads conflict-free: the K reads (16 lanes, 16 keys, one piece each)
+// need a bijection over 16 consecutive keys, the V transpose reads (32 lanes,
+// 4 aligned keys x 4 consecutive pieces) need those 4 keys to differ in piece
+// bits 2..3 (HD = 128), or two consecutive lines in bit 2 (HD = 64).
+template <int HD>
+__device__ __forceinline__ int swz(int line) {
+  if constexpr (HD == 128) return ((line & 3) << 2) | ((line >> 2) & 3);
+  else return ((line & 1) << 2) | ((line >> 1) & 3);
+}
+
+// byte offset, inside a K or V tile, of dims [8c, 8c + 8) of key `key`
+template <int HD>
+__device__ __forceinline__ int piece_off(int key, int c) {
+  constexpr int P = HD / 8;
+  const int flat = key * P + c, line = flat >> 4;
+  return (line * 16 + ((flat & 15) ^ swz<HD>(line))) * 16;
+}
+
+// 16 bytes from global address base + voff (base the same for the whole wave)
+// to LDS byte address lds_base + 16 * lane.  Issued as inline assembly so the
+// compiler inserts no wait of its own for these loads: the ring tracks them
+// with explicit vmcnt waits and a barrier.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
+// wait until at most N vector memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Tiles are consumed in order and loads complete in order, so tile x is in LDS
+// once no more than the loads of the `ahead` tiles issued after it remain.
+template <int L, int A>
+__device__ __forceinline__ void wait_tiles(int ahead) {
+  if constexpr (A == 0) {
+    vm_wait<0>();
+  } else {
+    if (ahead >= A) vm_wait<A * L>();
+    else wait_tiles<L, A - 1>(ahead);
+  }
+}
+
+// Position of a workgroup in its run of tiles: request b, KV head g, tile ti
+// of that item (context tiles first, then block tiles).
+struct Cur {
+  int b, g, ti, nt, nct, lo, nctx;
+  int64_t cbase;
 };
 
-template <int HD, int NT>
-__device__ __forceinline__ int fetch_tile(const AttnArgs& a, int ti, int nct, int nt, int b, int g,
-                                          int64_t cbase, int lo, int nctx, int t, TileRegs<HD, NT>& r) {
-  using TR = TileRegs<HD, NT>;
-  const size_t kstride = size_t(a.n_kv) * HD;
+__device__ __forceinline__ void cur_item(const AttnArgs& a, const int* s_pref, Cur& c) {
+  c.b = __builtin_amdgcn_readfirstlane(c.b);
+  c.nt = __builtin_amdgcn_readfirstlane(s_pref[c.b + 1] - s_pref[c.b]);
+  c.nct = c.nt - a.nbt;
+  int64_t base = 0;
+  int lo = 0, hi = 0;
+  const bool ok = visible(a, c.b, base, lo, hi);
+  c.cbase = ok ? base : 0;
+  c.lo = ok ? lo : 0;
+  c.nctx = ok ? hi - lo : 0;
+}
+
+__device__ __forceinline__ void cur_init(const AttnArgs& a, const int* s_pref, Cur& c, int x) {
+  c.b = __builtin_amdgcn_readfirstlane(find_req(a, s_pref, x));
+  const int nt = __builtin_amdgcn_readfirstlane(s_pref[c.b + 1] - s_pref[c.b]);
+  const int r = x - a.n_kv * __builtin_amdgcn_readfirstlane(s_pref[c.b]);
+  c.g = r / nt;
+  c.ti = r - c.g * nt;
+  cur_item(a, s_pref, c);
+}
+
+__device__ __forceinline__ void cur_next(const AttnArgs& a, const int* s_pref, Cur& c) {
+  if (++c.ti < c.nt) return;
+  c.ti = 0;
+  if (++c.g == a.n_kv) {
+    c.g = 0;
+    if (++c.b >= a.B) return;  // past the last tile: never read
+  }
+  cur_item(a, s_pref, c);
+}
+
+// first K and V rows of the cursor's tile; returns its number of keys (>= 1)
+template <int HD>
+__device__ __forceinline__ int tile_src(const AttnArgs& a, const Cur& c, const uint16_t*& kp, const uint16_t*& vp) {
+  if (c.ti >= c.nct) {
+    const int k0 = (c.ti - c.nct) * TK;
+    const size_t o = ((size_t(c.b) * a.K + k0) * a.n_kv + c.g) * HD;
+    kp = a.kb + o;
+    vp = a.vb + o;
+    return min(TK, a.K - k0);
+  }
+  const int k0 = c.ti * TK;
+  const size_t o = (size_t(c.cbase + c.lo + k0) * a.n_kv + c.g) * HD;
+  kp = a.kc + o;
+  vp = a.vc + o;
+  return min(TK, c.nctx - k0);
+}
+
+// Loads of one tile into a ring stage: 2 * NH one-KB wave loads spread over
+// the waves (wave w issues loads w, w + NW, ...; its t-th is load w + t NW).
+// Lane l of load j fills piece slot 64 (j % NH) + l of the K (j < NH) or V
+// half.  lane_piece() gives that slot's key and 16-byte column; for a full
+// tile the byte offsets from the tile's first row are fixed per lane and
+// computed once (voff); a short tile re-reads its last key in place of the
+// missing ones (their scores are masked).
+template <int HD>
+__device__ __forceinline__ void lane_piece(int jj, int lane, int& key, int& cc) {
+  constexpr int P = HD / 8;
+  const int ps = jj * 64 + lane, line = ps >> 4;
+  const int flat = line * 16 + ((ps & 15) ^ swz<HD>(line));
+  key = flat / P;
+  cc = flat % P;
+}
+
+template <int HD, int NW>
+struct IssuePlan {
+  static constexpr int TB = TK * HD * 2, NH = TB / 1024;
+  static constexpr int LMAX = (2 * NH + NW - 1) / NW;
+  uint32_t voff[LMAX];  // byte offsets of a full tile
+};
+
+template <int HD, int NW>
+__device__ __forceinline__ void plan_init(IssuePlan<HD, NW>& pl, int kstride_bytes, int w, int lane) {
+  using PL = IssuePlan<HD, NW>;
+#pragma unroll
+  for (int t = 0; t < PL::LMAX; ++t) {
+    const int j = w + t * NW;
+    const int jj = j >= PL::NH ? j - PL::NH : j;
+    int key, cc;
+    lane_piece<HD>(jj, lane, key, cc);
+    pl.voff[t] = uint32_t(key * kstride_bytes + cc * 16);
+  }
+}
+
+template <int HD, int NW>
+__device__ __forceinline__ void issue_tile(const AttnArgs& a, const Cur& c, const IssuePlan<HD, NW>& pl,
+                                           uint32_t stage, int w, int lane) {
+  using PL = IssuePlan<HD, NW>;
   const uint16_t* kp;
   const uint16_t* vp;
-  int nkeys;
-  if (ti >= nt) {
-    // past the segment: the same number of loads from one valid line, so the
-    // count of loads in flight does not depend on the path
-    kp = a.kb + (size_t(b) * a.K * a.n_kv + g) * HD;
-    vp = kp;
-    nkeys = 0;
-  } else if (ti >= nct) {
-    const int k0 = (ti - nct) * TK;
-    kp = a.kb + ((size_t(b) * a.K + k0) * a.n_kv + g) * HD;
-    vp = a.vb + ((size_t(b) * a.K + k0) * a.n_kv + g) * HD;
-    nkeys = min(TK, a.K - k0);
-  } else {
-    const int k0 = ti * TK;
-    kp = a.kc + (size_t(cbase + lo + k0) * a.n_kv + g) * HD;
-    vp = a.vc + (size_t(cbase + lo + k0) * a.n_kv + g) * HD;
-    nkeys = min(TK, nctx - k0);
-  }
+  const int nkeys = tile_src<HD>(a, c, kp, vp);
+  const int kstride_bytes = a.n_kv * HD * 2;
 #pragma unroll
-  for (int p = 0; p < TR::KP; ++p) {
-    const int piece = t + p * NT;
-    const int key = piece / (HD / 8), dc = piece - key * (HD / 8);
-    const bool in = piece < TR::KPIECES && key < nkeys;
-    r.k[p] = ld_stream_v(kp + (in ? size_t(key) * kstride + dc * 8 : 0));
-  }
-#pragma unroll
-  for (int i = 0; i < TR::VU; ++i) {
-    const int u = t + i * NT;
-    const int kg = u & 7, vd = u >> 3;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int key = 4 * kg + c;
-      const bool in = u < TR::VUNITS && key < nkeys;
-      r.v[i][c] = ld_stream_v(vp + (in ? size_t(key) * kstride + vd * 8 : 0));
-    }
-  }
-  return nkeys;
-}
-
-// LDS column of key 4 kg within a tile's V^T rows (see the header comment)
-__device__ __forceinline__ int vcol(int kg) { return 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1); }
-
-template <int HD, int NT>
-__device__ __forceinline__ void stage_tile(const TileRegs<HD, NT>& r, int nvalid, int t, uint16_t* Ks, uint16_t* Vt) {
-  using TR = TileRegs<HD, NT>;
-  constexpr int LS = HD + 8;
-  constexpr int LV = TK + 8;
-  const u32x4 z4 = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int p = 0; p < TR::KP; ++p) {
-    const int piece = t + p * NT;
-    const int key = piece / (HD / 8), dc = piece - key * (HD / 8);
-    if (piece < TR::KPIECES) *reinterpret_cast<u32x4*>(&Ks[key * LS + dc * 8]) = key < nvalid ? r.k[p] : z4;
-  }
-#pragma unroll
-  for (int i = 0; i < TR::VU; ++i) {
-    const int u = t + i * NT;
-    if (u < TR::VUNITS) {
-      const int kg = u & 7, vd = u >> 3;
-      const int col = vcol(kg);
-      const u32x4 a0 = 4 * kg + 0 < nvalid ? r.v[i][0] : z4;
-      const u32x4 a1 = 4 * kg + 1 < nvalid ? r.v[i][1] : z4;
-      const u32x4 a2 = 4 * kg + 2 < nvalid ? r.v[i][2] : z4;
-      const u32x4 a3 = 4 * kg + 3 < nvalid ? r.v[i][3] : z4;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        // dims 2m and 2m + 1 of the piece, keys 4 kg .. 4 kg + 3
-        const uint2 even = make_uint2((a0[m] & 0xffffu) | (a1[m] << 16), (a2[m] & 0xffffu) | (a3[m] << 16));
-        const uint2 odd = make_uint2((a0[m] >> 16) | (a1[m] & 0xffff0000u), (a2[m] >> 16) | (a3[m] & 0xffff0000u));
-        *reinterpret_cast<uint2*>(&Vt[(vd * 8 + 2 * m) * LV + col]) = even;
-        *reinterpret_cast<uint2*>(&Vt[(vd * 8 + 2 * m + 1) * LV + col]) = odd;
+  for (int t = 0; t < PL::LMAX; ++t) {
+    const int j = w + t * NW;
+    if (j < 2 * PL::NH) {
+      const bool isv = j >= PL::NH;
+      const int jj = isv ? j - PL::NH : j;
+      uint32_t off = pl.voff[t];
+      if (nkeys < TK) {
+        int key, cc;
+        lane_piece<HD>(jj, lane, key, cc);
+        off = uint32_t(min(key, nkeys - 1) * kstride_bytes + cc * 16);
       }
+      dma16(isv ? vp : kp, off, stage + (isv ? PL::TB : 0) + jj * 1024);
     }
   }
 }
 
-// One key tile (in LDS) against the wave's 32 query rows: scores, online
-// softmax in the exp2 domain, and the P.V accumulation.
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two probabilities to packed bf16 (round to nearest even)
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Query fragments of item (b, g) for this lane's row (rows past R re-read row
+// R - 1; their results are never used): the B operand of S^T, lane holds
+// Q[row][16 ks + 8 h .. + 8].
 template <int HD>
-__device__ __forceinline__ void tile_math(const AttnArgs& a, const uint16_t* Ks, const uint16_t* Vt, int nvalid,
-                                          int lane, const bf16x8 (&qf)[HD / 16], floatx16 (&acc)[HD / 32],
-                                          float& m_run, float& l_run) {
-  constexpr int LS = HD + 8;
-  constexpr int LV = TK + 8;
+__device__ __forceinline__ void load_q(const AttnArgs& a, int b, int g, int row, int h, bf16x8 (&qf)[HD / 16]) {
+  const int r = min(row, a.R - 1);
+  const int i = r / a.group, hh = r - i * a.group;
+  const uint16_t* p = a.q + ((size_t(b) * a.K + i) * a.n_q + g * a.group + hh) * HD + h * 8;
+#pragma unroll
+  for (int ks = 0; ks < HD / 16; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(p + ks * 16));
+}
+
+// One key tile (K at byte kt, V at byte vt of LDS) against the wave's 32 query
+// rows: scores, online softmax in the exp2 domain, and the P.V accumulation.
+template <int HD>
+__device__ __forceinline__ void tile_math(const AttnArgs& a, const uint8_t* lds, uint32_t kt, uint32_t vt,
+                                          int nvalid, int lane, const bf16x8 (&qf)[HD / 16],
+                                          floatx16 (&acc)[HD / 32], float& m_run, float& l_run) {
   const int lr = lane & 31, h = lane >> 5;
   floatx16 s = {};
 #pragma unroll
   for (int ks = 0; ks < HD / 16; ++ks) {
-    const u32x4 kf = *reinterpret_cast<const u32x4*>(&Ks[lr * LS + ks * 16 + h * 8]);
+    const u32x4 kf = *reinterpret_cast<const u32x4*>(lds + kt + piece_off<HD>(lr, 2 * ks + h));
     s = mfma32x32x16(__builtin_bit_cast(bf16x8, kf), qf[ks], s);
   }
-  // lane holds keys 8 (r / 4) + 4 h + r % 4 of row lr
+  // lane holds keys 8 (r / 4) + 4 h + r % 4 of row lr; masked keys get -inf
   float tmax = -INFINITY;
+  if (nvalid < TK) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int key = 8 * (r >> 2) + 4 * h + (r & 3);
-    const float v = key < nvalid ? s[r] * a.sl2 : -INFINITY;
-    s[r] = v;
-    tmax = fmaxf(tmax, v);
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * h + (r & 3);
+      s[r] = key < nvalid ? s[r] : -INFINITY;
+    }
   }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-  const float m_new = fmaxf(m_run, tmax);
+  // running maximum in the exp2 domain (scores times scale * log2(e) > 0)
+  const float m_new = fmaxf(m_run, tmax * a.sl2);
   const float alpha = exp2_hw(m_run - m_new);
   m_run = m_new;
   float psum = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    s[r] = exp2_hw(s[r] - m_new);
+    s[r] = exp2_hw(fmaf(s[r], a.sl2, -m_new));
     psum += s[r];
   }
   l_run = l_run * alpha + psum;
@@ -270,156 +374,216 @@ __device__ __forceinline__ void tile_math(const AttnArgs& a, const uint16_t* Ks,
   bf16x8 pb[2];
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2)
-    pb[s2] = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(s[8 * s2 + 0], s[8 * s2 + 1]),
-                                                   pack_bf16x2(s[8 * s2 + 2], s[8 * s2 + 3]),
-                                                   pack_bf16x2(s[8 * s2 + 4], s[8 * s2 + 5]),
-                                                   pack_bf16x2(s[8 * s2 + 6], s[8 * s2 + 7])));
+    pb[s2] = __builtin_bit_cast(bf16x8, make_uint4(pk_bf16(s[8 * s2 + 0], s[8 * s2 + 1]),
+                                                   pk_bf16(s[8 * s2 + 2], s[8 * s2 + 3]),
+                                                   pk_bf16(s[8 * s2 + 4], s[8 * s2 + 5]),
+                                                   pk_bf16(s[8 * s2 + 6], s[8 * s2 + 7])));
+  // V^T fragments by transpose reads: in each group of 16 lanes, lane 4e + q
+  // points at key k0 + e, dims 4q .. 4q + 3 of the group's 16 dims, and lane i
+  // receives dim i of keys k0 .. k0 + 3.  Two reads give the lane's 8 keys
+  // (4h .. 4h + 3 and 8 + 4h .. 8 + 4h + 3 of the 16-key step).
+  const int gi = lane & 15, e = gi >> 2, q = gi & 3, gh = (lane >> 4) & 1;
 #pragma unroll
-  for (int d = 0; d < HD / 32; ++d)
+  for (int d = 0; d < HD / 32; ++d) {
+    const int c = 4 * d + 2 * gh + (q >> 1);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      const u32x4 vf = *reinterpret_cast<const u32x4*>(&Vt[(d * 32 + lr) * LV + s2 * 16 + h * 8]);
-      acc[d] = mfma32x32x16(__builtin_bit_cast(bf16x8, vf), pb[s2], acc[d]);
+      const int k0 = 16 * s2 + 4 * h + e;
+      const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (lds_bf16x4*)(lds + vt + piece_off<HD>(k0, c) + 8 * (q & 1)));
+      const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (lds_bf16x4*)(lds + vt + piece_off<HD>(k0 + 8, c) + 8 * (q & 1)));
+      const bf16x8 vf = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc[d] = mfma32x32x16(vf, pb[s2], acc[d]);
     }
+  }
 }
 
 template <int HD, int NW>
 __global__ __launch_bounds__(64 * NW) BD_ATTN_OCC(NW) void attn_partial(AttnArgs a) {
-  constexpr int NT = 64 * NW;
-  constexpr int LS = HD + 8;
-  constexpr int LV = TK + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[TK * LS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[HD * LV];
+  constexpr int S = BD_ATTN_STAGES;
+  constexpr int TB = TK * HD * 2;
+  constexpr int NI = 2 * TB / 1024;          // one-KB loads per tile
+  constexpr int LMAX = (NI + NW - 1) / NW;   // loads per tile of wave 0
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[S * 2 * TB];
   extern __shared__ int s_pref[];
 
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lr = lane & 31, h = lane >> 5;
   const Sched sc = build_sched(a, s_pref);
   const int wg = blockIdx.x;
-  int x = wg * sc.tpw;
-  const int x_end = min(x + sc.tpw, sc.total);
+  const int x0 = wg * sc.tpw;
+  const int x_end = min(x0 + sc.tpw, sc.total);
+  if (x0 >= x_end) return;
+  const bool full_wave = (NI % NW == 0) || w < NI % NW;  // issues LMAX loads per tile
+  const uint32_t ring0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring)));
   const int row = w * 32 + lr;  // this lane's query row
 
-  while (x < x_end) {
-    // the segment of this workgroup inside one item
-    const int b = find_req(a, s_pref, x);
-    const int nt = s_pref[b + 1] - s_pref[b];
-    const int g = (x - a.n_kv * s_pref[b]) / nt;
-    const int item_s = a.n_kv * s_pref[b] + g * nt;
-    const int t0 = x - item_s;                      // first tile of the item we take
-    const int t1 = min(nt, x_end - item_s);         // one past the last
-    const int item = b * a.n_kv + g;
-    const int nct = nt - a.nbt;                     // context tiles of the item
-    int64_t cbase = 0;
-    int lo = 0, hi = 0;
-    const bool ok = visible(a, b, cbase, lo, hi);
-    const int nctx = ok ? hi - lo : 0;
-
-    // query fragments: B operand of S^T, lane holds Q[row][16 ks + 8 h .. +8]
-    bf16x8 qf[HD / 16];
+  IssuePlan<HD, NW> plan;
+  plan_init<HD, NW>(plan, a.n_kv * HD * 2, w, lane);
+  Cur ic, cc;
+  cur_init(a, s_pref, ic, x0);
+  cc = ic;
 #pragma unroll
-    for (int ks = 0; ks < HD / 16; ++ks) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (row < a.R) {
-        const int i = row / a.group, hh = row - i * a.group;
-        v = *reinterpret_cast<const uint4*>(a.q + ((size_t(b) * a.K + i) * a.n_q + g * a.group + hh) * HD + ks * 16 + h * 8);
+  for (int s = 0; s < S - 1; ++s) {
+    if (x0 + s < x_end) {
+      issue_tile<HD, NW>(a, ic, plan, ring0 + s * 2 * TB, w, lane);
+      cur_next(a, s_pref, ic);
+    }
+  }
+
+  bf16x8 qf[HD / 16];
+  floatx16 acc[HD / 32];
+  float m_run = -INFINITY, l_run = 0.f;
+  int stage = 0;
+  int ready = x0 - 1;  // tiles up to here are known to be in LDS
+  for (int x = x0; x < x_end; ++x) {
+    if (x > ready) {
+      const int ahead = min(S - 2, x_end - 1 - x);
+      if (full_wave) wait_tiles<LMAX, S - 2>(ahead);
+      else wait_tiles<(LMAX > 1 ? LMAX - 1 : 1), S - 2>(ahead);
+    }
+    __syncthreads();
+    if (x == x0) {
+      load_q<HD>(a, cc.b, cc.g, row, h, qf);
+      vm_wait<0>();
+      ready = x + S - 2;
+    }
+    if (x == x0 || cc.ti == 0) {
+#pragma unroll
+      for (int d = 0; d < HD / 32; ++d) acc[d] = floatx16{};
+      m_run = -INFINITY;
+      l_run = 0.f;
+    }
+    // refill the stage that every wave finished with before the barrier
+    if (x + S - 1 < x_end) {
+      const int st = stage == 0 ? S - 1 : stage - 1;
+      issue_tile<HD, NW>(a, ic, plan, ring0 + st * 2 * TB, w, lane);
+      cur_next(a, s_pref, ic);
+    }
+    const uint16_t* kp;
+    const uint16_t* vp;
+    const int nvalid = tile_src<HD>(a, cc, kp, vp);
+    tile_math<HD>(a, ring, stage * 2 * TB, stage * 2 * TB + TB, nvalid, lane, qf, acc, m_run, l_run);
+
+    if (x == x_end - 1 || cc.ti == cc.nt - 1) {
+      if (x < x_end - 1) {
+        // the next item's query rows, waited for before this segment's stores
+        // are issued: a store is never waited for inside the loop (stores may
+        // complete out of order with loads; the tile waits above rely only on
+        // loads completing in order)
+        Cur nx = cc;
+        cur_next(a, s_pref, nx);
+        load_q<HD>(a, nx.b, nx.g, row, h, qf);
+        vm_wait<0>();
+        ready = x + S - 1;
       }
-      qf[ks] = as_bf16x8(v);
-    }
-    floatx16 acc[HD / 32];
-#pragma unroll
-    for (int d = 0; d < HD / 32; ++d) acc[d] = floatx16{};
-    float m_run = -INFINITY, l_run = 0.f;
-
-    TileRegs<HD, NT> regs;
-    int nvalid_next = fetch_tile<HD, NT>(a, t0, nct, nt, b, g, cbase, lo, nctx, t, regs);
-    for (int ti = t0; ti < t1; ++ti) {
-      const int nvalid = nvalid_next;
-      __syncthreads();
-      stage_tile<HD, NT>(regs, nvalid, t, Ks, Vt);
-      __syncthreads();
-      // look-ahead for the next tile (past the segment end: a dummy fetch of
-      // one line), in flight during this tile's MFMAs
-      nvalid_next = fetch_tile<HD, NT>(a, ti + 1 < t1 ? ti + 1 : nt, nct, nt, b, g, cbase, lo, nctx, t, regs);
-      tile_math<HD>(a, Ks, Vt, nvalid, lane, qf, acc, m_run, l_run);
-    }
-
-    // partial result of (item, workgroup): slot item + wg is unique because a
-    // later item only starts in a workgroup at or after this one's last
-    const size_t slot = size_t(item) + wg;
-    const float l = l_run + __shfl_xor(l_run, 32);
-    if (row < a.R) {
-      float* o = a.wo + (slot * a.R + row) * HD;
+      // partial result of (item, workgroup): slot item + wg is unique because a
+      // later item only starts in a workgroup at or after this one's last.
+      // O^T is stored in accumulator order, so each store is one contiguous
+      // KB: float4 (d, r4, lane) holds dims 32 d + 8 r4 + 4 h .. + 3 of row lr
+      const size_t slot = size_t(cc.b) * a.n_kv + cc.g + wg;
+      const float l = l_run + __shfl_xor(l_run, 32);
+      float* o = a.wo + (slot * (a.Rp / 32) + w) * (32 * HD);
 #pragma unroll
       for (int d = 0; d < HD / 32; ++d)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
-          *reinterpret_cast<float4*>(o + d * 32 + 8 * r4 + 4 * h) =
+          *reinterpret_cast<float4*>(o + ((d * 4 + r4) * 64 + lane) * 4) =
               make_float4(acc[d][4 * r4], acc[d][4 * r4 + 1], acc[d][4 * r4 + 2], acc[d][4 * r4 + 3]);
-      if (h == 0) {
-        a.wml[(slot * a.R + row) * 2] = m_run;
-        a.wml[(slot * a.R + row) * 2 + 1] = l;
-      }
+      if (h == 0) *reinterpret_cast<float2*>(a.wml + (slot * a.Rp + row) * 2) = make_float2(m_run, l);
     }
-    x = item_s + t1;
+    cur_next(a, s_pref, cc);
+    stage = stage == S - 1 ? 0 : stage + 1;
   }
 }
 
-constexpr int MRS = 16;  // query rows per merge workgroup
-
+// One workgroup per (item, 32-row wave block): the records' (max, normaliser)
+// pairs are read in parallel into LDS, each row's weights 2^(m_s - M) / L
+// follow, then the weighted sum of the records in their stored (accumulator)
+// order, with the loads of four records in flight together, transposed through
+// LDS so the bf16 rows leave as whole rows.
 template <int HD>
 __global__ __launch_bounds__(MT) void attn_merge(AttnArgs a) {
   extern __shared__ int s_pref[];
-  __shared__ float s_f[MAXSEG * MRS];  // per record and row: 2^(m - M) / L
-  const int item = blockIdx.x, r0 = blockIdx.y * MRS, t = threadIdx.x;
+  __shared__ float2 s_ml[MAXSEG * 32];                                  // [record][row]
+  __shared__ float s_f[MAXSEG * 32];                                    // [record][row]
+  __shared__ __attribute__((aligned(16))) uint16_t s_o[32 * (HD + 8)];  // bf16 rows
+  const int item = blockIdx.x, wb = blockIdx.y, t = threadIdx.x;
   const int b = item / a.n_kv, g = item - b * a.n_kv;
   const Sched sc = build_sched(a, s_pref);
   const int nt = s_pref[b + 1] - s_pref[b];
   const int item_s = a.n_kv * s_pref[b] + g * nt;
   const int w0 = item_s / sc.tpw, w1 = (item_s + nt - 1) / sc.tpw;
-  const int ns = w1 - w0 + 1;
+  const int ns = min(w1 - w0 + 1, MAXSEG);
   int64_t cbase;
   int lo, hi;
-  const bool ok = visible(a, b, cbase, lo, hi) && ns <= MAXSEG;
+  const bool ok = visible(a, b, cbase, lo, hi) && w1 - w0 + 1 <= MAXSEG;
   const size_t slot0 = size_t(item) + w0;
-  const int nr = min(MRS, a.R - r0);
-  if (nr <= 0) return;
-  if (t < nr) {
-    const int row = r0 + t;
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, a.wml[((slot0 + s) * a.R + row) * 2]);
-    float L = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float ms = a.wml[((slot0 + s) * a.R + row) * 2];
-      L += a.wml[((slot0 + s) * a.R + row) * 2 + 1] * exp2f(ms - M);
-    }
-    const float inv = 1.f / L;
-    if (ok)
-      for (int s = 0; s < ns; ++s) s_f[s * MRS + t] = exp2f(a.wml[((slot0 + s) * a.R + row) * 2] - M) * inv;
-    const int i = row / a.group, hh = row - i * a.group;
-    const size_t oidx = (size_t(b) * a.K + i) * a.n_q + g * a.group + hh;
-    if (a.lse) a.lse[oidx] = ok ? (M + log2f(L)) * 0.6931471805599453f : NAN;
+  const int nr = min(32, a.R - 32 * wb);  // valid rows of this block
+  for (int e = t; e < ns * 32; e += MT) {
+    const int s = e >> 5, r = e & 31;
+    s_ml[e] = *reinterpret_cast<const float2*>(a.wml + ((slot0 + s) * a.Rp + 32 * wb + r) * 2);
   }
   __syncthreads();
-  // outputs four dims at a time; the records of one float4 load independently
-  for (int e4 = t; e4 < nr * HD / 4; e4 += MT) {
-    const int rr = e4 / (HD / 4), d4 = (e4 - rr * (HD / 4)) * 4;
-    const int row = r0 + rr;
+  if (t < 32) {
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, s_ml[s * 32 + t].x);
+    float L = 0.f;
+    for (int s = 0; s < ns; ++s) L += s_ml[s * 32 + t].y * exp2f(s_ml[s * 32 + t].x - M);
+    const float inv = 1.f / L;
+    for (int s = 0; s < ns; ++s) s_f[s * 32 + t] = exp2f(s_ml[s * 32 + t].x - M) * inv;
+    if (t < nr && a.lse) {
+      const int row = 32 * wb + t;
+      const int i = row / a.group, hh = row - i * a.group;
+      a.lse[(size_t(b) * a.K + i) * a.n_q + g * a.group + hh] = ok ? (M + log2f(L)) * 0.6931471805599453f : NAN;
+    }
+  }
+  __syncthreads();
+  // float4 p of a record: (d, r4, lane) -> row lane % 32, dims 32 d + 8 r4 + 4 (lane / 32)
+  constexpr int NP = 32 * HD / 4, PPT = NP / MT;
+  const float* base = a.wo + (slot0 * (a.Rp / 32) + wb) * (32 * HD);
+  const size_t rstride = size_t(a.Rp) * HD;  // floats between consecutive records
+  float4 o[PPT];
+#pragma unroll
+  for (int k = 0; k < PPT; ++k) o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < ns; s0 += 4) {
+    float4 v[4][PPT];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s = min(s0 + u, ns - 1);  // a repeated record gets weight 0
+#pragma unroll
+      for (int k = 0; k < PPT; ++k)
+        v[u][k] = *reinterpret_cast<const float4*>(base + s * rstride + size_t(t + k * MT) * 4);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int k = 0; k < PPT; ++k) {
+        const int rr = (t + k * MT) & 31;
+        const float f = s0 + u < ns ? s_f[(s0 + u) * 32 + rr] : 0.f;
+        o[k].x += v[u][k].x * f; o[k].y += v[u][k].y * f; o[k].z += v[u][k].z * f; o[k].w += v[u][k].w * f;
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PPT; ++k) {
+    const int p = t + k * MT;
+    const int lane = p & 63, dr = p >> 6, d = dr >> 2, r4 = dr & 3;
+    const int rr = lane & 31, dim = 32 * d + 8 * r4 + 4 * (lane >> 5);
+    const uint2 packed = ok ? make_uint2(pack_bf16x2(o[k].x, o[k].y), pack_bf16x2(o[k].z, o[k].w))
+                            : make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
+    *reinterpret_cast<uint2*>(&s_o[rr * (HD + 8) + dim]) = packed;
+  }
+  __syncthreads();
+  // whole rows out: 16 bytes per thread
+  for (int e = t; e < nr * (HD / 8); e += MT) {
+    const int rr = e / (HD / 8), c8 = (e - rr * (HD / 8)) * 8;
+    const int row = 32 * wb + rr;
     const int i = row / a.group, hh = row - i * a.group;
     const size_t oidx = (size_t(b) * a.K + i) * a.n_q + g * a.group + hh;
-    uint2 packed;
-    if (!ok) {
-      packed = make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
-    } else {
-      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int s = 0; s < ns; ++s) {
-        const float f = s_f[s * MRS + rr];
-        const float4 v = *reinterpret_cast<const float4*>(a.wo + ((slot0 + s) * a.R + row) * HD + d4);
-        o.x += v.x * f; o.y += v.y * f; o.z += v.z * f; o.w += v.w * f;
-      }
-      packed = make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
-    }
-    *reinterpret_cast<uint2*>(a.out + oidx * HD + d4) = packed;
+    *reinterpret_cast<uint4*>(a.out + oidx * HD + c8) = *reinterpret_cast<const uint4*>(&s_o[rr * (HD + 8) + c8]);
   }
 }
 
@@ -467,9 +631,9 @@ static int resident_partial() {
 
 size_t attn_ws_bytes(int B, int K, int n_q, int n_kv, int hd, int max_ctx, int window) {
   if (B <= 0) return 0;
-  const size_t R = size_t(K) * (n_q / n_kv);
+  const size_t Rp = (size_t(K) * (n_q / n_kv) + 31) / 32 * 32;
   const size_t slots = size_t(B) * n_kv + attn_grid(B, n_kv, max_ctx, window);
-  return al(slots * R * hd * 4) + al(slots * R * 2 * 4);
+  return al(slots * Rp * hd * 4) + al(slots * Rp * 2 * 4);
 }
 
 // one partial-kernel variant: NW = ceil(R / 32) waves of 32 query rows
@@ -488,7 +652,7 @@ static void run_attn(AttnArgs& a, size_t pref_bytes, hipStream_t stream) {
     case 3: run_partial<HD, 3>(a, pref_bytes, stream); break;
     default: run_partial<HD, 4>(a, pref_bytes, stream); break;
   }
-  hipLaunchKernelGGL(attn_merge<HD>, dim3(a.B * a.n_kv, (a.R + MRS - 1) / MRS), dim3(MT), pref_bytes, stream, a);
+  hipLaunchKernelGGL(attn_merge<HD>, dim3(a.B * a.n_kv, a.Rp / 32), dim3(MT), pref_bytes, stream, a);
 }
 
 hipError_t launch_attn(const uint16_t* q, const uint16_t* kb, const uint16_t* vb, const uint16_t* kc,
@@ -500,6 +664,7 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* kb, const uint16_t* vb
   a.q = q; a.kb = kb; a.vb = vb; a.kc = kc; a.vc = vc;
   a.cache_base = cache_base; a.ctx_len = ctx_len; a.T_cap = T_cap;
   a.B = B; a.K = K; a.n_q = n_q; a.n_kv = n_kv; a.group = n_q / n_kv; a.R = K * a.group;
+  a.Rp = (a.R + 31) / 32 * 32;
   a.window = window; a.max_ctx = max_ctx;
   a.nbt = (K + TK - 1) / TK;
   a.tmin = attn_tmin(max_ctx, window);
@@ -508,10 +673,10 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* kb, const uint16_t* vb
   const float sc = scale > 0.f ? scale : float(1.0 / sqrt(double(hd)));
   a.sl2 = float(double(sc) * 1.4426950408889634);
   a.out = out; a.lse = lse;
-  const size_t R = size_t(a.R);
+  const size_t Rp = size_t(a.Rp);
   const size_t slots = size_t(B) * n_kv + a.grid;
   a.wo = static_cast<float*>(ws);
-  a.wml = reinterpret_cast<float*>(static_cast<char*>(ws) + al(slots * R * hd * 4));
+  a.wml = reinterpret_cast<float*>(static_cast<char*>(ws) + al(slots * Rp * hd * 4));
   const size_t pref_bytes = size_t(B + 1) * sizeof(int);
   if (hd == 128) run_attn<128>(a, pref_bytes, stream);
   else run_attn<64>(a, pref_bytes, stream);
