@@ -162,23 +162,6 @@ __device__ __forceinline__ int piece_off(int key, int c) {
   return (line * 16 + ((flat & 15) ^ swz<HD>(line))) * 16;
 }
 
-// 16 bytes from global address base + voff (base the same for the whole wave)
-// to LDS byte address lds_base + 16 * lane.  Issued as inline assembly so the
-// compiler inserts no wait of its own for these loads: the ring tracks them
-// with explicit vmcnt waits and a barrier.
-__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base),
-               "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory");
-}
-
-// wait until at most N vector memory operations of this wave are outstanding
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // Tiles are consumed in order and loads complete in order, so tile x is in LDS
 // once no more than the loads of the `ahead` tiles issued after it remain.
 template <int L, int A>

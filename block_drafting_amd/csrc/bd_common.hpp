@@ -49,6 +49,31 @@ __device__ __forceinline__ float4 ld_stream(const float* p) {
   return make_float4(v[0], v[1], v[2], v[3]);
 }
 
+// ---------------------------------------------------------------- global -> LDS
+// 16 bytes from global address base + voff (base the same for the whole wave)
+// to LDS byte address lds_base + 16 * lane; NT marks data read once (streamed
+// past the caches at low priority).  Issued as inline assembly so the compiler
+// inserts no wait of its own for these loads: callers track them with
+// explicit vmcnt waits and a barrier.
+template <bool NT = true>
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
+  if constexpr (NT)
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+  else
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+}
+
+// wait until at most N vector memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // 2^x with the hardware instruction (no denormal-result handling): used for
 // softmax terms exp((z - max) / T), where a result below 2^-126 is negligible
 // next to the term 1 of the maximum itself.

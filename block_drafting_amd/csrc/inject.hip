@@ -131,6 +131,181 @@ __global__ __launch_bounds__(GT) void ik_gemm(GemmArgs g) {
     }
 }
 
+// ---------------------------------------------------------------- wide-M projection
+// For M > 256: one workgroup computes a 512 x 128 tile over its d_in range, so
+// every weight row is read from HBM once (the rows of H are re-read from L2).
+// Eight waves as 4 (M) x 2 (N), each a 128 x 64 tile of 32x32x16 MFMAs.  Both
+// operands reach LDS straight from global memory (global_load_lds, 16 bytes per
+// lane) through rings of SA (H) and SW (W) stages of BK-wide d_in steps; in
+// iteration k a wave issues its W loads of step k + SW - 1, then its H loads of
+// step k + SA - 1 (SW >= SA, so the W loads of a step are always older than its
+// H loads).  A row is BK / 8 pieces of 16 bytes; the pieces of each 256-byte
+// line are XOR-permuted so the operand reads (16 lanes: 16 rows, one piece
+// each) are conflict-free.
+constexpr int WBM = 512, WBN = 128;
+#ifndef BD_GEMM_WIDE_WAVES
+#define BD_GEMM_WIDE_WAVES 8
+#endif
+constexpr int WNW = BD_GEMM_WIDE_WAVES;  // 8: 4 (M) x 2 (N) waves of 128 x 64; 4: 4 x 1 of 128 x 128
+constexpr int WNT = 64 * WNW;
+constexpr int WFN = WNW == 8 ? 2 : 4;    // 32-column blocks per wave
+#ifndef BD_GEMM_WIDE_BK
+#define BD_GEMM_WIDE_BK 64
+#endif
+#ifndef BD_GEMM_WIDE_SA
+#define BD_GEMM_WIDE_SA 2
+#endif
+#ifndef BD_GEMM_WIDE_SW
+#define BD_GEMM_WIDE_SW 2
+#endif
+constexpr int WBK = BD_GEMM_WIDE_BK, WSA = BD_GEMM_WIDE_SA, WSW = BD_GEMM_WIDE_SW;
+static_assert(WSW >= WSA && WSA >= 2, "ring depths");
+constexpr int WA_BYTES = WBM * WBK * 2;
+constexpr int WW_BYTES = WBN * WBK * 2;
+constexpr int WA_PW = WA_BYTES / 1024 / WNW;  // H loads per wave per step
+constexpr int WW_PW = WW_BYTES / 1024 / WNW;  // W loads per wave per step
+static_assert(WSA * WA_BYTES + WSW * WW_BYTES <= 160 * 1024, "LDS");
+
+// byte offset of piece c (16 bytes) of row `row` in a stage
+__device__ __forceinline__ int wpiece(int row, int c) {
+  constexpr int P = WBK / 8, RPL = 16 / P;  // pieces per row, rows per line
+  const int line = row / RPL;
+  return (line * 16 + (((row % RPL) * P + c) ^ (line & (P - 1)))) * 16;
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait_le(int n) {
+  if constexpr (N == 0) {
+    vm_wait<0>();
+  } else {
+    if (n >= N) vm_wait<N>();
+    else vm_wait_le<N - 1>(n);
+  }
+}
+
+// ops a wave issues after its H loads of step k (loads complete in order, so
+// once no more than these remain, step k's H and W loads have landed)
+__device__ __forceinline__ int wide_younger(int k, int ns) {
+  int n = 0;
+  // rest of the iteration that issued H step k (k - SA + 1): nothing after H
+  for (int j = k - WSA + 2; j <= k - 1; ++j) {
+    if (j + WSW - 1 < ns) n += WW_PW;
+    if (j + WSA - 1 < ns) n += WA_PW;
+  }
+  return n;
+}
+
+__global__ __launch_bounds__(WNT) void ik_gemm_wide(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ringA[WSA * WA_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ringW[WSW * WW_BYTES];
+  constexpr int P = WBK / 8;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = WNW == 8 ? w >> 1 : w, wn = WNW == 8 ? w & 1 : 0;
+  const int lr = lane & 31, h = lane >> 5;
+  const int tile = blockIdx.x, split = blockIdx.y;
+  const int tm = tile / g.tiles_n, tn = tile - tm * g.tiles_n;
+  const int m0 = tm * WBM, n0 = tn * WBN;
+  const int step0 = split * g.steps_per_split;
+  const int ns = min(g.steps_per_split, g.Kd / WBK - step0);
+  const uint32_t lA = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ringA)));
+  const uint32_t lW = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ringW)));
+
+  // per-lane byte offsets of this wave's loads from the step's first column:
+  // load q of the wave fills piece slots 64 (w + WNW q) + lane of a stage
+  uint32_t offA[WA_PW], offW[WW_PW];
+#pragma unroll
+  for (int q = 0; q < WA_PW; ++q) {
+    const int ps = (w + WNW * q) * 64 + lane;
+    // the (row, piece) that wpiece places at slot ps
+    constexpr int RPL = 16 / P;
+    const int line = ps >> 4, lc = (ps & 15) ^ (line & (P - 1));
+    const int row = line * RPL + lc / P, c = lc % P;
+    const int m = min(m0 + row, g.M - 1);  // rows past M re-read row M - 1; never stored
+    offA[q] = uint32_t(m * g.Kd * 2 + c * 16);
+  }
+#pragma unroll
+  for (int q = 0; q < WW_PW; ++q) {
+    const int ps = (w + WNW * q) * 64 + lane;
+    constexpr int RPL = 16 / P;
+    const int line = ps >> 4, lc = (ps & 15) ^ (line & (P - 1));
+    const int row = line * RPL + lc / P, c = lc % P;
+    offW[q] = uint32_t(row * g.Kd * 2 + c * 16);
+  }
+  const uint16_t* Abase = g.A + size_t(step0) * WBK;
+  const uint16_t* Wbase = g.Bw + size_t(n0) * g.Kd + size_t(step0) * WBK;
+
+  floatx16 acc[4][WFN];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < WFN; ++j) acc[i][j] = floatx16{};
+
+  // prologue: the iterations before the loop, W steps 0 .. SW - SA - 1 alone,
+  // then (W step j + SW - 1, H step j + SA - 1) for j = -(SA - 1) .. -1
+  for (int k = 0; k < WSW - WSA && k < ns; ++k)
+#pragma unroll
+    for (int q = 0; q < WW_PW; ++q)
+      dma16<true>(Wbase + size_t(k) * WBK, offW[q], lW + (k % WSW) * WW_BYTES + (w + WNW * q) * 1024);
+  for (int j = -(WSA - 1); j < 0; ++j) {
+    const int kw = j + WSW - 1, ka = j + WSA;
+    if (kw < ns)
+#pragma unroll
+      for (int q = 0; q < WW_PW; ++q)
+        dma16<true>(Wbase + size_t(kw) * WBK, offW[q], lW + (kw % WSW) * WW_BYTES + (w + WNW * q) * 1024);
+    if (ka - 1 < ns && ka - 1 >= 0)
+#pragma unroll
+      for (int q = 0; q < WA_PW; ++q)
+        dma16<false>(Abase + size_t(ka - 1) * WBK, offA[q], lA + ((ka - 1) % WSA) * WA_BYTES + (w + WNW * q) * 1024);
+  }
+  for (int k = 0; k < ns; ++k) {
+    vm_wait_le<(WSA - 2) * (WA_PW + WW_PW)>(wide_younger(k, ns));
+    __syncthreads();
+    // refill the stages consumed in iteration k - 1
+    {
+      const int kw = k + WSW - 1, ka = k + WSA - 1;
+      if (kw < ns)
+#pragma unroll
+        for (int q = 0; q < WW_PW; ++q)
+          dma16<true>(Wbase + size_t(kw) * WBK, offW[q], lW + (kw % WSW) * WW_BYTES + (w + WNW * q) * 1024);
+      if (ka < ns)
+#pragma unroll
+        for (int q = 0; q < WA_PW; ++q)
+          dma16<false>(Abase + size_t(ka) * WBK, offA[q], lA + (ka % WSA) * WA_BYTES + (w + WNW * q) * 1024);
+    }
+    const uint8_t* As = ringA + (k % WSA) * WA_BYTES;
+    const uint8_t* Ws = ringW + (k % WSW) * WW_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < WBK / 16; ++kk) {
+      bf16x8 af[4], bfr[WFN];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(As + wpiece(128 * wm + 32 * i + lr, 2 * kk + h)));
+#pragma unroll
+      for (int j = 0; j < WFN; ++j)
+        bfr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Ws + wpiece(64 * wn + 32 * j + lr, 2 * kk + h)));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < WFN; ++j) acc[i][j] = mfma32x32x16(af[i], bfr[j], acc[i][j]);
+    }
+  }
+
+  // C block layout: lane holds column (lane & 31), rows 8 (r / 4) + 4 h + r % 4
+  float* P_ = g.P + size_t(split) * g.M * g.N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < WFN; ++j) {
+      const int n = n0 + 64 * wn + 32 * j + lr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (m < g.M) P_[size_t(m) * g.N + n] = acc[i][j][r];
+      }
+    }
+}
+
 struct FinishArgs {
   const float* P;  // [S][M][N]
   const uint16_t* gain;  // [L][hd] or NULL
@@ -239,14 +414,32 @@ static inline size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 #define BD_GEMM_WGS 512
 #endif
 
+#ifndef BD_GEMM_WIDE_WGS
+#define BD_GEMM_WIDE_WGS 256
+#endif
+
 struct GemmPlan {
   int bm, bn, bk, S, steps_per_split, tiles;
+  bool wide;
 };
 
-// Large M: 256 x BD_GEMM_BN tiles; small M (weight-bound): 64 x 128 tiles.
-// Split d_in until about BD_GEMM_WGS workgroups run.
+// M > 256: 512 x 128 tiles of the wide kernel, d_in split until about one
+// workgroup per CU runs.  Otherwise 256 x BD_GEMM_BN tiles (M > 128) or
+// 64 x 128 tiles (small M, weight-bound), split until about BD_GEMM_WGS run.
 static GemmPlan gemm_plan(int M, int N, int Kd) {
   GemmPlan p;
+  p.wide = M > 256 && N % WBN == 0;
+  if (p.wide) {
+    p.bm = WBM; p.bn = WBN; p.bk = WBK;
+    p.tiles = ((M + WBM - 1) / WBM) * (N / WBN);
+    const int steps = Kd / WBK;
+    int S = (BD_GEMM_WIDE_WGS + p.tiles / 2) / p.tiles;
+    if (S > steps) S = steps;
+    if (S < 1) S = 1;
+    p.steps_per_split = (steps + S - 1) / S;
+    p.S = (steps + p.steps_per_split - 1) / p.steps_per_split;
+    return p;
+  }
   const bool big = M > 128 && N % BD_GEMM_BN == 0;
   p.bm = big ? 256 : 64;
   p.bn = big ? BD_GEMM_BN : 128;
@@ -281,7 +474,8 @@ hipError_t launch_inject(const uint16_t* h, const uint16_t* w, const uint16_t* g
   g.M = M; g.N = N; g.Kd = d_in; g.S = p.S; g.steps_per_split = p.steps_per_split;
   g.tiles_n = N / p.bn;
   dim3 grid(p.tiles, p.S);
-  if (p.bm == 256) hipLaunchKernelGGL((ik_gemm<256, BD_GEMM_BN, BD_GEMM_BK>), grid, dim3(GT), 0, stream, g);
+  if (p.wide) hipLaunchKernelGGL(ik_gemm_wide, grid, dim3(WNT), 0, stream, g);
+  else if (p.bm == 256) hipLaunchKernelGGL((ik_gemm<256, BD_GEMM_BN, BD_GEMM_BK>), grid, dim3(GT), 0, stream, g);
   else hipLaunchKernelGGL((ik_gemm<64, 128, 64>), grid, dim3(GT), 0, stream, g);
 
   FinishArgs f{};

@@ -75,6 +75,17 @@ def test_m_above_128_uses_big_tiles():
     run_case(2, 8, 128, 512, [150, 150], [100, 0], 3)
 
 
+def test_wide_tiles_two_m_tiles_one_step_splits():
+    """M = 700 > 512: two 512-row tiles of the wide kernel, the second ragged;
+    d_in = 128 gives four 32-wide steps, split one per workgroup (ring tails)."""
+    run_case(1, 2, 128, 128, [400, 300], [5, 20000], 7)
+
+
+def test_wide_tiles_hd64_long_k():
+    """M = 513 (one row into the second tile), hd = 64, d_in = 2048 (64 steps)."""
+    run_case(2, 4, 64, 2048, [500, 13], [0, 77], 8)
+
+
 def test_no_gains_hd64():
     run_case(2, 3, 64, 640, [40, 9], [7, 1000], 4, gains=False)
 
