@@ -71,7 +71,7 @@ struct AttnArgs {
   float sl2;                      // scale * log2(e)
   uint16_t* out;
   float* lse;
-  float* wo;   // [items + grid][Rp / 32][HD / 32][4][64 lanes][4] partial outputs
+  uint16_t* wo;  // [items + grid][Rp / 32][HD / 32][2][64 lanes][8] partial O / l (bf16)
   float* wml;  // [items + grid][Rp][2]  running max (exp2 domain), normaliser
 };
 
@@ -464,17 +464,24 @@ __global__ __launch_bounds__(64 * NW) BD_ATTN_OCC(NW) void attn_partial(AttnArgs
       }
       // partial result of (item, workgroup): slot item + wg is unique because a
       // later item only starts in a workgroup at or after this one's last.
-      // O^T is stored in accumulator order, so each store is one contiguous
-      // KB: float4 (d, r4, lane) holds dims 32 d + 8 r4 + 4 h .. + 3 of row lr
+      // O / l is stored in bf16 (the normaliser l and the running max stay
+      // fp32) in accumulator order, so each store is one contiguous KB: the
+      // 16 bytes (d, rp, lane) hold dims 32 d + 16 rp + 4 h .. + 3 and
+      // 32 d + 16 rp + 8 + 4 h .. + 3 of row lr
       const size_t slot = size_t(cc.b) * a.n_kv + cc.g + wg;
       const float l = l_run + __shfl_xor(l_run, 32);
-      float* o = a.wo + (slot * (a.Rp / 32) + w) * (32 * HD);
+      const float il = 1.f / l;
+      uint16_t* o = a.wo + (slot * (a.Rp / 32) + w) * (32 * HD);
 #pragma unroll
       for (int d = 0; d < HD / 32; ++d)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-          *reinterpret_cast<float4*>(o + ((d * 4 + r4) * 64 + lane) * 4) =
-              make_float4(acc[d][4 * r4], acc[d][4 * r4 + 1], acc[d][4 * r4 + 2], acc[d][4 * r4 + 3]);
+        for (int rp = 0; rp < 2; ++rp) {
+          const floatx16& c = acc[d];
+          const int r0 = 8 * rp;
+          *reinterpret_cast<uint4*>(o + ((d * 2 + rp) * 64 + lane) * 8) =
+              make_uint4(pk_bf16(c[r0] * il, c[r0 + 1] * il), pk_bf16(c[r0 + 2] * il, c[r0 + 3] * il),
+                         pk_bf16(c[r0 + 4] * il, c[r0 + 5] * il), pk_bf16(c[r0 + 6] * il, c[r0 + 7] * il));
+        }
       if (h == 0) *reinterpret_cast<float2*>(a.wml + (slot * a.Rp + row) * 2) = make_float2(m_run, l);
     }
     cur_next(a, s_pref, cc);
@@ -516,7 +523,8 @@ __global__ __launch_bounds__(MT) void attn_merge(AttnArgs a) {
     float L = 0.f;
     for (int s = 0; s < ns; ++s) L += s_ml[s * 32 + t].y * exp2f(s_ml[s * 32 + t].x - M);
     const float inv = 1.f / L;
-    for (int s = 0; s < ns; ++s) s_f[s * 32 + t] = exp2f(s_ml[s * 32 + t].x - M) * inv;
+    // records hold O_s / l_s: weight l_s 2^(m_s - M) / L
+    for (int s = 0; s < ns; ++s) s_f[s * 32 + t] = s_ml[s * 32 + t].y * exp2f(s_ml[s * 32 + t].x - M) * inv;
     if (t < nr && a.lse) {
       const int row = 32 * wb + t;
       const int i = row / a.group, hh = row - i * a.group;
@@ -524,21 +532,24 @@ __global__ __launch_bounds__(MT) void attn_merge(AttnArgs a) {
     }
   }
   __syncthreads();
-  // float4 p of a record: (d, r4, lane) -> row lane % 32, dims 32 d + 8 r4 + 4 (lane / 32)
-  constexpr int NP = 32 * HD / 4, PPT = NP / MT;
-  const float* base = a.wo + (slot0 * (a.Rp / 32) + wb) * (32 * HD);
-  const size_t rstride = size_t(a.Rp) * HD;  // floats between consecutive records
-  float4 o[PPT];
+  // 16 bytes p of a record: (d, rp, lane) -> row lane % 32, dims
+  // 32 d + 16 rp + 4 (lane / 32) .. + 3 and the same + 8
+  constexpr int NP = 32 * HD / 8, PPT = NP / MT;
+  const uint16_t* base = a.wo + (slot0 * (a.Rp / 32) + wb) * (32 * HD);
+  const size_t rstride = size_t(a.Rp) * HD;  // elements between consecutive records
+  float o[PPT][8];
 #pragma unroll
-  for (int k = 0; k < PPT; ++k) o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k = 0; k < PPT; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[k][e] = 0.f;
   for (int s0 = 0; s0 < ns; s0 += 4) {
-    float4 v[4][PPT];
+    uint4 v[4][PPT];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int s = min(s0 + u, ns - 1);  // a repeated record gets weight 0
 #pragma unroll
       for (int k = 0; k < PPT; ++k)
-        v[u][k] = *reinterpret_cast<const float4*>(base + s * rstride + size_t(t + k * MT) * 4);
+        v[u][k] = *reinterpret_cast<const uint4*>(base + s * rstride + size_t(t + k * MT) * 8);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -546,18 +557,26 @@ __global__ __launch_bounds__(MT) void attn_merge(AttnArgs a) {
       for (int k = 0; k < PPT; ++k) {
         const int rr = (t + k * MT) & 31;
         const float f = s0 + u < ns ? s_f[(s0 + u) * 32 + rr] : 0.f;
-        o[k].x += v[u][k].x * f; o[k].y += v[u][k].y * f; o[k].z += v[u][k].z * f; o[k].w += v[u][k].w * f;
+        const uint32_t wd[4] = {v[u][k].x, v[u][k].y, v[u][k].z, v[u][k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[k][2 * e] += bf16_to_f32(uint16_t(wd[e] & 0xffffu)) * f;
+          o[k][2 * e + 1] += bf16_to_f32(uint16_t(wd[e] >> 16)) * f;
+        }
       }
     }
   }
 #pragma unroll
   for (int k = 0; k < PPT; ++k) {
     const int p = t + k * MT;
-    const int lane = p & 63, dr = p >> 6, d = dr >> 2, r4 = dr & 3;
-    const int rr = lane & 31, dim = 32 * d + 8 * r4 + 4 * (lane >> 5);
-    const uint2 packed = ok ? make_uint2(pack_bf16x2(o[k].x, o[k].y), pack_bf16x2(o[k].z, o[k].w))
-                            : make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
-    *reinterpret_cast<uint2*>(&s_o[rr * (HD + 8) + dim]) = packed;
+    const int lane = p & 63, dr = p >> 6, d = dr >> 1, rp = dr & 1;
+    const int rr = lane & 31, dim = 32 * d + 16 * rp + 4 * (lane >> 5);
+    const uint2 lo4 = ok ? make_uint2(pack_bf16x2(o[k][0], o[k][1]), pack_bf16x2(o[k][2], o[k][3]))
+                         : make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
+    const uint2 hi4 = ok ? make_uint2(pack_bf16x2(o[k][4], o[k][5]), pack_bf16x2(o[k][6], o[k][7]))
+                         : make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
+    *reinterpret_cast<uint2*>(&s_o[rr * (HD + 8) + dim]) = lo4;
+    *reinterpret_cast<uint2*>(&s_o[rr * (HD + 8) + dim + 8]) = hi4;
   }
   __syncthreads();
   // whole rows out: 16 bytes per thread
@@ -616,7 +635,7 @@ size_t attn_ws_bytes(int B, int K, int n_q, int n_kv, int hd, int max_ctx, int w
   if (B <= 0) return 0;
   const size_t Rp = (size_t(K) * (n_q / n_kv) + 31) / 32 * 32;
   const size_t slots = size_t(B) * n_kv + attn_grid(B, n_kv, max_ctx, window);
-  return al(slots * Rp * hd * 4) + al(slots * Rp * 2 * 4);
+  return al(slots * Rp * hd * 2) + al(slots * Rp * 2 * 4);
 }
 
 // one partial-kernel variant: NW = ceil(R / 32) waves of 32 query rows
@@ -658,8 +677,8 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* kb, const uint16_t* vb
   a.out = out; a.lse = lse;
   const size_t Rp = size_t(a.Rp);
   const size_t slots = size_t(B) * n_kv + a.grid;
-  a.wo = static_cast<float*>(ws);
-  a.wml = reinterpret_cast<float*>(static_cast<char*>(ws) + al(slots * Rp * hd * 4));
+  a.wo = static_cast<uint16_t*>(ws);
+  a.wml = reinterpret_cast<float*>(static_cast<char*>(ws) + al(slots * Rp * hd * 2));
   const size_t pref_bytes = size_t(B + 1) * sizeof(int);
   if (hd == 128) run_attn<128>(a, pref_bytes, stream);
   else run_attn<64>(a, pref_bytes, stream);
