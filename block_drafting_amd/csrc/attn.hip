@@ -104,11 +104,24 @@ constexpr int MAXSEG = 64;  // partial records one merge may combine
 // Shared schedule: every workgroup (and the merge) derives the same tile
 // prefix over requests from ctx_len: item i = b * n_kv + g owns global tiles
 // [s_i, s_i + nt_b) with s_i = n_kv * P_b + g * nt_b, P_b = sum_{b' < b} nt_b'.
-// Workgroup w takes global tiles [w * tpw, (w + 1) * tpw).
+// Workgroup w < ge takes global tiles [floor(w T / ge), floor((w + 1) T / ge))
+// (T tiles in all): every workgroup of the grid gets floor or ceil of T / ge.
+// Measured: weighting the shares (e.g. more work for the workgroups placed
+// first on a CU, whose older waves win the issue arbitration) does not help,
+// since a CU's workgroups share its bandwidth.
 struct Sched {
   int total;  // all tiles
-  int tpw;    // tiles per workgroup
+  int ge;     // workgroups with work
 };
+
+__device__ __forceinline__ int sched_start(const Sched& s, int w) {
+  return int((long long)s.total * w / s.ge);
+}
+
+// workgroup holding global tile x: the last w with start(w) <= x
+__device__ __forceinline__ int sched_owner(const Sched& s, int x) {
+  return int((((long long)x + 1) * s.ge - 1) / s.total);
+}
 
 __device__ Sched build_sched(const AttnArgs& a, int* s_pref /* [B + 1] */) {
   const int t = threadIdx.x;
@@ -123,8 +136,8 @@ __device__ Sched build_sched(const AttnArgs& a, int* s_pref /* [B + 1] */) {
   Sched s;
   // values read from LDS are the same in every lane: keep them in scalar registers
   s.total = __builtin_amdgcn_readfirstlane(a.n_kv * s_pref[a.B]);
-  int tpw = (s.total + a.grid - 1) / a.grid;
-  s.tpw = tpw < a.tmin ? a.tmin : tpw;
+  // every share at least tmin tiles (fewer workgroups for small problems)
+  s.ge = (long long)s.total >= (long long)a.grid * a.tmin ? a.grid : (s.total / a.tmin > 1 ? s.total / a.tmin : 1);
   return s;
 }
 
@@ -396,8 +409,9 @@ __global__ __launch_bounds__(64 * NW) BD_ATTN_OCC(NW) void attn_partial(AttnArgs
   const int lr = lane & 31, h = lane >> 5;
   const Sched sc = build_sched(a, s_pref);
   const int wg = blockIdx.x;
-  const int x0 = wg * sc.tpw;
-  const int x_end = min(x0 + sc.tpw, sc.total);
+  if (wg >= sc.ge) return;
+  const int x0 = sched_start(sc, wg);
+  const int x_end = sched_start(sc, wg + 1);
   if (x0 >= x_end) return;
   const bool full_wave = (NI % NW == 0) || w < NI % NW;  // issues LMAX loads per tile
   const uint32_t ring0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring)));
@@ -505,7 +519,7 @@ __global__ __launch_bounds__(MT) void attn_merge(AttnArgs a) {
   const Sched sc = build_sched(a, s_pref);
   const int nt = s_pref[b + 1] - s_pref[b];
   const int item_s = a.n_kv * s_pref[b] + g * nt;
-  const int w0 = item_s / sc.tpw, w1 = (item_s + nt - 1) / sc.tpw;
+  const int w0 = sched_owner(sc, item_s), w1 = sched_owner(sc, item_s + nt - 1);
   const int ns = min(w1 - w0 + 1, MAXSEG);
   int64_t cbase;
   int lo, hi;
@@ -614,19 +628,28 @@ static int attn_grid(int B, int n_kv, int max_ctx, int window) {
   return int(g);
 }
 
-// Workgroups of attn_partial<HD, NW> that fit on the device at once (queried
-// once per variant; falls back to two per CU on 256 CUs).
-template <int HD, int NW>
-static int resident_partial() {
+// Compute units of the current device (queried once; 256 if the query fails).
+static int device_cus() {
   static const int n = [] {
-    int dev = 0, cus = 0, per = 0;
+    int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
+    return cus;
+  }();
+  return n;
+}
+
+// Workgroups of attn_partial<HD, NW> that fit on the device at once (queried
+// once per variant; falls back to two per CU).
+template <int HD, int NW>
+static int resident_partial() {
+  static const int n = [] {
+    int per = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, attn_partial<HD, NW>, 64 * NW, 4096) != hipSuccess ||
         per < 1)
       per = 2;
-    return cus * per;
+    return device_cus() * per;
   }();
   return n;
 }
