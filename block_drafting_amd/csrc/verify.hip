@@ -787,13 +787,39 @@ __global__ __launch_bounds__(VT) void vb_draw_pick(VerifyArgs a) {
   const float u2 = a.uni[(size_t(b) * (a.G + 1) + pos) * 2 + 1];
   const double* cs = a.ws.jsum + size_t(b) * a.nch;
 
+  // chunk sums: one per thread, an exclusive scan in thread order gives each
+  // chunk's running start; the crossing is in the first chunk whose running
+  // end exceeds u' Z (nch <= VT; larger vocabularies walk the sums in order)
   bool use_p = false;
-  double Z = 0.0;
-  for (int c = 0; c < a.nch; ++c) Z += cs[c];
+  double Z = 0.0, base_c = 0.0;
+  int chunk = -1;
+  if (a.nch <= VT) {
+    const double mine = t < a.nch ? cs[t] : 0.0;
+    const double excl = block_exclusive_scan(mine, s_ex);
+    if (t == a.nch - 1) s_mg = excl + mine;  // total, in the scan's order
+    __syncthreads();
+    Z = s_mg;
+    __syncthreads();
+    if (t == 0) s_chunk = INT32_MAX;
+    __syncthreads();
+    if (!(resid && Z == 0.0)) {
+      const double tgt0 = double(u2) * Z;
+      if (t < a.nch && excl + mine > tgt0) atomicMin(&s_chunk, t);
+    }
+    __syncthreads();
+    if (s_chunk != INT32_MAX && s_chunk == t) s_mg = excl;
+    __syncthreads();
+    chunk = s_chunk == INT32_MAX ? -1 : s_chunk;
+    base_c = chunk >= 0 ? s_mg : 0.0;
+    __syncthreads();
+  } else {
+    for (int c = 0; c < a.nch; ++c) Z += cs[c];
+  }
   double tot_p = 0.0;
   if (resid && Z == 0.0) {
     // every residual weight rounded to zero: draw from P instead
     use_p = true;
+    chunk = -1;
     for (int c = 0; c < a.nch; ++c) {
       double s = 0.0;
       for (int j = 0; j < VPT; ++j) {
@@ -805,26 +831,27 @@ __global__ __launch_bounds__(VT) void vb_draw_pick(VerifyArgs a) {
     Z = tot_p;
   }
   const double tgt = double(u2) * Z;
-  // chunk holding the crossing
-  if (t == 0) {
-    double run = 0.0;
-    int chunk = -1;
-    if (!use_p) {
+  if (a.nch > VT && !use_p) {
+    // chunk holding the crossing, walking the sums in order
+    if (t == 0) {
+      double run = 0.0;
+      int ch = -1;
       for (int c = 0; c < a.nch; ++c) {
         run += cs[c];
-        if (run > tgt) { chunk = c; break; }
+        if (run > tgt) { ch = c; break; }
       }
+      s_chunk = ch;
     }
-    s_chunk = chunk;
+    __syncthreads();
+    chunk = s_chunk;
+    base_c = 0.0;
+    if (chunk >= 0)
+      for (int c = 0; c < chunk; ++c) base_c += cs[c];
   }
-  __syncthreads();
-  int chunk = s_chunk;
-  double base = 0.0;
   int pick = INT32_MAX;
   double mg = 0.0;
   if (!use_p && chunk >= 0) {
-    for (int c = 0; c < chunk; ++c) base += cs[c];
-    scan_chunk(a, r, resid, false, chunk, base, tgt, &s_pick, &s_mg, s_ex);
+    scan_chunk(a, r, resid, false, chunk, base_c, tgt, &s_pick, &s_mg, s_ex);
     pick = s_pick;
     mg = s_mg;
     if (pick == INT32_MAX) {
