@@ -134,7 +134,8 @@ __global__ __launch_bounds__(GT) void ik_gemm(GemmArgs g) {
 // ---------------------------------------------------------------- wide-M projection
 // For M > 256: one workgroup computes a 512 x 128 tile over its d_in range, so
 // every weight row is read from HBM once (the rows of H are re-read from L2).
-// Eight waves as 4 (M) x 2 (N), each a 128 x 64 tile of 32x32x16 MFMAs.  Both
+// Eight waves as 4 (M) x 2 (N), each a 128 x 64 tile of 32x32x16 MFMAs (16
+// waves of 64 x 64 or 4 of 128 x 128 measured slower).  Both
 // operands reach LDS straight from global memory (global_load_lds, 16 bytes per
 // lane) through rings of SA (H) and SW (W) stages of BK-wide d_in steps; in
 // iteration k a wave issues its W loads of step k + SW - 1, then its H loads of
@@ -146,9 +147,12 @@ constexpr int WBM = 512, WBN = 128;
 #ifndef BD_GEMM_WIDE_WAVES
 #define BD_GEMM_WIDE_WAVES 8
 #endif
-constexpr int WNW = BD_GEMM_WIDE_WAVES;  // 8: 4 (M) x 2 (N) waves of 128 x 64; 4: 4 x 1 of 128 x 128
+constexpr int WNW = BD_GEMM_WIDE_WAVES;  // 16: 8 (M) x 2 (N) of 64 x 64; 8: 4 x 2 of 128 x 64; 4: 4 x 1 of 128 x 128
 constexpr int WNT = 64 * WNW;
-constexpr int WFN = WNW == 8 ? 2 : 4;    // 32-column blocks per wave
+constexpr int WMW = WNW == 16 ? 8 : 4;   // waves along M
+constexpr int WNWN = WNW / WMW;          // waves along N
+constexpr int WFM = WBM / WMW / 32;      // 32-row blocks per wave
+constexpr int WFN = WBN / WNWN / 32;     // 32-column blocks per wave
 #ifndef BD_GEMM_WIDE_BK
 #define BD_GEMM_WIDE_BK 64
 #endif
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(WNT) void ik_gemm_wide(GemmArgs g) {
   constexpr int P = WBK / 8;
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = WNW == 8 ? w >> 1 : w, wn = WNW == 8 ? w & 1 : 0;
+  const int wm = w / WNWN, wn = w % WNWN;
   const int lr = lane & 31, h = lane >> 5;
   const int tile = blockIdx.x, split = blockIdx.y;
   const int tm = tile / g.tiles_n, tn = tile - tm * g.tiles_n;
@@ -235,9 +239,9 @@ __global__ __launch_bounds__(WNT) void ik_gemm_wide(GemmArgs g) {
   const uint16_t* Abase = g.A + size_t(step0) * WBK;
   const uint16_t* Wbase = g.Bw + size_t(n0) * g.Kd + size_t(step0) * WBK;
 
-  floatx16 acc[4][WFN];
+  floatx16 acc[WFM][WFN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WFM; ++i)
 #pragma unroll
     for (int j = 0; j < WFN; ++j) acc[i][j] = floatx16{};
 
@@ -261,46 +265,60 @@ __global__ __launch_bounds__(WNT) void ik_gemm_wide(GemmArgs g) {
   for (int k = 0; k < ns; ++k) {
     vm_wait_le<(WSA - 2) * (WA_PW + WW_PW)>(wide_younger(k, ns));
     __syncthreads();
-    // refill the stages consumed in iteration k - 1
-    {
-      const int kw = k + WSW - 1, ka = k + WSA - 1;
-      if (kw < ns)
-#pragma unroll
-        for (int q = 0; q < WW_PW; ++q)
-          dma16<true>(Wbase + size_t(kw) * WBK, offW[q], lW + (kw % WSW) * WW_BYTES + (w + WNW * q) * 1024);
-      if (ka < ns)
-#pragma unroll
-        for (int q = 0; q < WA_PW; ++q)
-          dma16<false>(Abase + size_t(ka) * WBK, offA[q], lA + (ka % WSA) * WA_BYTES + (w + WNW * q) * 1024);
-    }
+    // refill the stages consumed in iteration k - 1: this wave's W loads, then
+    // its H loads (in that order), one after every few MFMAs so that their
+    // issue overlaps the MFMAs instead of stalling the SIMD after the barrier
+    const int kw = k + WSW - 1, ka = k + WSA - 1;
+    auto refill = [&](int d) {
+      if (d < WW_PW) {
+        if (kw < ns) dma16<true>(Wbase + size_t(kw) * WBK, offW[d], lW + (kw % WSW) * WW_BYTES + (w + WNW * d) * 1024);
+      } else {
+        const int q = d - WW_PW;
+        if (ka < ns) dma16<false>(Abase + size_t(ka) * WBK, offA[q], lA + (ka % WSA) * WA_BYTES + (w + WNW * q) * 1024);
+      }
+    };
+    constexpr int NDMA = WW_PW + WA_PW;
+    constexpr int NMF = (WBK / 16) * WFM * WFN;
+#ifdef BD_GEMM_DMA_EVERY
+    constexpr int EVERY = BD_GEMM_DMA_EVERY;
+#else
+    constexpr int EVERY = NMF / NDMA > 2 ? 2 : (NMF / NDMA > 0 ? NMF / NDMA : 1);
+#endif
     const uint8_t* As = ringA + (k % WSA) * WA_BYTES;
     const uint8_t* Ws = ringW + (k % WSW) * WW_BYTES;
 #pragma unroll
     for (int kk = 0; kk < WBK / 16; ++kk) {
-      bf16x8 af[4], bfr[WFN];
+      bf16x8 af[WFM], bfr[WFN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(As + wpiece(128 * wm + 32 * i + lr, 2 * kk + h)));
+      for (int i = 0; i < WFM; ++i)
+        af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(As + wpiece(32 * (WFM * wm + i) + lr, 2 * kk + h)));
 #pragma unroll
       for (int j = 0; j < WFN; ++j)
-        bfr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Ws + wpiece(64 * wn + 32 * j + lr, 2 * kk + h)));
+        bfr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Ws + wpiece(32 * (WFN * wn + j) + lr, 2 * kk + h)));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < WFM; ++i)
 #pragma unroll
-        for (int j = 0; j < WFN; ++j) acc[i][j] = mfma32x32x16(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < WFN; ++j) {
+          acc[i][j] = mfma32x32x16(af[i], bfr[j], acc[i][j]);
+          const int m = (kk * WFM + i) * WFN + j;
+          if (m % EVERY == 0 && m / EVERY < NDMA) refill(m / EVERY);
+        }
     }
+    // loads not yet issued (when there are more loads than MFMA slots)
+#pragma unroll
+    for (int d = (NMF + EVERY - 1) / EVERY; d < NDMA; ++d) refill(d);
   }
 
   // C block layout: lane holds column (lane & 31), rows 8 (r / 4) + 4 h + r % 4
   float* P_ = g.P + size_t(split) * g.M * g.N;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WFM; ++i)
 #pragma unroll
     for (int j = 0; j < WFN; ++j) {
-      const int n = n0 + 64 * wn + 32 * j + lr;
+      const int n = n0 + 32 * (WFN * wn + j) + lr;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int m = m0 + 32 * (WFM * wm + i) + 8 * (r >> 2) + 4 * h + (r & 3);
         if (m < g.M) P_[size_t(m) * g.N + n] = acc[i][j][r];
       }
     }
