@@ -191,6 +191,29 @@ __device__ __forceinline__ void consume_chunk(const VerifyArgs& a, const float (
                                               float& mt, int& it, double& st) {
   float cm = -INFINITY;
   int ci = INT32_MAX;
+  if (start + VCH <= a.V) {
+    // full chunk (every chunk of a row but its last): no bounds checks; the
+    // slots increase with the index, so the first strict maximum in slot
+    // order is the lowest index; the sum folds the scale into one FMA
+    int cs = 0;
+    cm = x[0];
+#pragma unroll
+    for (int s = 1; s < VPT; ++s)
+      if (x[s] > cm) { cm = x[s]; cs = s; }
+    ci = start + (VEC ? 4 * ((cs >> 2) * VT + t) + (cs & 3) : cs * VT + t);
+    const bool first = it == INT32_MAX;
+    const float mn = first ? cm : fmaxf(mt, cm);
+    if (a.need_sum && mn != -INFINITY) {
+      if (!first && mn > mt && st != 0.0) st *= exp2(double(mt - mn) * double(a.c2));
+      const float nb = -mn * a.c2;
+      float part = 0.f;
+#pragma unroll
+      for (int s = 0; s < VPT; ++s) part += exp2_hw(fmaf(x[s], a.c2, nb));
+      st += double(part);
+    }
+    if (first || cm > mt) { mt = cm; it = ci; }
+    return;
+  }
 #pragma unroll
   for (int s = 0; s < VPT; ++s) {
     const int e = start + slot_offset<VEC>(s, t);
