@@ -152,7 +152,7 @@ def main():
             ev[1].record(stream)
         for l in range(L):
             bd.draft_block_attn(q[l], kb[l], vb[l], kc[l], vc[l], cache_base, ctx_len, max_ctx, cfg.window,
-                                0.0, out=attn_out[l], workspace=ws_att)
+                                out=attn_out[l], workspace=ws_att)
         if ev is not None:
             ev[2].record(stream)
         bd.verify_block(zt, zd, dtok, uni, cfg.temperature, cfg.top_k, cfg.top_p, tau=tau, out_tokens=out_tok,

@@ -21,6 +21,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libblockdraft.so")
 
 BD_OK, BD_E_NULL, BD_E_SHAPE, BD_E_UNSUPPORTED, BD_E_WORKSPACE, BD_E_LAUNCH = 0, -1, -2, -3, -4, -5
+BD_ATTN_CAUSAL, BD_ATTN_QUERY_WINDOW = 1, 2
 
 EXPORTS = (
     "blockdraft_last_error",
@@ -63,7 +64,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     L.draft_block_attn_workspace_size.restype = c_sz
     L.draft_block_attn_workspace_size.argtypes = [c_i32] * 7
     L.draft_block_attn.restype = ctypes.c_int
-    L.draft_block_attn.argtypes = [c_p] * 7 + [c_i64, c_i32] + [c_i32] * 5 + [c_i32, c_f, c_p, c_p, c_p, c_sz, c_p]
+    L.draft_block_attn.argtypes = [c_p] * 7 + [c_i64, c_i32] + [c_i32] * 5 + [c_i32, c_i32, c_f, c_p, c_p, c_p, c_sz, c_p]
     L.verify_block_workspace_size.restype = c_sz
     L.verify_block_workspace_size.argtypes = [c_i32] * 4
     L.verify_block.restype = ctypes.c_int
@@ -149,9 +150,11 @@ def draft_block_attn_workspace_size(B, K, n_q, n_kv, hd, max_ctx, window) -> int
 
 
 def draft_block_attn(q, k_blk, v_blk, k_cache, v_cache, cache_base, ctx_len, max_ctx: int,
-                     window: int = 0, scale: float = 0.0, out=None, lse=None, workspace=None, stream=None):
+                     window: int = 0, flags: int = 0, scale: float = 0.0, out=None, lse=None, workspace=None,
+                     stream=None):
     """One layer of block attention. q [B,K,n_q,hd]; k_blk/v_blk [B,K,n_kv,hd];
-    k_cache/v_cache [T_cap,n_kv,hd]. Returns (out bf16-bits tensor, lse or None)."""
+    k_cache/v_cache [T_cap,n_kv,hd]. flags: BD_ATTN_CAUSAL | BD_ATTN_QUERY_WINDOW.
+    Returns (out bf16-bits tensor, lse or None)."""
     B, K, n_q, hd = q.shape
     n_kv = k_blk.shape[2]
     T_cap = k_cache.shape[0]
@@ -165,7 +168,7 @@ def draft_block_attn(q, k_blk, v_blk, k_cache, v_cache, cache_base, ctx_len, max
     ws, nb = _workspace(need, workspace, q.device)
     st = load().draft_block_attn(_ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(k_cache), _ptr(v_cache),
                                  _ptr(cache_base), _ptr(ctx_len), T_cap, int(max_ctx), B, K, n_q, n_kv, hd,
-                                 int(window), float(scale), _ptr(out), _ptr(lse), _ptr(ws), nb, _stream(stream))
+                                 int(window), int(flags), float(scale), _ptr(out), _ptr(lse), _ptr(ws), nb, _stream(stream))
     _check(st)
     return out, lse
 

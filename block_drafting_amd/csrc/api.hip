@@ -90,7 +90,7 @@ int draft_block_attn(const uint16_t* q, const uint16_t* k_blk, const uint16_t* v
                      const int64_t* cache_base, const int32_t* ctx_len,
                      int64_t T_cap, int32_t max_ctx,
                      int32_t B, int32_t K, int32_t n_q, int32_t n_kv, int32_t hd,
-                     int32_t window, float scale,
+                     int32_t window, int32_t flags, float scale,
                      uint16_t* out, float* lse,
                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (B < 0 || K < 1 || n_q < 1 || n_kv < 1 || hd < 1 || max_ctx < 0 || window < 0 || T_cap < 0)
@@ -99,6 +99,8 @@ int draft_block_attn(const uint16_t* q, const uint16_t* k_blk, const uint16_t* v
                 B, K, n_q, n_kv, hd, max_ctx, window);
   if (n_q % n_kv) return fail(BD_E_SHAPE, "draft_block_attn: n_q (%d) must be a multiple of n_kv (%d)", n_q, n_kv);
   if (scale != scale) return fail(BD_E_SHAPE, "draft_block_attn: scale is NaN");
+  if (flags & ~(BD_ATTN_CAUSAL | BD_ATTN_QUERY_WINDOW))
+    return fail(BD_E_UNSUPPORTED, "draft_block_attn: unknown flags 0x%x", unsigned(flags));
   if (hd != 64 && hd != 128) return fail(BD_E_UNSUPPORTED, "draft_block_attn: hd must be 64 or 128 (got %d)", hd);
   if (K > 64) return fail(BD_E_UNSUPPORTED, "draft_block_attn: K must be <= 64 (got %d)", K);
   if ((n_q / n_kv) * K > 128)
@@ -115,7 +117,7 @@ int draft_block_attn(const uint16_t* q, const uint16_t* k_blk, const uint16_t* v
     return fail(BD_E_UNSUPPORTED, "draft_block_attn: workspace must be 16-byte aligned");
   if (B == 0) return ok();
   return launched(bd::launch_attn(q, k_blk, v_blk, k_cache, v_cache, cache_base, ctx_len, T_cap, max_ctx, B, K,
-                                  n_q, n_kv, hd, window, scale, out, lse, workspace, stream),
+                                  n_q, n_kv, hd, window, flags, scale, out, lse, workspace, stream),
                   "draft_block_attn");
 }
 

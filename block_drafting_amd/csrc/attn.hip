@@ -65,6 +65,7 @@ struct AttnArgs {
   int B, K, n_q, n_kv, group, R;  // R = K * group query rows per item
   int Rp;                         // R rounded up to whole 32-row wave blocks
   int window, max_ctx;
+  int flags;                      // 1: causal in-block keys, 2: per-query window
   int nbt;                        // tiles of block keys per item, ceil(K / 32)
   int grid;                       // workgroups of the partial kernel
   int tmin;                       // fewest tiles a workgroup takes
@@ -84,7 +85,10 @@ __device__ __forceinline__ bool visible(const AttnArgs& a, int b, int64_t& base,
   base = ((c_int64*)a.cache_base)[b];
   int ctx = ((c_int32*)a.ctx_len)[b];
   if (ctx < 0 || ctx > a.max_ctx || base < 0 || base + ctx > a.T_cap) return false;
-  lo = (a.window > 0 && ctx > a.window) ? ctx - a.window : 0;
+  // the keys of block position 0 under a per-query window, else of every
+  // position: the union over the block either way
+  const int w_lo = (a.flags & 2) ? ctx + 1 - a.window : ctx - a.window;
+  lo = (a.window > 0 && w_lo > 0) ? w_lo : 0;
   hi = ctx;
   return true;
 }
@@ -330,7 +334,7 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int b, int g, int row,
 // rows: scores, online softmax in the exp2 domain, and the P.V accumulation.
 template <int HD>
 __device__ __forceinline__ void tile_math(const AttnArgs& a, const uint8_t* lds, uint32_t kt, uint32_t vt,
-                                          int nvalid, int lane, const bf16x8 (&qf)[HD / 16],
+                                          bool mask, int klo, int khi, int lane, const bf16x8 (&qf)[HD / 16],
                                           floatx16 (&acc)[HD / 32], float& m_run, float& l_run) {
   const int lr = lane & 31, h = lane >> 5;
   floatx16 s = {};
@@ -339,26 +343,31 @@ __device__ __forceinline__ void tile_math(const AttnArgs& a, const uint8_t* lds,
     const u32x4 kf = *reinterpret_cast<const u32x4*>(lds + kt + piece_off<HD>(lr, 2 * ks + h));
     s = mfma32x32x16(__builtin_bit_cast(bf16x8, kf), qf[ks], s);
   }
-  // lane holds keys 8 (r / 4) + 4 h + r % 4 of row lr; masked keys get -inf
+  // lane holds keys 8 (r / 4) + 4 h + r % 4 of row lr; keys outside the
+  // lane's [klo, khi) get -inf (short tiles, and the causal / per-query
+  // window bounds)
   float tmax = -INFINITY;
-  if (nvalid < TK) {
+  if (mask) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = 8 * (r >> 2) + 4 * h + (r & 3);
-      s[r] = key < nvalid ? s[r] : -INFINITY;
+      s[r] = (key >= klo && key < khi) ? s[r] : -INFINITY;
     }
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-  // running maximum in the exp2 domain (scores times scale * log2(e) > 0)
+  // running maximum in the exp2 domain (scores times scale * log2(e) > 0); a
+  // row that has seen no key yet keeps m = -inf, l = 0
   const float m_new = fmaxf(m_run, tmax * a.sl2);
-  const float alpha = exp2_hw(m_run - m_new);
+  const bool none = m_new == -INFINITY;
+  const float alpha = none ? 1.f : exp2_hw(m_run - m_new);
+  const float mu = none ? 0.f : m_new;
   m_run = m_new;
   float psum = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    s[r] = exp2_hw(fmaf(s[r], a.sl2, -m_new));
+    s[r] = exp2_hw(fmaf(s[r], a.sl2, -mu));
     psum += s[r];
   }
   l_run = l_run * alpha + psum;
@@ -462,7 +471,22 @@ __global__ __launch_bounds__(64 * NW) BD_ATTN_OCC(NW) void attn_partial(AttnArgs
     const uint16_t* kp;
     const uint16_t* vp;
     const int nvalid = tile_src<HD>(a, cc, kp, vp);
-    tile_math<HD>(a, ring, stage * 2 * TB, stage * 2 * TB + TB, nvalid, lane, qf, acc, m_run, l_run);
+    // valid keys of this lane's row in the tile: [klo, khi)
+    int klo = 0, khi = nvalid;
+    if (a.flags) {
+      const int i = min(row, a.R - 1) / a.group;  // block position of the row
+      if (cc.ti >= cc.nct) {
+        const int j0 = (cc.ti - cc.nct) * TK;      // first block key of the tile
+        if (a.flags & 1) khi = min(khi, i - j0 + 1);
+        if ((a.flags & 2) && a.window > 0) klo = max(klo, i - a.window + 1 - j0);
+      } else if ((a.flags & 2) && a.window > 0) {
+        // context position p = lo + key: query i needs p >= ctx + i + 1 - W
+        const int ctx = cc.lo + cc.nctx;
+        klo = max(klo, max(0, ctx + i + 1 - a.window) - cc.lo - cc.ti * TK);
+      }
+    }
+    tile_math<HD>(a, ring, stage * 2 * TB, stage * 2 * TB + TB, nvalid < TK || a.flags != 0, klo, khi, lane, qf,
+                  acc, m_run, l_run);
 
     if (x == x_end - 1 || cc.ti == cc.nt - 1) {
       if (x < x_end - 1) {
@@ -484,7 +508,7 @@ __global__ __launch_bounds__(64 * NW) BD_ATTN_OCC(NW) void attn_partial(AttnArgs
       // 32 d + 16 rp + 8 + 4 h .. + 3 of row lr
       const size_t slot = size_t(cc.b) * a.n_kv + cc.g + wg;
       const float l = l_run + __shfl_xor(l_run, 32);
-      const float il = 1.f / l;
+      const float il = l > 0.f ? 1.f / l : 0.f;  // l = 0: no key of this segment was visible
       uint16_t* o = a.wo + (slot * (a.Rp / 32) + w) * (32 * HD);
 #pragma unroll
       for (int d = 0; d < HD / 32; ++d)
@@ -683,14 +707,14 @@ static void run_attn(AttnArgs& a, size_t pref_bytes, hipStream_t stream) {
 hipError_t launch_attn(const uint16_t* q, const uint16_t* kb, const uint16_t* vb, const uint16_t* kc,
                        const uint16_t* vc, const int64_t* cache_base, const int32_t* ctx_len,
                        int64_t T_cap, int max_ctx, int B, int K, int n_q, int n_kv, int hd, int window,
-                       float scale, uint16_t* out, float* lse, void* ws, hipStream_t stream) {
+                       int flags, float scale, uint16_t* out, float* lse, void* ws, hipStream_t stream) {
   if (B == 0) return hipSuccess;
   AttnArgs a{};
   a.q = q; a.kb = kb; a.vb = vb; a.kc = kc; a.vc = vc;
   a.cache_base = cache_base; a.ctx_len = ctx_len; a.T_cap = T_cap;
   a.B = B; a.K = K; a.n_q = n_q; a.n_kv = n_kv; a.group = n_q / n_kv; a.R = K * a.group;
   a.Rp = (a.R + 31) / 32 * 32;
-  a.window = window; a.max_ctx = max_ctx;
+  a.window = window; a.max_ctx = max_ctx; a.flags = flags;
   a.nbt = (K + TK - 1) / TK;
   a.tmin = attn_tmin(max_ctx, window);
   // the workspace holds items + attn_grid() partial slots; the launch may use fewer

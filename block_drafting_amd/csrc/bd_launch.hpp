@@ -17,7 +17,7 @@ size_t attn_ws_bytes(int B, int K, int n_q, int n_kv, int hd, int max_ctx, int w
 hipError_t launch_attn(const uint16_t* q, const uint16_t* kb, const uint16_t* vb, const uint16_t* kc,
                        const uint16_t* vc, const int64_t* cache_base, const int32_t* ctx_len,
                        int64_t T_cap, int max_ctx, int B, int K, int n_q, int n_kv, int hd, int window,
-                       float scale, uint16_t* out, float* lse, void* ws, hipStream_t stream);
+                       int flags, float scale, uint16_t* out, float* lse, void* ws, hipStream_t stream);
 
 size_t verify_ws_bytes(int B, int G, int V, int top_k);
 hipError_t launch_verify(const float* zt, const float* zd, const int* dtok, const float* uni,

@@ -106,10 +106,19 @@ int inject_kv(const uint16_t* h_target, const uint16_t* w_kv, const uint16_t* k_
  * For request b, query head h (KV head g = h / (n_q / n_kv)) and block
  * position i, the keys are the context positions [lo, ctx_len[b]) with
  * lo = max(0, ctx_len[b] - window) (lo = 0 when window == 0), read from slots
- * cache_base[b] + p, followed by the K in-block keys k_blk[b, :, g]; every
- * block position sees all of them (no mask).
+ * cache_base[b] + p, followed by the K in-block keys k_blk[b, :, g]; by
+ * default every block position sees all of them (DFlash: no mask).
  *   out[b, i, h] = softmax(q . keys^T * scale) . values   (bf16)
  *   lse[b, i, h] = log sum exp(q . keys^T * scale)          (fp32, natural log)
+ * flags (bit set):
+ *   BD_ATTN_CAUSAL        DSpine's causal in-block attention ("principle"):
+ *                         block position i sees block keys j <= i only.
+ *   BD_ATTN_QUERY_WINDOW  with window W > 0, a per-query sliding window: the
+ *                         query at block position i (absolute position
+ *                         ctx + i) sees the keys at absolute positions p with
+ *                         ctx + i - p < W, i.e. context [max(0, ctx + i + 1 - W),
+ *                         ctx) and block keys j > i - W; without the flag the
+ *                         window is block-uniform as above.
  *
  * q           device bf16 [B, K, n_q, hd] (already normalised / rotated).
  * k_blk, v_blk device bf16 [B, K, n_kv, hd].
@@ -117,10 +126,14 @@ int inject_kv(const uint16_t* h_target, const uint16_t* w_kv, const uint16_t* k_
  * cache_base  device int64 [B]; ctx_len device int32 [B], 0 <= ctx_len <= max_ctx.
  * max_ctx     host upper bound of ctx_len (sizes the grid).
  * window      0 = whole context, else the sliding-window length.
+ * flags       0 or an or of BD_ATTN_CAUSAL, BD_ATTN_QUERY_WINDOW; other bits
+ *             give BD_E_UNSUPPORTED.
  * scale       <= 0 selects 1/sqrt(hd).
  * out         device bf16 [B, K, n_q, hd]; lse device fp32 [B, K, n_q] or NULL.
  * Supported: hd in {64, 128}; 1 <= K <= 64; (n_q / n_kv) * K <= 128.
  * ------------------------------------------------------------------------ */
+enum { BD_ATTN_CAUSAL = 1, BD_ATTN_QUERY_WINDOW = 2 };
+
 size_t draft_block_attn_workspace_size(int32_t B, int32_t K, int32_t n_q, int32_t n_kv, int32_t hd,
                                        int32_t max_ctx, int32_t window);
 
@@ -129,7 +142,7 @@ int draft_block_attn(const uint16_t* q, const uint16_t* k_blk, const uint16_t* v
                      const int64_t* cache_base, const int32_t* ctx_len,
                      int64_t T_cap, int32_t max_ctx,
                      int32_t B, int32_t K, int32_t n_q, int32_t n_kv, int32_t hd,
-                     int32_t window, float scale,
+                     int32_t window, int32_t flags, float scale,
                      uint16_t* out, float* lse,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 

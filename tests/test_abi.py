@@ -72,10 +72,10 @@ def test_verify_validation_codes(lib):
 
 def _attn(lib, **kw):
     a = dict(q=1 << 20, kb=1 << 20, vb=1 << 20, kc=1 << 20, vc=1 << 20, base=1 << 20, ctx=1 << 20, T_cap=100,
-             max_ctx=50, B=2, K=16, n_q=32, n_kv=8, hd=128, W=0, out=1 << 20, ws=1 << 20, wsb=1 << 30)
+             max_ctx=50, B=2, K=16, n_q=32, n_kv=8, hd=128, W=0, flags=0, out=1 << 20, ws=1 << 20, wsb=1 << 30)
     a.update(kw)
     return lib.draft_block_attn(a["q"], a["kb"], a["vb"], a["kc"], a["vc"], a["base"], a["ctx"], a["T_cap"],
-                                a["max_ctx"], a["B"], a["K"], a["n_q"], a["n_kv"], a["hd"], a["W"], F(0.0),
+                                a["max_ctx"], a["B"], a["K"], a["n_q"], a["n_kv"], a["hd"], a["W"], a["flags"], F(0.0),
                                 a["out"], None, a["ws"], a["wsb"], None)
 
 
@@ -86,6 +86,8 @@ def test_attention_validation_codes(lib):
     assert _attn(lib, K=0) == bd.BD_E_SHAPE
     assert _attn(lib, max_ctx=-1) == bd.BD_E_SHAPE
     assert _attn(lib, hd=96) == bd.BD_E_UNSUPPORTED
+    assert _attn(lib, flags=4) == bd.BD_E_UNSUPPORTED                 # unknown flag bit
+    assert _attn(lib, flags=-1) == bd.BD_E_UNSUPPORTED
     assert _attn(lib, K=65) == bd.BD_E_UNSUPPORTED
     assert _attn(lib, K=64, n_q=24, n_kv=8) == bd.BD_E_UNSUPPORTED    # 3 * 64 rows > 128
     assert _attn(lib, kc=(1 << 20) + 2) == bd.BD_E_UNSUPPORTED

@@ -29,23 +29,23 @@ def case(B, K, n_q, n_kv, hd, ctx, seed, extra_slots=0):
     return q, kb, vb, kc, vc, base, ctx, T
 
 
-def run_gpu(q, kb, vb, kc, vc, base, ctx, window, scale=0.0, max_ctx=None, with_lse=True):
+def run_gpu(q, kb, vb, kc, vc, base, ctx, window, scale=0.0, max_ctx=None, with_lse=True, flags=0):
     import block_drafting_amd as bd
     B, K, n_q, hd = q.shape
     max_ctx = int(ctx.max()) if max_ctx is None else max_ctx
     lse = torch.full((B, K, n_q), -7.0, dtype=torch.float32, device="cuda") if with_lse else None
     out, lse = bd.draft_block_attn(cuda_bits(q), cuda_bits(kb), cuda_bits(vb), cuda_bits(kc), cuda_bits(vc),
                                    torch.from_numpy(base).cuda(), torch.from_numpy(ctx).cuda(), max_ctx,
-                                   window, scale, lse=lse)
+                                   window, flags=flags, scale=scale, lse=lse)
     torch.cuda.synchronize()
     return bits_to_f64(host_bits(out)), (lse.cpu().numpy() if with_lse else None)
 
 
-def check(q, kb, vb, kc, vc, base, ctx, window, scale=0.0, label="", **kw):
-    say(f"attention {label} q={q.shape} ctx={list(ctx)[:6]} window={window}")
-    go, gl = run_gpu(q, kb, vb, kc, vc, base, ctx, window, scale, **kw)
+def check(q, kb, vb, kc, vc, base, ctx, window, scale=0.0, label="", flags=0, **kw):
+    say(f"attention {label} q={q.shape} ctx={list(ctx)[:6]} window={window} flags={flags}")
+    go, gl = run_gpu(q, kb, vb, kc, vc, base, ctx, window, scale, flags=flags, **kw)
     oo, ol = oa.block_attn(bits_to_f64(q), bits_to_f64(kb), bits_to_f64(vb), bits_to_f64(kc), bits_to_f64(vc),
-                           base, ctx, window, scale)
+                           base, ctx, window, scale, causal=bool(flags & 1), per_query_window=bool(flags & 2))
     worst = max(rel_err(go[b], oo[b]) for b in range(q.shape[0]))
     say(f"  worst relative error {worst:.2e}, lse max abs err {np.abs(gl - ol).max():.2e}")
     assert worst <= TOL
@@ -179,3 +179,83 @@ def test_one_long_item_many_partials():
 def test_batch1_4b_shape():
     cfg = wl.CONFIGS["qwen3-4b"]
     check(*case(1, cfg.K, cfg.n_q, cfg.n_kv, cfg.hd, [cfg.ctx_a], 12)[:7], 0, label="qwen3-4b")
+
+
+# ---- causal in-block mask and per-query window
+
+CAUSAL, PER_QUERY = 1, 2
+
+
+def _segment_starts_at_last_tile(ctx, K, n_kv, window=0, per_query=False):
+    """Items (b, g) one of whose partial segments holds only the item's last
+    tile, under the kernel's schedule (equal shares of the flattened tiles,
+    at least 4 tiles and at most 64 workgroups per item, grid at most 2048):
+    there a causal block gives rows that see no key of the segment."""
+    TK = 32
+    vis = window if (window > 0 and max(ctx) > window) else max(ctx)
+    nt_max = (vis + TK - 1) // TK + 2
+    tmin = max(4, (nt_max + 61) // 62)
+    grid = max(1, min(2048, -(-len(ctx) * n_kv * nt_max // tmin)))
+    nts = []
+    for c in ctx:
+        w_lo = c + 1 - window if per_query else c - window
+        lo = w_lo if (window > 0 and w_lo > 0) else 0
+        nts.append((c - lo + TK - 1) // TK + (K + TK - 1) // TK)
+    pref = np.concatenate([[0], np.cumsum(nts)])
+    total = n_kv * int(pref[-1])
+    ge = grid if total >= grid * tmin else max(1, total // tmin)
+    starts = {total * w // ge for w in range(ge)}
+    return [(b, g) for b, nt in enumerate(nts) for g in range(n_kv)
+            if nt > 1 and n_kv * pref[b] + g * nt + nt - 1 in starts]
+
+
+@pytest.mark.parametrize("flags", [CAUSAL, PER_QUERY, CAUSAL | PER_QUERY])
+def test_flags_ragged_contexts(flags):
+    check(*case(6, 16, 32, 8, 128, [0, 1, 63, 64, 1000, 130], 31)[:7], 100, label="ragged", flags=flags)
+
+
+def test_causal_no_window():
+    check(*case(4, 16, 32, 8, 128, [0, 5, 700, 33], 32)[:7], 0, label="causal", flags=CAUSAL)
+
+
+def test_causal_two_block_tiles_hd64():
+    # K = 64: the block spans two key tiles, rows of position < 32 see none of the second
+    check(*case(3, 64, 4, 2, 64, [700, 0, 129], 33)[:7], 0, label="causal K64", flags=CAUSAL)
+
+
+def test_per_query_window_shorter_than_block():
+    # W = 10 < K: block keys j <= i - 10 drop out as well
+    check(*case(4, 16, 32, 8, 128, [0, 3, 9, 2000], 34)[:7], 10, label="W<K", flags=PER_QUERY)
+    check(*case(4, 16, 32, 8, 128, [0, 3, 9, 2000], 35)[:7], 10, label="W<K causal", flags=CAUSAL | PER_QUERY)
+
+
+def test_flags_group5_padding_rows():
+    check(*case(2, 16, 40, 8, 128, [3000, 17], 36)[:7], 1024, label="group5", flags=CAUSAL | PER_QUERY)
+
+
+def test_flags_causal_window_of_one():
+    # W = 1 and causal: every query sees only its own key, so out = its value
+    q, kb, vb, kc, vc, base, ctx, _ = case(2, 16, 32, 8, 128, [50, 0], 37)
+    go, _ = run_gpu(q, kb, vb, kc, vc, base, ctx, 1, flags=CAUSAL | PER_QUERY)
+    vbf = bits_to_f64(vb)
+    for b in range(2):
+        for h in range(32):
+            np.testing.assert_array_equal(go[b, :, h], vbf[b, :, h // 4])
+    check(q, kb, vb, kc, vc, base, ctx, 1, label="W=1 causal", flags=CAUSAL | PER_QUERY)
+    check(q, kb, vb, kc, vc, base, ctx, 1, label="W=1", flags=PER_QUERY)
+
+
+def test_causal_segments_that_see_no_key():
+    # many partial segments; some hold only an item's last block tile, which
+    # the rows of positions below 32 do not see: their records carry l = 0
+    args = case(8, 64, 2, 1, 64, [2551, 1910, 1533, 809, 923, 122, 225, 49], 38)[:7]
+    assert _segment_starts_at_last_tile(list(args[6]), 64, 1)
+    check(*args, 0, label="empty segments", flags=CAUSAL)
+
+
+def test_flags_rejects_unknown_bits():
+    import block_drafting_amd as bd
+    q, kb, vb, kc, vc, base, ctx, _ = case(1, 16, 32, 8, 128, [5], 39)
+    with pytest.raises(RuntimeError, match="flags"):
+        run_gpu(q, kb, vb, kc, vc, base, ctx, 0, flags=4)
+    assert bd.BD_ATTN_CAUSAL == CAUSAL and bd.BD_ATTN_QUERY_WINDOW == PER_QUERY

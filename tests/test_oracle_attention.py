@@ -123,3 +123,104 @@ def test_default_scale_is_inverse_sqrt_hd():
     a = oa.block_attn(q, kb, vb, kc, vc, base, ctx, scale=0.0)
     b = oa.block_attn(q, kb, vb, kc, vc, base, ctx, scale=1 / 4.0)
     np.testing.assert_array_equal(a[0], b[0])
+
+
+# ---- causal in-block mask and per-query window (DSpine article, "principle";
+# "what these weights are" for the window)
+
+def _attn_abs_positions(q, kb, vb, kc, vc, base, ctx, window, causal, per_query, b, h, i, scale):
+    """One query by brute force over absolute positions: the context token p
+    sits at position p, block key j at ctx + j, the query at ctx + i."""
+    n_q, n_kv = q.shape[2], kb.shape[2]
+    g = h // (n_q // n_kv)
+    c = int(ctx[b])
+    keys, vals = [], []
+    for p in range(c + q.shape[1]):
+        is_block = p >= c
+        if causal and is_block and p > c + i:
+            continue
+        if window > 0:
+            if per_query and (c + i) - p >= window:
+                continue
+            if not per_query and not is_block and p < c - window:
+                continue
+        if is_block:
+            keys.append(kb[b, p - c, g]); vals.append(vb[b, p - c, g])
+        else:
+            keys.append(kc[base[b] + p, g]); vals.append(vc[base[b] + p, g])
+    s = np.array(keys) @ q[b, i, h] * scale
+    return round_to_bf16(special.softmax(s) @ np.array(vals)), special.logsumexp(s)
+
+
+@pytest.mark.parametrize("window,causal,per_query", [(0, True, False), (5, True, False), (5, False, True),
+                                                     (3, True, True), (30, False, True), (2, False, True)])
+def test_masks_match_absolute_position_brute_force(window, causal, per_query):
+    q, kb, vb, kc, vc, base, ctx = make(B=3, K=6, ctx=(0, 4, 13), seed=21)
+    out, lse = oa.block_attn(q, kb, vb, kc, vc, base, ctx, window, causal=causal, per_query_window=per_query)
+    for b in range(3):
+        for h in range(4):
+            for i in range(6):
+                o, l = _attn_abs_positions(q, kb, vb, kc, vc, base, ctx, window, causal, per_query, b, h, i,
+                                           1 / 4.0)
+                np.testing.assert_allclose(out[b, i, h], o, rtol=0, atol=1e-12)
+                assert abs(lse[b, i, h] - l) < 1e-10
+
+
+def test_causal_with_one_position_equals_bidirectional():
+    q, kb, vb, kc, vc, base, ctx = make(K=1, seed=22)
+    a = oa.block_attn(q, kb, vb, kc, vc, base, ctx)
+    c = oa.block_attn(q, kb, vb, kc, vc, base, ctx, causal=True)
+    np.testing.assert_array_equal(a[0], c[0])
+    np.testing.assert_array_equal(a[1], c[1])
+
+
+def test_causal_first_position_without_context_returns_its_own_value():
+    q, kb, vb, kc, vc, base, ctx = make(ctx=(0, 0), seed=23)
+    out, lse = oa.block_attn(q, kb, vb, kc, vc, base, ctx, causal=True)
+    for b in range(2):
+        for h in range(4):
+            g = h // 2
+            np.testing.assert_array_equal(out[b, 0, h], round_to_bf16(vb[b, 0, g]))
+            assert abs(lse[b, 0, h] - q[b, 0, h] @ kb[b, 0, g] / 4.0) < 1e-12
+
+
+def test_causal_position_t_equals_bidirectional_block_cut_after_t():
+    q, kb, vb, kc, vc, base, ctx = make(K=5, seed=24)
+    out, lse = oa.block_attn(q, kb, vb, kc, vc, base, ctx, window=6, causal=True)
+    for t in range(5):
+        o2, l2 = oa.block_attn(q[:, :t + 1], kb[:, :t + 1], vb[:, :t + 1], kc, vc, base, ctx, window=6)
+        np.testing.assert_allclose(out[:, t], o2[:, t], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[:, t], l2[:, t], rtol=0, atol=1e-12)
+
+
+def test_per_query_window_row_equals_block_uniform_window_shrunk_by_position():
+    # query i sees context [ctx + i + 1 - W, ctx): the block-uniform window W - i - 1
+    q, kb, vb, kc, vc, base, ctx = make(K=4, ctx=(9, 12), seed=25)
+    W = 8
+    out, lse = oa.block_attn(q, kb, vb, kc, vc, base, ctx, W, per_query_window=True)
+    for i in range(4):
+        o2, l2 = oa.block_attn(q, kb, vb, kc, vc, base, ctx, W - i - 1)
+        np.testing.assert_allclose(out[:, i], o2[:, i], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[:, i], l2[:, i], rtol=0, atol=1e-12)
+
+
+def test_per_query_window_wider_than_everything_is_no_window():
+    q, kb, vb, kc, vc, base, ctx = make(K=4, seed=26)
+    a = oa.block_attn(q, kb, vb, kc, vc, base, ctx, 0, causal=True)
+    c = oa.block_attn(q, kb, vb, kc, vc, base, ctx, int(ctx.max()) + 4, causal=True, per_query_window=True)
+    np.testing.assert_allclose(a[0], c[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(a[1], c[1], rtol=0, atol=1e-12)
+
+
+def test_causal_sliding_window_without_context_is_banded_attention():
+    # ctx = 0: block position i sees block keys max(0, i - W + 1) .. i (a band)
+    K, W = 7, 3
+    q, kb, vb, kc, vc, base, ctx = make(B=1, K=K, n_q=2, n_kv=2, ctx=(0,), seed=27)
+    out, lse = oa.block_attn(q, kb, vb, kc, vc, base, ctx, W, causal=True, per_query_window=True)
+    band = np.tril(np.ones((K, K), bool)) & ~np.tril(np.ones((K, K), bool), -W)
+    for h in range(2):
+        s = q[0, :, h] @ kb[0, :, h].T / 4.0
+        s = np.where(band, s, -np.inf)
+        np.testing.assert_allclose(out[0, :, h], round_to_bf16(special.softmax(s, axis=1) @ vb[0, :, h]),
+                                   rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[0, :, h], special.logsumexp(s, axis=1), rtol=0, atol=1e-12)
