@@ -12,12 +12,14 @@
 // Pass 1 (vb_stats) streams every logits row once, split in chunks of 8192:
 // per chunk the maximum and its lowest index, the sum of exp((z - max) / T)
 // (fp32 lanes, fp64 across lanes) and, under top-k, the chunk's k best
-// (value desc, index asc).  Pass 2 (vb_decide, one workgroup per request)
-// merges the chunks of its rows, applies the filters, runs the accept chain
-// and, where the draw needs only the filtered support, draws the token.
-// Without top-k the draw needs the whole row pair once more: vb_draw_sums
-// gives per-chunk sums of the draw weights and vb_draw_pick scans the one
-// chunk that holds the crossing.
+// (value desc, index asc).  Greedy and top-k: pass 2 (vb_decide, one
+// workgroup per request) merges the chunks of its rows, applies the filters,
+// runs the accept chain and draws over the filtered support.  Full-vocabulary
+// sampling needs the chosen row pair once more: there pass 2
+// (vb_decide_sums, one workgroup per (chunk, request)) merges the request's
+// rows and runs the accept chain in every workgroup, then sums the draw
+// weights of its chunk, and vb_draw_pick scans the one chunk that holds the
+// crossing.
 #include "bd_common.hpp"
 #include "bd_launch.hpp"
 
@@ -29,6 +31,12 @@ constexpr int VT = 256;        // threads of a stats / draw workgroup
 constexpr int VCH = 8192;      // logits per chunk (32 per thread)
 constexpr int VPT = VCH / VT;  // 32
 constexpr int TOPK_MAX = 64;
+// Vector rows: a chunk's draw-weight sum is also kept per run of SUBLEN
+// consecutive logits (run k = 4 j + w: the slot group j of wave w), so the
+// draw can find the run holding the crossing without re-reading the chunk.
+constexpr int NSUB = VPT / 4 * (VT / 64);  // 32
+constexpr int SUBLEN = VCH / NSUB;         // 256
+constexpr int PICK_FAST_NCH = 64;          // chunks whose run sums the draw keeps in LDS
 // Target workgroups of the streaming statistics pass and its register budget
 // (waves per SIMD) so that they are all resident at once.
 #ifndef BD_STATS_GRID
@@ -41,7 +49,14 @@ constexpr int TOPK_MAX = 64;
 constexpr int STATS_GRID = BD_STATS_GRID;
 constexpr int CAND_PER_WAVE = 64;
 
-enum { JOB_NONE = 0, JOB_RESID = 1, JOB_BONUS = 2 };
+enum { JOB_RESID = 1, JOB_BONUS = 2 };
+
+// The full-vocabulary draw of one request: the position, the kind, the
+// uniform, and the row maxima and 1 / sums of the row pair (one load).
+struct alignas(32) DrawJob {
+  int pos, kind;
+  float u2, mt, st, md, sd, pad;
+};
 
 // -------------------------------------------------------------------------
 // element access: thread t holds, for j = 0..7 and c = 0..3 (vector rows) the
@@ -134,8 +149,9 @@ struct VerifyWs {
   int* rkn;      // [rows]           kept count after filters
   int* rki;      // [rows][TOPK_MAX] kept indices (value desc, index asc)
   double* rkp;   // [rows][TOPK_MAX] kept probabilities
-  int* job;      // [B][2]           (position, kind)
+  DrawJob* job;  // [B]             the draw each request needs
   double* jsum;  // [B][nch]
+  double* jsub;  // [B][nch][NSUB]  vector rows: sums over runs of SUBLEN logits
 };
 
 struct VerifyArgs {
@@ -451,30 +467,54 @@ __device__ __forceinline__ float draw_weight(const DrawRow& r, float c2, float z
 // -------------------------------------------------------------------------
 // Pass 2: one workgroup per request.
 // -------------------------------------------------------------------------
-__device__ void merge_row(const VerifyArgs& a, int row, int lane) {
-  // records of this row: slots row + w for the workgroups w that covered it
+// The row's merged maximum, lowest-index argmax and (when asked) sum of
+// exp((z - max) / T) from its records: slots row + w for the workgroups w of
+// the statistics pass that covered it.  The records of the first 64 are kept
+// in registers between the two reductions.
+__device__ __forceinline__ int row_records(const VerifyArgs& a, int row, size_t& slot0) {
   const long long w0 = (long long)row * a.nch / a.cpw;
   const long long w1 = ((long long)row * a.nch + a.nch - 1) / a.cpw;
-  const int nrec = int(w1 - w0 + 1);
-  const size_t slot0 = size_t(row) + size_t(w0);
-  float v = -INFINITY;
-  int i = INT32_MAX;
-  for (int c = lane; c < nrec; c += 64) {
-    size_t rc = slot0 + c;
-    float cv = a.ws.cmax[rc];
-    int ci = a.ws.carg[rc];
+  slot0 = size_t(row) + size_t(w0);
+  return int(w1 - w0 + 1);
+}
+
+__device__ __forceinline__ void merge_stats(const VerifyArgs& a, int row, int lane, float& v, int& i, double& S) {
+  size_t slot0;
+  const int nrec = row_records(a, row, slot0);
+  v = -INFINITY;
+  i = INT32_MAX;
+  float cm0 = -INFINITY;
+  double cs0 = 0.0;
+  if (lane < nrec) {
+    cm0 = a.ws.cmax[slot0 + lane];
+    i = a.ws.carg[slot0 + lane];
+    if (a.need_sum) cs0 = a.ws.csum[slot0 + lane];
+    v = cm0;
+  }
+  for (int c = lane + 64; c < nrec; c += 64) {
+    const size_t rc = slot0 + c;
+    const float cv = a.ws.cmax[rc];
+    const int ci = a.ws.carg[rc];
     if (better(cv, ci, v, i)) { v = cv; i = ci; }
   }
   wave_argmax(v, i);
-  double S = 0.0;
+  S = 0.0;
   if (a.need_sum && v != -INFINITY) {
-    for (int c = lane; c < nrec; c += 64) {
-      size_t rc = slot0 + c;
-      float cm = a.ws.cmax[rc];
+    if (cm0 != -INFINITY) S = cs0 * exp2(double(cm0 - v) * double(a.c2));
+    for (int c = lane + 64; c < nrec; c += 64) {
+      const size_t rc = slot0 + c;
+      const float cm = a.ws.cmax[rc];
       if (cm != -INFINITY) S += a.ws.csum[rc] * exp2(double(cm - v) * double(a.c2));
     }
     S = wave_sum(S);
   }
+}
+
+__device__ void merge_row(const VerifyArgs& a, int row, int lane) {
+  float v;
+  int i;
+  double S;
+  merge_stats(a, row, lane, v, i, S);
   if (lane == 0) {
     a.ws.rmax[row] = v;
     a.ws.rarg[row] = i;
@@ -482,6 +522,8 @@ __device__ void merge_row(const VerifyArgs& a, int row, int lane) {
   }
   if (a.topk > 0) {
     // k best of the chunk lists, then softmax over them and the top-p cut
+    size_t slot0;
+    const int nrec = row_records(a, row, slot0);
     const int k = a.topk;
     const int ncand = nrec * k;
     const float* cv = a.ws.ctv + slot0 * k;
@@ -572,16 +614,8 @@ __global__ __launch_bounds__(DT) void vb_decide(VerifyArgs a) {
       const int drow = a.n_trows + b * G + lane;
       double p = 0.0, q = 0.0;
       if (d >= 0 && d < a.V) {
-        if (a.topk > 0) {
-          p = kept_prob(a, trow, d);
-          q = kept_prob(a, drow, d);
-        } else {
-          float zt = a.zt[size_t(trow) * a.V + d];
-          float zd = a.zd[size_t(b * G + lane) * a.V + d];
-          double Tt = double(a.T);
-          p = exp(double(zt) / Tt - double(a.ws.rmax[trow]) / Tt) / a.ws.rsum[trow];
-          q = exp(double(zd) / Tt - double(a.ws.rmax[drow]) / Tt) / a.ws.rsum[drow];
-        }
+        p = kept_prob(a, trow, d);
+        q = kept_prob(a, drow, d);
       }
       float p32 = float(p), q32 = float(q);
       ratio = p32 / q32;
@@ -605,8 +639,10 @@ __global__ __launch_bounds__(DT) void vb_decide(VerifyArgs a) {
     }
     return;
   }
+  // top-k: draw over the kept support (full-vocabulary sampling runs
+  // vb_decide_sums instead of this kernel)
   const float u2 = a.uni[(size_t(b) * (G + 1) + tau) * 2 + 1];
-  if (a.topk > 0) {
+  {
     if (lane != 0) return;
     // draw over P's kept support in vocabulary order
     const int n = a.ws.rkn[trow];
@@ -651,53 +687,182 @@ __global__ __launch_bounds__(DT) void vb_decide(VerifyArgs a) {
     }
     a.out[b * (G + 1) + tau] = idx[pick];
     if (a.margin) a.margin[b] = float(mg);
-    return;
-  }
-  if (lane == 0) {
-    a.ws.job[2 * b] = tau;
-    a.ws.job[2 * b + 1] = (tau < G) ? JOB_RESID : JOB_BONUS;
   }
 }
 
-__device__ __forceinline__ DrawRow draw_row(const VerifyArgs& a, int b, int pos, bool resid) {
+__device__ __forceinline__ DrawRow job_row(const VerifyArgs& a, int b, const DrawJob& j) {
   DrawRow r;
-  const int trow = b * (a.G + 1) + pos;
-  r.zt = a.zt + size_t(trow) * a.V;
-  r.mt = a.ws.rmax[trow];
-  r.st = float(1.0 / a.ws.rsum[trow]);
-  r.zd = nullptr;
-  r.md = 0.f;
-  r.sd = 0.f;
-  if (resid) {
-    const int drow = a.n_trows + b * a.G + pos;
-    r.zd = a.zd + size_t(b * a.G + pos) * a.V;
-    r.md = a.ws.rmax[drow];
-    r.sd = float(1.0 / a.ws.rsum[drow]);
-  }
+  r.zt = a.zt + size_t(b * (a.G + 1) + j.pos) * a.V;
+  r.zd = j.kind == JOB_RESID ? a.zd + size_t(b * a.G + j.pos) * a.V : nullptr;
+  r.mt = j.mt;
+  r.st = j.st;
+  r.md = j.md;
+  r.sd = j.sd;
   return r;
 }
 
-// per-chunk sums of the draw weights (full-vocabulary draws only)
+// Eight sums over the wave at once: lane 8 j + i (i < 8) ends with the sum of
+// v[j] over all 64 lanes.  Three halving exchanges (each lane keeps the half
+// of its values its half of the wave owns) and three plain butterfly steps:
+// 14 exchanges of doubles instead of 48 for eight separate reductions.
+__device__ __forceinline__ double wave_sum8(const double (&v)[8]) {
+  const int lane = threadIdx.x & 63;
+  const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8;
+  double k4[4], k2[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) k4[i] = (h5 ? v[i + 4] : v[i]) + __shfl_xor(h5 ? v[i] : v[i + 4], 32);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) k2[i] = (h4 ? k4[i + 2] : k4[i]) + __shfl_xor(h4 ? k4[i] : k4[i + 2], 16);
+  double k1 = (h3 ? k2[1] : k2[0]) + __shfl_xor(h3 ? k2[0] : k2[1], 8);
+  k1 += __shfl_xor(k1, 4);
+  k1 += __shfl_xor(k1, 2);
+  k1 += __shfl_xor(k1, 1);
+  return k1;
+}
+
+// Full-vocabulary sampling, pass 2: workgroup (c, b) merges request b's
+// 2G + 1 rows, runs the accept chain (every workgroup of the request reaches
+// the same decision from the same records), and sums the draw weights of
+// chunk c of the row pair at the first rejection (or of the extra target
+// row).  Workgroup (0, b) also writes tau, the accepted tokens, the ratios,
+// the row statistics and the draw job.  The draft logits at the drafted
+// tokens are loaded before the merge, which they do not depend on.
 template <bool VEC>
-__global__ __launch_bounds__(VT) void vb_draw_sums(VerifyArgs a) {
+__global__ __launch_bounds__(VT) void vb_decide_sums(VerifyArgs a) {
+  __shared__ float s_m[2 * 64 + 1];
+  __shared__ int s_i[2 * 64 + 1];
+  __shared__ double s_s[2 * 64 + 1];
   __shared__ double s_d[4];
-  const int b = blockIdx.y, c = blockIdx.x, t = threadIdx.x;
-  const int kind = a.ws.job[2 * b + 1];
-  if (kind == JOB_NONE) return;
-  const bool resid = kind == JOB_RESID;
-  const DrawRow r = draw_row(a, b, a.ws.job[2 * b], resid);
+  __shared__ int s_tau;
+  const int b = blockIdx.y, c = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int G = a.G;
+  int d = -1;
+  float zt_d = 0.f, zd_d = 0.f, u = 0.f;
+  if (w == 0 && lane < G) {
+    d = a.dtok[b * G + lane];
+    u = a.uni[(size_t(b) * (G + 1) + lane) * 2];
+    if (d >= 0 && d < a.V) {
+      zt_d = a.zt[size_t(b * (G + 1) + lane) * a.V + d];
+      zd_d = a.zd[size_t(b * G + lane) * a.V + d];
+    }
+  }
+  // rows j = 0..G: target rows, j = G + 1..2G: draft rows; thread j merges
+  // row j's few records in record order, so all rows' loads are in flight
+  // together
+  const int n_my = 2 * G + 1;
+  if (t < n_my) {
+    const int row = t <= G ? b * (G + 1) + t : a.n_trows + b * G + (t - G - 1);
+    size_t slot0;
+    const int nrec = row_records(a, row, slot0);
+    float v = -INFINITY;
+    int i = INT32_MAX;
+    for (int r = 0; r < nrec; ++r) {
+      const float cv = a.ws.cmax[slot0 + r];
+      const int ci = a.ws.carg[slot0 + r];
+      if (better(cv, ci, v, i)) { v = cv; i = ci; }
+    }
+    double S = 0.0;
+    if (v != -INFINITY)
+      for (int r = 0; r < nrec; ++r) {
+        const float cm = a.ws.cmax[slot0 + r];
+        if (cm != -INFINITY) S += a.ws.csum[slot0 + r] * exp2(double(cm - v) * double(a.c2));
+      }
+    s_m[t] = v;
+    s_i[t] = i;
+    s_s[t] = S;
+  }
+  __syncthreads();
+  if (w == 0) {
+    bool acc = false;
+    float ratio = 0.f;
+    if (lane < G) {
+      double p = 0.0, q = 0.0;
+      if (d >= 0 && d < a.V) {
+        const double Tt = double(a.T);
+        p = exp(double(zt_d) / Tt - double(s_m[lane]) / Tt) / s_s[lane];
+        q = exp(double(zd_d) / Tt - double(s_m[G + 1 + lane]) / Tt) / s_s[G + 1 + lane];
+      }
+      const float p32 = float(p), q32 = float(q);
+      ratio = p32 / q32;
+      acc = u < ratio;
+    }
+    const unsigned long long rej = __ballot(lane < G && !acc);
+    const int tau = rej ? __ffsll((long long)rej) - 1 : G;
+    if (lane == 0) s_tau = tau;
+    if (c == 0) {
+      if (lane < G && a.ratio) a.ratio[b * G + lane] = ratio;
+      if (lane == 0) a.tau[b] = tau;
+      for (int i = lane; i <= G; i += 64) {
+        if (i < tau) a.out[b * (G + 1) + i] = a.dtok[b * G + i];
+        else if (i > tau) a.out[b * (G + 1) + i] = -1;
+      }
+      for (int j = lane; j < n_my; j += 64) {
+        const int row = j <= G ? b * (G + 1) + j : a.n_trows + b * G + (j - G - 1);
+        a.ws.rmax[row] = s_m[j];
+        a.ws.rarg[row] = s_i[j];
+        a.ws.rsum[row] = s_s[j];
+      }
+      if (lane == 0) {
+        DrawJob jb;
+        jb.pos = tau;
+        jb.kind = tau < G ? JOB_RESID : JOB_BONUS;
+        jb.u2 = a.uni[(size_t(b) * (G + 1) + tau) * 2 + 1];
+        jb.mt = s_m[tau];
+        jb.st = float(1.0 / s_s[tau]);
+        jb.md = tau < G ? s_m[G + 1 + tau] : 0.f;
+        jb.sd = tau < G ? float(1.0 / s_s[G + 1 + tau]) : 0.f;
+        jb.pad = 0.f;
+        a.ws.job[b] = jb;
+      }
+    }
+  }
+  __syncthreads();
+  const int tau = s_tau;
+  const bool resid = tau < G;
+  DrawRow r;
+  r.zt = a.zt + size_t(b * (G + 1) + tau) * a.V;
+  r.zd = resid ? a.zd + size_t(b * G + tau) * a.V : nullptr;
+  r.mt = s_m[tau];
+  r.st = float(1.0 / s_s[tau]);
+  r.md = resid ? s_m[G + 1 + tau] : 0.f;
+  r.sd = resid ? float(1.0 / s_s[G + 1 + tau]) : 0.f;
   const int start = c * VCH;
   float xt[VPT], xd[VPT];
   load_chunk<VEC>(r.zt, start, a.V, t, xt);
   if (resid) load_chunk<VEC>(r.zd, start, a.V, t, xd);
-  double s = 0.0;
+  if constexpr (VEC) {
+    // run sums (wave w, slot group j: logits 1024 j + 256 w .. + 255 of the
+    // chunk), then the chunk sum as their sum in run order
+    __shared__ double s_sub[NSUB];
+    double ls[VPT / 4];
 #pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    const int e = start + slot_offset<VEC>(j, t);
-    if (e < a.V) s += double(draw_weight(r, a.c2, xt[j], resid ? xd[j] : 0.f, resid));
+    for (int j = 0; j < VPT / 4; ++j) {
+      ls[j] = 0.0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = start + slot_offset<true>(4 * j + q, t);
+        if (e < a.V) ls[j] += double(draw_weight(r, a.c2, xt[4 * j + q], resid ? xd[4 * j + q] : 0.f, resid));
+      }
+    }
+    const double sj = wave_sum8(ls);  // lane 8 j: the wave's sum of slot group j
+    if ((lane & 7) == 0) s_sub[4 * (lane >> 3) + w] = sj;
+    __syncthreads();
+    if (t < NSUB) a.ws.jsub[(size_t(b) * a.nch + c) * NSUB + t] = s_sub[t];
+    if (t == 0) {
+      double sum = 0.0;
+      for (int k = 0; k < NSUB; ++k) sum += s_sub[k];
+      a.ws.jsum[size_t(b) * a.nch + c] = sum;
+    }
+  } else {
+    double sum = 0.0;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int e = start + slot_offset<VEC>(j, t);
+      if (e < a.V) sum += double(draw_weight(r, a.c2, xt[j], resid ? xd[j] : 0.f, resid));
+    }
+    sum = block_sum_f64(sum, s_d);
+    if (t == 0) a.ws.jsum[size_t(b) * a.nch + c] = sum;
   }
-  s = block_sum_f64(s, s_d);
-  if (t == 0) a.ws.jsum[size_t(b) * a.nch + c] = s;
 }
 
 // The thread's 32 consecutive logits of a row, starting at element e0.
@@ -733,11 +898,13 @@ __device__ __forceinline__ double block_exclusive_scan(double v, double* s_w /* 
 
 // Scan one chunk for the first running sum above tgt.  Returns the vocabulary
 // index (or INT32_MAX) and the margin through the shared outputs.
-__device__ void scan_chunk(const VerifyArgs& a, const DrawRow& r, bool resid, bool use_p, int c,
-                           double base, double tgt, int* s_pick, double* s_mg, double* s_w) {
+template <bool VEC, bool USE_P>
+__device__ __forceinline__ void scan_chunk(const VerifyArgs& a, const DrawRow& r, bool resid, int c, double base,
+                                           double tgt, int* s_pick, double* s_mg, double* s_w) {
+  constexpr bool use_p = USE_P;
   const int t = threadIdx.x;
   const int start = c * VCH + t * VPT;
-  const bool vec = (a.V & 3) == 0;
+  const bool vec = VEC;
   float xt[VPT], xd[VPT];
   load_run(r.zt, start, a.V, vec, xt);
   if (resid && !use_p) load_run(r.zd, start, a.V, vec, xd);
@@ -795,67 +962,51 @@ __device__ int last_positive(const VerifyArgs& a, const DrawRow& r, bool resid, 
   return *s_pick;
 }
 
-__global__ __launch_bounds__(VT) void vb_draw_pick(VerifyArgs a) {
-  __shared__ double s_ex[4];
-  __shared__ double s_d[4];
-  __shared__ int s_pick;
-  __shared__ double s_mg;
-  __shared__ int s_chunk;
-  const int b = blockIdx.x, t = threadIdx.x;
-  const int kind = a.ws.job[2 * b + 1];
-  if (kind == JOB_NONE) return;
-  const int pos = a.ws.job[2 * b];
-  bool resid = kind == JOB_RESID;
-  const DrawRow r = draw_row(a, b, pos, resid);
-  const float u2 = a.uni[(size_t(b) * (a.G + 1) + pos) * 2 + 1];
-  const double* cs = a.ws.jsum + size_t(b) * a.nch;
+// Shared state of the draw: the scan's per-wave totals, the pick and its
+// margin, the crossing chunk.
+struct PickLds {
+  double ex[4];
+  double d[4];
+  double mg;
+  int pick;
+  int chunk;
+};
 
-  // chunk sums: one per thread, an exclusive scan in thread order gives each
-  // chunk's running start; the crossing is in the first chunk whose running
-  // end exceeds u' Z (nch <= VT; larger vocabularies walk the sums in order)
+// Every case the common path of vb_draw_pick does not finish: vocabularies
+// of more than VT chunks (the sums are walked in order), a residual whose
+// weights all rounded to zero (the draw then uses P), and no crossing found
+// (the last positive weight wins).  Out of line so that the common path stays
+// short in the instruction cache.  For nch <= VT, Z, chunk and base_c come
+// from the common path's scan.
+template <bool VEC>
+__device__ __forceinline__ void draw_pick_rest(const VerifyArgs& a, const DrawRow& r, bool resid, int b, int pos,
+                                            float u2, double Z, int chunk, double base_c, PickLds* sh) {
+  const int t = threadIdx.x;
+  const double* cs = a.ws.jsum + size_t(b) * a.nch;
   bool use_p = false;
-  double Z = 0.0, base_c = 0.0;
-  int chunk = -1;
-  if (a.nch <= VT) {
-    const double mine = t < a.nch ? cs[t] : 0.0;
-    const double excl = block_exclusive_scan(mine, s_ex);
-    if (t == a.nch - 1) s_mg = excl + mine;  // total, in the scan's order
-    __syncthreads();
-    Z = s_mg;
-    __syncthreads();
-    if (t == 0) s_chunk = INT32_MAX;
-    __syncthreads();
-    if (!(resid && Z == 0.0)) {
-      const double tgt0 = double(u2) * Z;
-      if (t < a.nch && excl + mine > tgt0) atomicMin(&s_chunk, t);
-    }
-    __syncthreads();
-    if (s_chunk != INT32_MAX && s_chunk == t) s_mg = excl;
-    __syncthreads();
-    chunk = s_chunk == INT32_MAX ? -1 : s_chunk;
-    base_c = chunk >= 0 ? s_mg : 0.0;
-    __syncthreads();
-  } else {
+  if (a.nch > VT) {
+    Z = 0.0;
     for (int c = 0; c < a.nch; ++c) Z += cs[c];
   }
-  double tot_p = 0.0;
   if (resid && Z == 0.0) {
     // every residual weight rounded to zero: draw from P instead
     use_p = true;
     chunk = -1;
+    double tot_p = 0.0;
     for (int c = 0; c < a.nch; ++c) {
       double s = 0.0;
       for (int j = 0; j < VPT; ++j) {
         int e = c * VCH + t * VPT + j;
         if (e < a.V) s += double(draw_weight(r, a.c2, r.zt[e], 0.f, false));
       }
-      tot_p += block_sum_f64(s, s_d);
+      tot_p += block_sum_f64(s, sh->d);
     }
     Z = tot_p;
   }
   const double tgt = double(u2) * Z;
   if (a.nch > VT && !use_p) {
     // chunk holding the crossing, walking the sums in order
+    __syncthreads();
     if (t == 0) {
       double run = 0.0;
       int ch = -1;
@@ -863,10 +1014,10 @@ __global__ __launch_bounds__(VT) void vb_draw_pick(VerifyArgs a) {
         run += cs[c];
         if (run > tgt) { ch = c; break; }
       }
-      s_chunk = ch;
+      sh->chunk = ch;
     }
     __syncthreads();
-    chunk = s_chunk;
+    chunk = sh->chunk;
     base_c = 0.0;
     if (chunk >= 0)
       for (int c = 0; c < chunk; ++c) base_c += cs[c];
@@ -874,31 +1025,31 @@ __global__ __launch_bounds__(VT) void vb_draw_pick(VerifyArgs a) {
   int pick = INT32_MAX;
   double mg = 0.0;
   if (!use_p && chunk >= 0) {
-    scan_chunk(a, r, resid, false, chunk, base_c, tgt, &s_pick, &s_mg, s_ex);
-    pick = s_pick;
-    mg = s_mg;
+    scan_chunk<VEC, false>(a, r, resid, chunk, base_c, tgt, &sh->pick, &sh->mg, sh->ex);
+    pick = sh->pick;
+    mg = sh->mg;
     if (pick == INT32_MAX) {
-      pick = last_positive(a, r, resid, false, chunk, &s_pick);
+      pick = last_positive(a, r, resid, false, chunk, &sh->pick);
       mg = 0.0;
     }
   } else if (use_p) {
-    // P-weights: walk chunk by chunk (rare path)
+    // P-weights: walk chunk by chunk
     double run = 0.0;
     for (int c = 0; c < a.nch && pick == INT32_MAX; ++c) {
-      scan_chunk(a, r, resid, true, c, run, tgt, &s_pick, &s_mg, s_ex);
-      if (s_pick != INT32_MAX) { pick = s_pick; mg = s_mg; break; }
+      scan_chunk<VEC, true>(a, r, resid, c, run, tgt, &sh->pick, &sh->mg, sh->ex);
+      if (sh->pick != INT32_MAX) { pick = sh->pick; mg = sh->mg; break; }
       double s = 0.0;
       for (int j = 0; j < VPT; ++j) {
         int e = c * VCH + t * VPT + j;
         if (e < a.V) s += double(draw_weight(r, a.c2, r.zt[e], 0.f, false));
       }
-      run += block_sum_f64(s, s_d);
+      run += block_sum_f64(s, sh->d);
     }
   }
   if (pick == INT32_MAX || pick < 0) {
     // no crossing anywhere: the last x with a positive weight
     int last = -1;
-    for (int c = a.nch - 1; c >= 0 && last < 0; --c) last = last_positive(a, r, resid, use_p, c, &s_pick);
+    for (int c = a.nch - 1; c >= 0 && last < 0; --c) last = last_positive(a, r, resid, use_p, c, &sh->pick);
     pick = last >= 0 ? last : a.V - 1;
     mg = 0.0;
   }
@@ -906,6 +1057,136 @@ __global__ __launch_bounds__(VT) void vb_draw_pick(VerifyArgs a) {
     a.out[b * (a.G + 1) + pos] = pick;
     if (a.margin) a.margin[b] = float(mg);
   }
+}
+
+// The run of SUBLEN logits that holds the crossing, scanned by one wave:
+// lane l takes logits 4 l .. 4 l + 3 of the run, an inclusive scan over the
+// lanes gives each lane's running start.  Returns the pick (INT32_MAX when
+// rounding put the crossing outside the run) and its margin.
+__device__ __forceinline__ int scan_run(const VerifyArgs& a, const DrawRow& r, bool resid, int e0, double base,
+                                        double tgt, double& mg) {
+  const int lane = threadIdx.x & 63;
+  const int e = e0 + 4 * lane;
+  float wv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (e < a.V) {  // V % 4 == 0: the whole group of four is in the row
+    const float4 ft = *reinterpret_cast<const float4*>(r.zt + e);
+    float4 fd = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (resid) fd = *reinterpret_cast<const float4*>(r.zd + e);
+    wv[0] = draw_weight(r, a.c2, ft.x, fd.x, resid);
+    wv[1] = draw_weight(r, a.c2, ft.y, fd.y, resid);
+    wv[2] = draw_weight(r, a.c2, ft.z, fd.z, resid);
+    wv[3] = draw_weight(r, a.c2, ft.w, fd.w, resid);
+  }
+  double mine = 0.0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) mine += double(wv[q]);
+  double inc = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  double run = base + (inc - mine);
+  int pick = INT32_MAX;
+  double m = 0.0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const double prev = run;
+    run += double(wv[q]);
+    if (pick == INT32_MAX && run > tgt) { pick = e + q; m = fmin(tgt - prev, run - tgt); }
+  }
+  const unsigned long long hit = __ballot(pick != INT32_MAX);
+  if (!hit) return INT32_MAX;
+  const int src = __ffsll((long long)hit) - 1;
+  mg = __shfl(m, src);
+  return __shfl(pick, src);
+}
+
+// One workgroup per request: the chunk sums of the draw weights give Z and,
+// through an exclusive scan in chunk order, the chunk whose running end first
+// exceeds u' Z.  Vector rows then walk that chunk's run sums in order and scan
+// the one run holding the crossing; other rows scan the whole chunk.  What
+// this does not settle (rounding at a boundary, residual weights that all
+// rounded to zero, very large vocabularies) goes to draw_pick_rest.
+template <bool VEC>
+__global__ __launch_bounds__(VT) void vb_draw_pick(VerifyArgs a) {
+  __shared__ PickLds sh;
+  __shared__ double s_sub[VEC ? PICK_FAST_NCH * NSUB : 1];
+  __shared__ int s_done;
+  const int b = blockIdx.x, t = threadIdx.x;
+  // the job, this thread's chunk sum and the run sums are loaded together
+  const DrawJob jb = a.ws.job[b];
+  const double* cs = a.ws.jsum + size_t(b) * a.nch;
+  const double cs_t = t < a.nch ? cs[t] : 0.0;
+  const bool fast_runs = VEC && a.nch <= PICK_FAST_NCH;
+  if (fast_runs) {
+    const double* sub = a.ws.jsub + size_t(b) * a.nch * NSUB;
+    for (int i = t; i < a.nch * NSUB; i += VT) s_sub[i] = sub[i];
+  }
+  const int pos = jb.pos;
+  const bool resid = jb.kind == JOB_RESID;
+  const DrawRow r = job_row(a, b, jb);
+  const float u2 = jb.u2;
+  double Z = 0.0, base_c = 0.0;
+  int chunk = -1;
+  if (a.nch <= VT) {
+    const double excl = block_exclusive_scan(cs_t, sh.ex);
+    if (t == a.nch - 1) sh.mg = excl + cs_t;  // total, in the scan's order
+    if (t == 0) { sh.chunk = INT32_MAX; s_done = 0; }
+    __syncthreads();
+    Z = sh.mg;
+    if (!(resid && Z == 0.0)) {
+      const double tgt0 = double(u2) * Z;
+      if (t < a.nch && excl + cs_t > tgt0) atomicMin(&sh.chunk, t);
+    }
+    __syncthreads();
+    if (sh.chunk != INT32_MAX && sh.chunk == t) sh.mg = excl;
+    __syncthreads();
+    chunk = sh.chunk == INT32_MAX ? -1 : sh.chunk;
+    base_c = chunk >= 0 ? sh.mg : 0.0;
+    __syncthreads();
+    const double tgt = double(u2) * Z;
+    if (chunk >= 0 && fast_runs) {
+      if (t < 64) {
+        // the chunk's runs in order: the first whose running end exceeds tgt
+        int k = -1;
+        double bsub = 0.0;
+        if (t == 0) {
+          double run = base_c;
+          for (int i = 0; i < NSUB; ++i) {
+            const double prev = run;
+            run += s_sub[chunk * NSUB + i];
+            if (run > tgt) { k = i; bsub = prev; break; }
+          }
+        }
+        k = __shfl(k, 0);
+        bsub = __shfl(bsub, 0);
+        if (k >= 0) {
+          const int e0 = chunk * VCH + (k >> 2) * (4 * VT) + (k & 3) * SUBLEN;
+          double mg = 0.0;
+          const int pick = scan_run(a, r, resid, e0, bsub, tgt, mg);
+          if (pick != INT32_MAX && t == 0) {
+            a.out[b * (a.G + 1) + pos] = pick;
+            if (a.margin) a.margin[b] = float(mg);
+            s_done = 1;
+          }
+        }
+      }
+      __syncthreads();
+      if (s_done) return;
+    } else if (chunk >= 0) {
+      scan_chunk<VEC, false>(a, r, resid, chunk, base_c, tgt, &sh.pick, &sh.mg, sh.ex);
+      const int pick = sh.pick;
+      if (pick != INT32_MAX) {
+        if (t == 0) {
+          a.out[b * (a.G + 1) + pos] = pick;
+          if (a.margin) a.margin[b] = float(sh.mg);
+        }
+        return;
+      }
+    }
+  }
+  draw_pick_rest<VEC>(a, r, resid, b, pos, u2, Z, chunk, base_c, &sh);
 }
 
 // probabilities for the test path: full rows of the (filtered) P and Q
@@ -941,7 +1222,7 @@ __global__ __launch_bounds__(VT) void vb_write_probs(VerifyArgs a) {
 static inline size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct VerifyLayout {
-  size_t cmax, carg, csum, ctv, cti, rmax, rarg, rsum, rkn, rki, rkp, job, jsum, total;
+  size_t cmax, carg, csum, ctv, cti, rmax, rarg, rsum, rkn, rki, rkp, job, jsum, jsub, total;
 };
 
 static VerifyLayout verify_layout(int B, int G, int V, int top_k) {
@@ -964,8 +1245,9 @@ static VerifyLayout verify_layout(int B, int G, int V, int top_k) {
   L.rkn = o; o += al(rows * 4);
   L.rki = o; o += al(k ? rows * TOPK_MAX * 4 : 0);
   L.rkp = o; o += al(k ? rows * TOPK_MAX * 8 : 0);
-  L.job = o; o += al(size_t(B) * 2 * 4);
+  L.job = o; o += al(size_t(B) * sizeof(DrawJob));
   L.jsum = o; o += al(size_t(B) * nch * 8);
+  L.jsub = o; o += al(size_t(B) * nch * NSUB * 8);
   L.total = o;
   return L;
 }
@@ -1009,8 +1291,9 @@ hipError_t launch_verify(const float* zt, const float* zd, const int* dtok, cons
   a.ws.rkn = reinterpret_cast<int*>(w + L.rkn);
   a.ws.rki = reinterpret_cast<int*>(w + L.rki);
   a.ws.rkp = reinterpret_cast<double*>(w + L.rkp);
-  a.ws.job = reinterpret_cast<int*>(w + L.job);
+  a.ws.job = reinterpret_cast<DrawJob*>(w + L.job);
   a.ws.jsum = reinterpret_cast<double*>(w + L.jsum);
+  a.ws.jsub = reinterpret_cast<double*>(w + L.jsub);
 
   const bool vec = (V & 3) == 0;
   const long long work = (long long)a.n_rows * a.nch;
@@ -1028,11 +1311,13 @@ hipError_t launch_verify(const float* zt, const float* zd, const int* dtok, cons
     if (vec) hipLaunchKernelGGL(vb_stats_stream<true>, dim3(grid), dim3(VT), 0, stream, a);
     else hipLaunchKernelGGL(vb_stats_stream<false>, dim3(grid), dim3(VT), 0, stream, a);
   }
-  hipLaunchKernelGGL(vb_decide, dim3(B), dim3(DT), 0, stream, a);
   if (!greedy && k == 0) {
-    if (vec) hipLaunchKernelGGL(vb_draw_sums<true>, dim3(a.nch, B), dim3(VT), 0, stream, a);
-    else hipLaunchKernelGGL(vb_draw_sums<false>, dim3(a.nch, B), dim3(VT), 0, stream, a);
-    hipLaunchKernelGGL(vb_draw_pick, dim3(B), dim3(VT), 0, stream, a);
+    if (vec) hipLaunchKernelGGL(vb_decide_sums<true>, dim3(a.nch, B), dim3(VT), 0, stream, a);
+    else hipLaunchKernelGGL(vb_decide_sums<false>, dim3(a.nch, B), dim3(VT), 0, stream, a);
+    if (vec) hipLaunchKernelGGL(vb_draw_pick<true>, dim3(B), dim3(VT), 0, stream, a);
+    else hipLaunchKernelGGL(vb_draw_pick<false>, dim3(B), dim3(VT), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(vb_decide, dim3(B), dim3(DT), 0, stream, a);
   }
   if (tprob || dprob)
     hipLaunchKernelGGL(vb_write_probs, dim3(unsigned(a.n_rows) * unsigned(a.nch)), dim3(VT), 0, stream, a);
