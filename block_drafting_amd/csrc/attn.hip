@@ -332,27 +332,49 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int b, int g, int row,
 
 // One key tile (K at byte kt, V at byte vt of LDS) against the wave's 32 query
 // rows: scores, online softmax in the exp2 domain, and the P.V accumulation.
+// All K fragment reads are issued before the score MFMAs and all V^T fragment
+// reads before the softmax, so the LDS latency is paid about once per phase
+// rather than once per MFMA.
 template <int HD>
 __device__ __forceinline__ void tile_math(const AttnArgs& a, const uint8_t* lds, uint32_t kt, uint32_t vt,
                                           bool mask, int klo, int khi, int lane, const bf16x8 (&qf)[HD / 16],
                                           floatx16 (&acc)[HD / 32], float& m_run, float& l_run) {
   const int lr = lane & 31, h = lane >> 5;
+  u32x4 kf[HD / 16];
+#pragma unroll
+  for (int ks = 0; ks < HD / 16; ++ks)
+    kf[ks] = *reinterpret_cast<const u32x4*>(lds + kt + piece_off<HD>(lr, 2 * ks + h));
   floatx16 s = {};
 #pragma unroll
-  for (int ks = 0; ks < HD / 16; ++ks) {
-    const u32x4 kf = *reinterpret_cast<const u32x4*>(lds + kt + piece_off<HD>(lr, 2 * ks + h));
-    s = mfma32x32x16(__builtin_bit_cast(bf16x8, kf), qf[ks], s);
+  for (int ks = 0; ks < HD / 16; ++ks) s = mfma32x32x16(__builtin_bit_cast(bf16x8, kf[ks]), qf[ks], s);
+  // V^T fragments by transpose reads: in each group of 16 lanes, lane 4e + q
+  // points at key k0 + e, dims 4q .. 4q + 3 of the group's 16 dims, and lane i
+  // receives dim i of keys k0 .. k0 + 3.  Two reads give the lane's 8 keys
+  // (4h .. 4h + 3 and 8 + 4h .. 8 + 4h + 3 of the 16-key step).
+  const int gi = lane & 15, e = gi >> 2, q = gi & 3, gh = (lane >> 4) & 1;
+  bf16x8 vf[HD / 32][2];
+#pragma unroll
+  for (int d = 0; d < HD / 32; ++d) {
+    const int c = 4 * d + 2 * gh + (q >> 1);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int k0 = 16 * s2 + 4 * h + e;
+      const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (lds_bf16x4*)(lds + vt + piece_off<HD>(k0, c) + 8 * (q & 1)));
+      const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (lds_bf16x4*)(lds + vt + piece_off<HD>(k0 + 8, c) + 8 * (q & 1)));
+      vf[d][s2] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
   }
   // lane holds keys 8 (r / 4) + 4 h + r % 4 of row lr; keys outside the
   // lane's [klo, khi) get -inf (short tiles, and the causal / per-query
-  // window bounds)
+  // window bounds): key - klo < khi - klo as unsigned
   float tmax = -INFINITY;
   if (mask) {
+    const int kb = 4 * h - klo;
+    const unsigned span = khi > klo ? unsigned(khi - klo) : 0u;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 8 * (r >> 2) + 4 * h + (r & 3);
-      s[r] = (key >= klo && key < khi) ? s[r] : -INFINITY;
-    }
+    for (int r = 0; r < 16; ++r) s[r] = unsigned(kb + 8 * (r >> 2) + (r & 3)) < span ? s[r] : -INFINITY;
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
@@ -383,25 +405,10 @@ __device__ __forceinline__ void tile_math(const AttnArgs& a, const uint8_t* lds,
                                                    pk_bf16(s[8 * s2 + 2], s[8 * s2 + 3]),
                                                    pk_bf16(s[8 * s2 + 4], s[8 * s2 + 5]),
                                                    pk_bf16(s[8 * s2 + 6], s[8 * s2 + 7])));
-  // V^T fragments by transpose reads: in each group of 16 lanes, lane 4e + q
-  // points at key k0 + e, dims 4q .. 4q + 3 of the group's 16 dims, and lane i
-  // receives dim i of keys k0 .. k0 + 3.  Two reads give the lane's 8 keys
-  // (4h .. 4h + 3 and 8 + 4h .. 8 + 4h + 3 of the 16-key step).
-  const int gi = lane & 15, e = gi >> 2, q = gi & 3, gh = (lane >> 4) & 1;
 #pragma unroll
-  for (int d = 0; d < HD / 32; ++d) {
-    const int c = 4 * d + 2 * gh + (q >> 1);
+  for (int d = 0; d < HD / 32; ++d)
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int k0 = 16 * s2 + 4 * h + e;
-      const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (lds_bf16x4*)(lds + vt + piece_off<HD>(k0, c) + 8 * (q & 1)));
-      const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (lds_bf16x4*)(lds + vt + piece_off<HD>(k0 + 8, c) + 8 * (q & 1)));
-      const bf16x8 vf = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-      acc[d] = mfma32x32x16(vf, pb[s2], acc[d]);
-    }
-  }
+    for (int s2 = 0; s2 < 2; ++s2) acc[d] = mfma32x32x16(vf[d][s2], pb[s2], acc[d]);
 }
 
 template <int HD, int NW>
