@@ -177,3 +177,58 @@ def verify(z_target, z_draft, draft_tokens, uniforms, temperature: float,
         res["target_probs"] = probs_t
         res["draft_probs"] = probs_d
     return res
+
+
+def confidence_label(p: np.ndarray, q: np.ndarray) -> float:
+    """DSpark tutorial, confidence-scheduled verification: the label of a drafted
+    position is one minus the total-variation distance of the draft and target
+    distributions, which equals sum_x min(p, q) (the acceptance probability)."""
+    return acceptance_probability(p, q)
+
+
+def verify_ragged(z_target, z_draft, draft_tokens, uniforms, row_cu, temperature: float,
+                  top_k: int = 0, top_p: float = 1.0, want_beta: bool = False):
+    """Verify requests with their own drafted lengths (the per-request verify
+    length the DSpark tutorial's prefix scheduler picks).
+
+    Request b owns target rows row_cu[b] .. row_cu[b+1] - 1 (G_b + 1 of them)
+    and draft rows row_cu[b] - b .. row_cu[b+1] - b - 2 (G_b).  z_target
+    [N, V], z_draft [N - B, V], draft_tokens [N - B], uniforms [N, 2].
+    Each request is verified exactly as verify() does for a batch of one.
+    Returns tau [B], out_tokens [N], accept_ratio [N - B], sample_margin [B],
+    near_ties [B] and, with want_beta, beta [N - B]: the confidence label of
+    each drafted position under the verification distributions (greedy: the
+    point masses at the two lowest-index maxima)."""
+    row_cu = np.asarray(row_cu, dtype=np.int64)
+    B = len(row_cu) - 1
+    N = int(row_cu[-1])
+    tau = np.zeros(B, dtype=np.int32)
+    out = np.full(N, -1, dtype=np.int32)
+    ratio = np.zeros(N - B, dtype=np.float32)
+    margin = np.full(B, np.inf)
+    near = np.zeros(B, dtype=np.int32)
+    beta = np.zeros(N - B) if want_beta else None
+    greedy = temperature == 0.0
+    for b in range(B):
+        t0, t1 = int(row_cu[b]), int(row_cu[b + 1])
+        G = t1 - t0 - 1
+        d0 = t0 - b
+        zd = None if z_draft is None else np.asarray(z_draft[d0:d0 + G])[None]
+        r = verify(np.asarray(z_target[t0:t1])[None], zd, np.asarray(draft_tokens[d0:d0 + G])[None],
+                   None if uniforms is None else np.asarray(uniforms[t0:t1])[None], temperature, top_k, top_p)
+        tau[b] = r["tau"][0]
+        out[t0:t1] = r["out_tokens"][0]
+        ratio[d0:d0 + G] = r["accept_ratio"][0]
+        margin[b] = r["sample_margin"][0]
+        near[b] = r["near_ties"][0]
+        if want_beta:
+            for i in range(G):
+                if greedy:
+                    beta[d0 + i] = float(np.argmax(z_target[t0 + i]) == np.argmax(z_draft[d0 + i]))
+                else:
+                    beta[d0 + i] = confidence_label(filtered_probs(z_target[t0 + i], temperature, top_k, top_p),
+                                                    filtered_probs(z_draft[d0 + i], temperature, top_k, top_p))
+    res = dict(tau=tau, out_tokens=out, accept_ratio=ratio, sample_margin=margin, near_ties=near)
+    if want_beta:
+        res["beta"] = beta
+    return res

@@ -256,3 +256,68 @@ def test_ratio_is_fp32_division():
             p = special.softmax(zt[b, i].astype(np.float64))[d[b, i]]
             q = special.softmax(zd[b, i].astype(np.float64))[d[b, i]]
             assert r["accept_ratio"][b, i] == np.float32(np.float32(p) / np.float32(q))
+
+
+# ---- per-request verify lengths and the confidence label (DSpark tutorial,
+# confidence-scheduled verification)
+
+def _ragged_case(rng, G_list, V, T):
+    row_cu = np.concatenate([[0], np.cumsum(np.asarray(G_list) + 1)])
+    N, B = int(row_cu[-1]), len(G_list)
+    zt = rng.standard_normal((N, V)).astype(np.float32)
+    zd = rng.standard_normal((N - B, V)).astype(np.float32)
+    d = rng.integers(0, V, N - B).astype(np.int32)
+    u = rng.uniform(0, 1, (N, 2)).astype(np.float32)
+    return zt, zd, d, u, row_cu
+
+
+@pytest.mark.parametrize("T,k,p", [(0.0, 0, 1.0), (1.0, 0, 1.0), (0.7, 5, 0.9)])
+def test_ragged_with_equal_lengths_is_the_batched_form(T, k, p):
+    rng = np.random.default_rng(40)
+    B, G, V = 3, 4, 50
+    zt, zd, d, u, row_cu = _ragged_case(rng, [G] * B, V, T)
+    a = ov.verify_ragged(zt, zd, d, u, row_cu, T, k, p)
+    b = ov.verify(zt.reshape(B, G + 1, V), zd.reshape(B, G, V), d.reshape(B, G), u.reshape(B, G + 1, 2), T, k, p)
+    np.testing.assert_array_equal(a["tau"], b["tau"])
+    np.testing.assert_array_equal(a["out_tokens"], b["out_tokens"].reshape(-1))
+    np.testing.assert_array_equal(a["accept_ratio"], b["accept_ratio"].reshape(-1))
+
+
+def test_ragged_request_without_drafts_emits_one_target_token():
+    rng = np.random.default_rng(41)
+    zt, zd, d, u, row_cu = _ragged_case(rng, [2, 0, 3], 30, 1.0)
+    g = ov.verify_ragged(zt, zd, d, u, row_cu, 0.0)
+    assert g["tau"][1] == 0 and g["out_tokens"][3] == int(np.argmax(zt[3]))
+    s = ov.verify_ragged(zt, zd, d, u, row_cu, 1.0)
+    p = special.softmax(zt[3].astype(np.float64))
+    c = np.cumsum(p)
+    assert s["tau"][1] == 0 and s["out_tokens"][3] == int(np.searchsorted(c, u[3, 1] * c[-1], side="right"))
+
+
+def test_confidence_label_closed_forms():
+    rng = np.random.default_rng(42)
+    p = rng.dirichlet(np.ones(20))
+    q = rng.dirichlet(np.ones(20))
+    assert ov.confidence_label(p, p) == pytest.approx(1.0)
+    assert ov.confidence_label(p, q) == pytest.approx(1.0 - 0.5 * np.abs(p - q).sum())
+    a = np.zeros(20); a[:10] = 0.1
+    b = np.zeros(20); b[10:] = 0.1
+    assert ov.confidence_label(a, b) == 0.0
+
+
+def test_ragged_beta_is_the_label_of_each_drafted_position():
+    rng = np.random.default_rng(43)
+    zt, zd, d, u, row_cu = _ragged_case(rng, [3, 1, 0, 2], 40, 0.8)
+    r = ov.verify_ragged(zt, zd, d, u, row_cu, 0.8, want_beta=True)
+    for b in range(4):
+        t0, t1 = row_cu[b], row_cu[b + 1]
+        for i in range(t1 - t0 - 1):
+            p = special.softmax(zt[t0 + i].astype(np.float64) / 0.8)
+            q = special.softmax(zd[t0 - b + i].astype(np.float64) / 0.8)
+            assert r["beta"][t0 - b + i] == pytest.approx(1.0 - 0.5 * np.abs(p - q).sum(), rel=1e-12)
+    # greedy: the point masses at the two lowest-index maxima
+    zt2 = zt.copy(); zd2 = zd.copy()
+    zd2[0] = zt2[0]                       # same argmax -> 1
+    zd2[1] = -zt2[1]                      # argmax differs (almost surely) -> 0
+    g = ov.verify_ragged(zt2, zd2, d, u, row_cu, 0.0, want_beta=True)
+    assert g["beta"][0] == 1.0 and g["beta"][1] == 0.0
