@@ -207,6 +207,9 @@ def main():
                     peak=dom["peak"], unit=dom["unit"], frac=round(dom["frac"], 4),
                     traffic=dom["traffic"])
 
+    extras = next_rows(a, cfg, r, bd, torch, dev, stream, q, kb, vb, kc, vc, cache_base, ctx_len, max_ctx, zt,
+                       zd, dtok, uni, att_bytes)
+
     # ---------------------------------------------------------------- CPU baseline
     cpu = None
     if not a.no_cpu_baseline:
@@ -236,10 +239,92 @@ def main():
         "stages": [{k: (round(v, 4) if isinstance(v, float) and k != "traffic" else v) for k, v in s.items()}
                    for s in stages],
         "cpu_baseline": cpu,
+        "extras": extras,
     }
     if a.copy_calibration:
         line["copy_calibration"] = copy_calibration(torch, dev)
     print(json.dumps(line), flush=True)
+
+
+def _time_us(torch, stream, fn, n=20, warm=3):
+    """Average time of fn() on the stream, from HIP events around n calls."""
+    for _ in range(warm):
+        fn()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def next_rows(a, cfg, r, bd, torch, dev, stream, q, kb, vb, kc, vc, cache_base, ctx_len, max_ctx, zt, zd, dtok,
+              uni, att_bytes):
+    """Measurements of the variants built on the same path, outside the timed
+    rounds: causal block attention, verification with a per-request drafted
+    length (and with the confidence labels), and the prefix scheduler driven
+    by a steps-per-second table measured from verify_block_ragged itself."""
+    B, K, G, L, V = cfg.B, cfg.K, cfg.G, cfg.L, cfg.V
+    ex = {}
+    # causal in-block attention, one layer at a time over the round's layers
+    ws_att = torch.empty(max(1, bd.draft_block_attn_workspace_size(B, K, cfg.n_q, cfg.n_kv, cfg.hd, max_ctx,
+                                                                    cfg.window)), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, K, cfg.n_q, cfg.hd), dtype=torch.int16, device=dev)
+    t_c = _time_us(torch, stream, lambda: [bd.draft_block_attn(q[l], kb[l], vb[l], kc[l], vc[l], cache_base, ctx_len,
+                                                               max_ctx, cfg.window, flags=bd.BD_ATTN_CAUSAL, out=out,
+                                                               workspace=ws_att) for l in range(L)]) / L
+    ex["draft_block_attn_causal"] = dict(per_call_us=round(t_c, 2), achieved_gbs=round(att_bytes / t_c / 1e3, 1),
+                                         frac=round(att_bytes / t_c / 1e3 / HBM_PEAK_GBS, 4))
+    if zd is None:
+        return ex
+    # per-request drafted lengths: G_b uniform in 0..G (seeded), rows cut from the round's logits
+    rng = np.random.default_rng(5)
+    g_list = [int(x) for x in rng.integers(0, G + 1, B)]
+
+    def packed(gl):
+        zt_p = torch.cat([zt[b, :g + 1] for b, g in enumerate(gl)]).contiguous()
+        zd_p = torch.cat([zd[b, :g] for b, g in enumerate(gl)]).contiguous()
+        dt_p = torch.cat([dtok[b, :g] for b, g in enumerate(gl)]).contiguous()
+        u_p = torch.cat([uni[b, :g + 1] for b, g in enumerate(gl)]).contiguous()
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(np.asarray(gl) + 1)]), dtype=torch.int32, device=dev)
+        return zt_p, zd_p, dt_p, u_p, cu
+
+    zt_p, zd_p, dt_p, u_p, cu = packed(g_list)
+    n_t = zt_p.shape[0]
+    ws = torch.empty(max(1, bd.verify_block_ragged_workspace_size(B, n_t, G, V, cfg.top_k, True)), dtype=torch.uint8,
+                     device=dev)
+    beta = torch.empty(max(1, n_t - B), dtype=torch.float32, device=dev)
+    run = lambda want: bd.verify_block_ragged(zt_p, zd_p, dt_p, u_p, cu, G, cfg.temperature, cfg.top_k, cfg.top_p,
+                                              beta=beta if want else None, workspace=ws)
+    t_r = _time_us(torch, stream, lambda: run(False))
+    t_rb = _time_us(torch, stream, lambda: run(True))
+    rbytes = 4.0 * V * (2 * n_t - B)
+    ex["verify_block_ragged"] = dict(workload=f"B={B} G_b uniform in 0..{G} (seed 5), {n_t} target rows, V={V}",
+                                     per_call_us=round(t_r, 2), achieved_gbs=round(rbytes / t_r / 1e3, 1),
+                                     frac=round(rbytes / t_r / 1e3 / HBM_PEAK_GBS, 4),
+                                     with_labels_us=round(t_rb, 2))
+    # steps-per-second table of the verify step from our own kernel, then the scheduler
+    table_b, table_v = [], []
+    for per in (1, 2, 4, 8, 12, G + 1):
+        gl = [per - 1] * B
+        zt_q, zd_q, dt_q, u_q, cu_q = packed(gl)
+        wsq = torch.empty(max(1, bd.verify_block_ragged_workspace_size(B, zt_q.shape[0], G, V, cfg.top_k, False)),
+                          dtype=torch.uint8, device=dev)
+        t = _time_us(torch, stream, lambda: bd.verify_block_ragged(zt_q, zd_q, dt_q, u_q, cu_q, G, cfg.temperature,
+                                                                   cfg.top_k, cfg.top_p, workspace=wsq), n=10)
+        table_b.append(float(zt_q.shape[0]))
+        table_v.append(1e6 / t)
+    surv = [np.full(G, c, np.float32) for c in rng.uniform(0.6, 0.95, B)]
+    t0 = time.perf_counter()
+    ell, theta = bd.prefix_schedule(surv, table_b, table_v)
+    host_us = (time.perf_counter() - t0) * 1e6
+    ex["prefix_schedule"] = dict(sps_table=[[int(b_), round(v_, 1)] for b_, v_ in zip(table_b, table_v)],
+                                 survival="per request constant c_r ~ U(0.6, 0.95) (seed 5), G positions",
+                                 chosen_tokens=int(sum(ell) + B), theta=round(theta, 1), host_us=round(host_us, 1))
+    return ex
 
 
 def copy_calibration(torch, dev):

@@ -28,6 +28,8 @@ EXPORTS = (
     "inject_kv_workspace_size", "inject_kv",
     "draft_block_attn_workspace_size", "draft_block_attn",
     "verify_block_workspace_size", "verify_block",
+    "verify_block_ragged_workspace_size", "verify_block_ragged",
+    "prefix_schedule",
 )
 
 
@@ -69,6 +71,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     L.verify_block_workspace_size.argtypes = [c_i32] * 4
     L.verify_block.restype = ctypes.c_int
     L.verify_block.argtypes = [c_p] * 4 + [c_i32] * 3 + [c_f, c_i32, c_f] + [c_p] * 6 + [c_p, c_sz, c_p]
+    L.verify_block_ragged_workspace_size.restype = c_sz
+    L.verify_block_ragged_workspace_size.argtypes = [c_i32] * 6
+    L.verify_block_ragged.restype = ctypes.c_int
+    L.verify_block_ragged.argtypes = [c_p] * 5 + [c_i32] * 4 + [c_f, c_i32, c_f] + [c_p] * 7 + [c_p, c_sz, c_p]
+    L.prefix_schedule.restype = ctypes.c_int
+    L.prefix_schedule.argtypes = [c_p, c_p, c_i32, c_p, c_p, c_i32, c_p, c_p]
     if path is None:
         _lib = L
     return L
@@ -203,6 +211,64 @@ def verify_block(target_logits, draft_logits, draft_tokens, uniforms, temperatur
     return tau, out_tokens
 
 
-__all__ = ["inject_kv", "draft_block_attn", "verify_block", "inject_kv_workspace_size",
-           "draft_block_attn_workspace_size", "verify_block_workspace_size", "BlockDraftError",
-           "load", "last_error", "lib_path", "EXPORTS"]
+def verify_block_ragged_workspace_size(B, n_target_rows, G_max, V, top_k, want_beta) -> int:
+    return int(load().verify_block_ragged_workspace_size(B, n_target_rows, G_max, V, top_k, int(bool(want_beta))))
+
+
+def verify_block_ragged(target_logits, draft_logits, draft_tokens, uniforms, row_cu, G_max: int,
+                        temperature: float = 0.0, top_k: int = 0, top_p: float = 1.0, tau=None, out_tokens=None,
+                        target_probs=None, draft_probs=None, accept_ratio=None, sample_margin=None, beta=None,
+                        workspace=None, stream=None):
+    """Verify requests with their own drafted lengths over packed rows
+    (request b: target rows row_cu[b] .. row_cu[b+1] - 1). target_logits
+    [N, V]; draft_logits [N - B, V]; row_cu int32 [B + 1] on the device.
+    Returns (tau, out_tokens)."""
+    N, V = target_logits.shape
+    B = row_cu.shape[0] - 1
+    dev = target_logits.device
+    _typed(target_logits, torch.float32, "target_logits")
+    _typed(draft_logits, torch.float32, "draft_logits")
+    _typed(draft_tokens, torch.int32, "draft_tokens")
+    _typed(uniforms, torch.float32, "uniforms")
+    _typed(row_cu, torch.int32, "row_cu")
+    _typed(beta, torch.float32, "beta")
+    if tau is None:
+        tau = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty(N, dtype=torch.int32, device=dev)
+    need = verify_block_ragged_workspace_size(B, N, G_max, V, top_k, beta is not None)
+    ws, nb = _workspace(need, workspace, dev)
+    st = load().verify_block_ragged(_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(uniforms),
+                                    _ptr(row_cu), B, N, int(G_max), V, float(temperature), int(top_k), float(top_p),
+                                    _ptr(tau), _ptr(out_tokens), _ptr(target_probs), _ptr(draft_probs),
+                                    _ptr(accept_ratio), _ptr(sample_margin), _ptr(beta), _ptr(ws), nb,
+                                    _stream(stream))
+    _check(st)
+    return tau, out_tokens
+
+
+def prefix_schedule(survival, sps_b, sps_v):
+    """Host prefix scheduler. survival: list of per-request sequences of
+    conditional survival probabilities; (sps_b, sps_v) the measured
+    batch -> steps-per-second table. Returns (ell list, theta)."""
+    import numpy as np
+    R = len(survival)
+    cu = np.zeros(R + 1, dtype=np.int32)
+    for r, c in enumerate(survival):
+        cu[r + 1] = cu[r] + len(c)
+    flat = np.ascontiguousarray(np.concatenate([np.asarray(c, np.float32) for c in survival]) if R else
+                                np.zeros(0, np.float32), dtype=np.float32)
+    tb = np.ascontiguousarray(sps_b, dtype=np.float32)
+    tv = np.ascontiguousarray(sps_v, dtype=np.float32)
+    ell = np.zeros(max(R, 1), dtype=np.int32)
+    theta = ctypes.c_double(0.0)
+    P = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    st = load().prefix_schedule(P(flat) if flat.size else None, P(cu), R, P(tb), P(tv), len(tb), P(ell),
+                                ctypes.byref(theta))
+    _check(st)
+    return [int(x) for x in ell[:R]], float(theta.value)
+
+
+__all__ = ["inject_kv", "draft_block_attn", "verify_block", "verify_block_ragged", "prefix_schedule",
+           "inject_kv_workspace_size", "draft_block_attn_workspace_size", "verify_block_workspace_size",
+           "verify_block_ragged_workspace_size", "BlockDraftError", "load", "last_error", "lib_path", "EXPORTS"]

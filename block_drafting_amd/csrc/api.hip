@@ -124,7 +124,7 @@ int draft_block_attn(const uint16_t* q, const uint16_t* k_blk, const uint16_t* v
 // ---------------------------------------------------------------- verify_block
 size_t verify_block_workspace_size(int32_t B, int32_t G, int32_t V, int32_t top_k) {
   if (B <= 0 || G < 0 || V <= 0 || top_k < 0) return 0;
-  return bd::verify_ws_bytes(B, G, V, top_k);
+  return bd::verify_ws_bytes(B, B * (G + 1), V, top_k, false);
 }
 
 int verify_block(const float* target_logits, const float* draft_logits,
@@ -159,10 +159,70 @@ int verify_block(const float* target_logits, const float* draft_logits,
                 workspace ? workspace_bytes : (size_t)0);
   if (need > 0 && !aligned16(workspace)) return fail(BD_E_UNSUPPORTED, "verify_block: workspace must be 16-byte aligned");
   if (B == 0) return ok();
-  return launched(bd::launch_verify(target_logits, draft_logits, draft_tokens, uniforms, B, G, V, temperature,
-                                    top_k, top_p, tau, out_tokens, target_probs, draft_probs, accept_ratio,
-                                    sample_margin, workspace, stream),
+  return launched(bd::launch_verify(target_logits, draft_logits, draft_tokens, uniforms, nullptr, B, B * (G + 1), G,
+                                    V, temperature, top_k, top_p, tau, out_tokens, target_probs, draft_probs,
+                                    accept_ratio, sample_margin, nullptr, workspace, stream),
                   "verify_block");
+}
+
+size_t verify_block_ragged_workspace_size(int32_t B, int32_t n_target_rows, int32_t G_max, int32_t V,
+                                          int32_t top_k, int32_t want_beta) {
+  if (B <= 0 || n_target_rows < B || G_max < 0 || V <= 0 || top_k < 0) return 0;
+  return bd::verify_ws_bytes(B, n_target_rows, V, top_k, want_beta != 0);
+}
+
+int verify_block_ragged(const float* target_logits, const float* draft_logits,
+                        const int32_t* draft_tokens, const float* uniforms, const int32_t* row_cu,
+                        int32_t B, int32_t n_target_rows, int32_t G_max, int32_t V,
+                        float temperature, int32_t top_k, float top_p,
+                        int32_t* tau, int32_t* out_tokens,
+                        float* target_probs, float* draft_probs,
+                        float* accept_ratio, float* sample_margin, float* beta,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || G_max < 0 || V < 1 || top_k < 0 || n_target_rows < B)
+    return fail(BD_E_SHAPE, "verify_block_ragged: need B >= 0, n_target_rows >= B, G_max >= 0, V >= 1, top_k >= 0 "
+                "(got B=%d n_target_rows=%d G_max=%d V=%d top_k=%d)", B, n_target_rows, G_max, V, top_k);
+  if ((long long)n_target_rows > (long long)B * (G_max + 1))
+    return fail(BD_E_SHAPE, "verify_block_ragged: n_target_rows (%d) exceeds B * (G_max + 1) (%lld)", n_target_rows,
+                (long long)B * (G_max + 1));
+  if (!(temperature >= 0.f) || temperature == INFINITY || top_p != top_p)
+    return fail(BD_E_SHAPE, "verify_block_ragged: temperature must be finite and >= 0, top_p not NaN");
+  if (top_k > 64) return fail(BD_E_UNSUPPORTED, "verify_block_ragged: top_k must be <= 64 (got %d)", top_k);
+  if (G_max > 64) return fail(BD_E_UNSUPPORTED, "verify_block_ragged: G_max must be <= 64 (got %d)", G_max);
+  if ((2LL * n_target_rows - B) * ((V + 8191) / 8192) > 0x7fffffffLL)
+    return fail(BD_E_UNSUPPORTED, "verify_block_ragged: too many (row, chunk) pairs");
+  const bool greedy = temperature == 0.f;
+  const bool drafts = n_target_rows > B;
+  if (!target_logits || !tau || !out_tokens || (B > 0 && !row_cu) || (drafts && !draft_tokens))
+    return fail(BD_E_NULL, "verify_block_ragged: target_logits, row_cu, draft_tokens, tau and out_tokens are required");
+  if (!greedy && (!uniforms || (drafts && !draft_logits)))
+    return fail(BD_E_NULL, "verify_block_ragged: sampling needs draft_logits and uniforms");
+  if ((draft_probs || beta) && drafts && !draft_logits)
+    return fail(BD_E_NULL, "verify_block_ragged: draft_probs and beta need draft_logits");
+  if (!aligned16(target_logits) || (draft_logits && !aligned16(draft_logits)))
+    return fail(BD_E_UNSUPPORTED, "verify_block_ragged: logits must be 16-byte aligned");
+  const size_t need = verify_block_ragged_workspace_size(B, n_target_rows, G_max, V, top_k, beta != nullptr);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(BD_E_WORKSPACE, "verify_block_ragged: workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (need > 0 && !aligned16(workspace))
+    return fail(BD_E_UNSUPPORTED, "verify_block_ragged: workspace must be 16-byte aligned");
+  if (B == 0) return ok();
+  return launched(bd::launch_verify(target_logits, draft_logits, draft_tokens, uniforms, row_cu, B, n_target_rows,
+                                    G_max, V, temperature, top_k, top_p, tau, out_tokens, target_probs, draft_probs,
+                                    accept_ratio, sample_margin, beta, workspace, stream),
+                  "verify_block_ragged");
+}
+
+// ---------------------------------------------------------------- prefix_schedule
+int prefix_schedule(const float* survival, const int32_t* survival_cu, int32_t R, const float* sps_b,
+                    const float* sps_v, int32_t n_sps, int32_t* ell, double* theta) {
+  if (R < 0 || n_sps < 1) return fail(BD_E_SHAPE, "prefix_schedule: need R >= 0 and n_sps >= 1 (got R=%d n_sps=%d)",
+                                      R, n_sps);
+  if (!sps_b || !sps_v || (R > 0 && (!survival_cu || !ell)))
+    return fail(BD_E_NULL, "prefix_schedule: sps_b, sps_v, survival_cu and ell are required");
+  bd::prefix_schedule(survival, survival_cu, R, sps_b, sps_v, n_sps, ell, theta);
+  return ok();
 }
 
 }  // extern "C"

@@ -19,10 +19,16 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* kb, const uint16_t* vb
                        int64_t T_cap, int max_ctx, int B, int K, int n_q, int n_kv, int hd, int window,
                        int flags, float scale, uint16_t* out, float* lse, void* ws, hipStream_t stream);
 
-size_t verify_ws_bytes(int B, int G, int V, int top_k);
+// n_trows target rows in all (B * (G + 1) without a row map); G is the
+// largest drafted length; beta (labels) may be NULL
+size_t verify_ws_bytes(int B, int n_trows, int V, int top_k, bool beta);
 hipError_t launch_verify(const float* zt, const float* zd, const int* dtok, const float* uni,
-                         int B, int G, int V, float temperature, int top_k, float top_p,
-                         int* tau, int* out, float* tprob, float* dprob, float* ratio, float* margin,
-                         void* ws, hipStream_t stream);
+                         const int* row_cu, int B, int n_trows, int G, int V, float temperature, int top_k,
+                         float top_p, int* tau, int* out, float* tprob, float* dprob, float* ratio, float* margin,
+                         float* beta, void* ws, hipStream_t stream);
+
+// prefix scheduler (host)
+int prefix_schedule(const float* surv, const int32_t* surv_cu, int R, const float* sps_b, const float* sps_v,
+                    int n_sps, int32_t* ell, double* theta);
 
 }  // namespace bd

@@ -49,7 +49,7 @@ constexpr int PICK_FAST_NCH = 64;          // chunks whose run sums the draw kee
 constexpr int STATS_GRID = BD_STATS_GRID;
 constexpr int CAND_PER_WAVE = 64;
 
-enum { JOB_RESID = 1, JOB_BONUS = 2 };
+enum { JOB_NONE = 0, JOB_RESID = 1, JOB_BONUS = 2 };
 
 // The full-vocabulary draw of one request: the position, the kind, the
 // uniform, and the row maxima and 1 / sums of the row pair (one load).
@@ -152,6 +152,7 @@ struct VerifyWs {
   DrawJob* job;  // [B]             the draw each request needs
   double* jsum;  // [B][nch]
   double* jsub;  // [B][nch][NSUB]  vector rows: sums over runs of SUBLEN logits
+  double* jbeta; // [n_draft][nch]  per-chunk sums of min(P, Q) (labels, full vocabulary)
 };
 
 struct VerifyArgs {
@@ -159,9 +160,10 @@ struct VerifyArgs {
   const float* zd;
   const int* dtok;
   const float* uni;
-  int B, G, V, nch;
+  int B, G, V, nch;      // G: drafted tokens per request (the largest one with row_cu)
   int cpw;               // consecutive (row, chunk) pairs per statistics workgroup
-  int n_trows, n_rows;   // target rows B*(G+1); all rows with draft rows
+  int n_trows, n_rows;   // target rows; all rows with the draft rows
+  const int* row_cu;     // [B + 1] first target row of each request, or NULL: B * (G + 1)
   float T;               // temperature used for probabilities (1 when greedy)
   float c2;              // log2(e) / T
   int greedy, topk, need_sum;
@@ -172,8 +174,36 @@ struct VerifyArgs {
   float* dprob;
   float* ratio;
   float* margin;
+  float* beta;           // [n_draft] confidence label of each drafted position, or NULL
   VerifyWs ws;
 };
+
+// Rows of request b: target rows t0 .. t0 + G, draft rows d0 .. d0 + G - 1
+// (packed: d0 = t0 - b).  With a row map the request is valid when its rows
+// lie inside the packed arrays with room for one row per other request and
+// 0 <= G <= the largest G; an invalid request gets tau = -1 and nothing else.
+struct ReqRows {
+  int t0, d0, G;
+  bool ok;
+};
+
+__device__ __forceinline__ ReqRows req_rows(const VerifyArgs& a, int b) {
+  ReqRows r;
+  if (!a.row_cu) {
+    r.t0 = b * (a.G + 1);
+    r.d0 = b * a.G;
+    r.G = a.G;
+    r.ok = true;
+    return r;
+  }
+  const int c0 = a.row_cu[b], c1 = a.row_cu[b + 1];
+  r.G = c1 - c0 - 1;
+  r.t0 = c0;
+  r.d0 = c0 - b;
+  r.ok = c0 >= b && r.G >= 0 && r.G <= a.G && c1 <= a.n_trows - (a.B - 1 - b);
+  if (!r.ok) { r.t0 = 0; r.d0 = 0; r.G = 0; }
+  return r;
+}
 
 __device__ __forceinline__ const float* row_ptr(const VerifyArgs& a, int r) {
   return r < a.n_trows ? a.zt + size_t(r) * a.V : a.zd + size_t(r - a.n_trows) * a.V;
@@ -589,11 +619,17 @@ constexpr int DT = 1024;  // threads of the decision workgroup (16 waves)
 __global__ __launch_bounds__(DT) void vb_decide(VerifyArgs a) {
   const int b = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int G = a.G;
-  // rows of this request: G+1 target rows, then G draft rows when sampling
-  const int n_my = (G + 1) + ((a.n_rows > a.n_trows) ? G : 0);
+  const ReqRows rr = req_rows(a, b);
+  if (!rr.ok) {
+    if (t == 0) a.tau[b] = -1;
+    return;
+  }
+  const int G = rr.G;
+  const bool drafts = a.n_rows > a.n_trows;
+  // rows of this request: G+1 target rows, then G draft rows when present
+  const int n_my = (G + 1) + (drafts ? G : 0);
   for (int j = w; j < n_my; j += DT / 64) {
-    int row = j <= G ? b * (G + 1) + j : a.n_trows + b * G + (j - G - 1);
+    int row = j <= G ? rr.t0 + j : a.n_trows + rr.d0 + (j - G - 1);
     merge_row(a, row, lane);
   }
   __threadfence_block();
@@ -605,13 +641,14 @@ __global__ __launch_bounds__(DT) void vb_decide(VerifyArgs a) {
   float ratio = 0.f;
   int d = -1;
   if (lane < G) {
-    d = a.dtok[b * G + lane];
-    const int trow = b * (G + 1) + lane;
+    d = a.dtok[rr.d0 + lane];
+    const int trow = rr.t0 + lane;
+    const int drow = a.n_trows + rr.d0 + lane;
     if (a.greedy) {
       acc = (d == a.ws.rarg[trow]);
       ratio = acc ? 1.f : 0.f;
+      if (a.beta) a.beta[rr.d0 + lane] = a.ws.rarg[trow] == a.ws.rarg[drow] ? 1.f : 0.f;
     } else {
-      const int drow = a.n_trows + b * G + lane;
       double p = 0.0, q = 0.0;
       if (d >= 0 && d < a.V) {
         p = kept_prob(a, trow, d);
@@ -619,29 +656,38 @@ __global__ __launch_bounds__(DT) void vb_decide(VerifyArgs a) {
       }
       float p32 = float(p), q32 = float(q);
       ratio = p32 / q32;
-      float u = a.uni[(size_t(b) * (G + 1) + lane) * 2];
+      float u = a.uni[(size_t(rr.t0) + lane) * 2];
       acc = u < ratio;
+      if (a.beta) {
+        // sum over P's kept support of min(P, Q) (outside it min is 0)
+        const int n = a.ws.rkn[trow];
+        const int* ki = a.ws.rki + size_t(trow) * TOPK_MAX;
+        const double* kp = a.ws.rkp + size_t(trow) * TOPK_MAX;
+        double sm = 0.0;
+        for (int j = 0; j < n; ++j) sm += fmin(kp[j], kept_prob(a, drow, ki[j]));
+        a.beta[rr.d0 + lane] = float(sm);
+      }
     }
-    if (a.ratio) a.ratio[b * G + lane] = ratio;
+    if (a.ratio) a.ratio[rr.d0 + lane] = ratio;
   }
   unsigned long long rej = __ballot(lane < G && !acc);
   int tau = rej ? __ffsll((long long)rej) - 1 : G;
   if (lane == 0) a.tau[b] = tau;
   for (int i = lane; i <= G; i += 64) {
-    if (i < tau) a.out[b * (G + 1) + i] = a.dtok[b * G + i];
-    else if (i > tau) a.out[b * (G + 1) + i] = -1;
+    if (i < tau) a.out[rr.t0 + i] = a.dtok[rr.d0 + i];
+    else if (i > tau) a.out[rr.t0 + i] = -1;
   }
-  const int trow = b * (G + 1) + tau;
+  const int trow = rr.t0 + tau;
   if (a.greedy) {
     if (lane == 0) {
-      a.out[b * (G + 1) + tau] = a.ws.rarg[trow];
+      a.out[rr.t0 + tau] = a.ws.rarg[trow];
       if (a.margin) a.margin[b] = INFINITY;
     }
     return;
   }
   // top-k: draw over the kept support (full-vocabulary sampling runs
   // vb_decide_sums instead of this kernel)
-  const float u2 = a.uni[(size_t(b) * (G + 1) + tau) * 2 + 1];
+  const float u2 = a.uni[(size_t(rr.t0) + tau) * 2 + 1];
   {
     if (lane != 0) return;
     // draw over P's kept support in vocabulary order
@@ -659,7 +705,7 @@ __global__ __launch_bounds__(DT) void vb_decide(VerifyArgs a) {
     }
     double Z = 0.0;
     if (tau < G) {
-      const int drow = a.n_trows + b * G + tau;
+      const int drow = a.n_trows + rr.d0 + tau;
       for (int j = 0; j < n; ++j) {
         double r = wgt[j] - kept_prob(a, drow, idx[j]);
         wgt[j] = r > 0.0 ? r : 0.0;
@@ -685,15 +731,16 @@ __global__ __launch_bounds__(DT) void vb_decide(VerifyArgs a) {
       if (pick < 0) pick = n - 1;
       mg = 0.0;
     }
-    a.out[b * (G + 1) + tau] = idx[pick];
+    a.out[rr.t0 + tau] = idx[pick];
     if (a.margin) a.margin[b] = float(mg);
   }
 }
 
 __device__ __forceinline__ DrawRow job_row(const VerifyArgs& a, int b, const DrawJob& j) {
   DrawRow r;
-  r.zt = a.zt + size_t(b * (a.G + 1) + j.pos) * a.V;
-  r.zd = j.kind == JOB_RESID ? a.zd + size_t(b * a.G + j.pos) * a.V : nullptr;
+  const ReqRows rr = req_rows(a, b);
+  r.zt = a.zt + size_t(rr.t0 + j.pos) * a.V;
+  r.zd = j.kind == JOB_RESID ? a.zd + size_t(rr.d0 + j.pos) * a.V : nullptr;
   r.mt = j.mt;
   r.st = j.st;
   r.md = j.md;
@@ -735,15 +782,25 @@ __global__ __launch_bounds__(VT) void vb_decide_sums(VerifyArgs a) {
   __shared__ double s_d[4];
   __shared__ int s_tau;
   const int b = blockIdx.y, c = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int G = a.G;
+  const ReqRows rr = req_rows(a, b);
+  if (!rr.ok) {
+    if (c == 0 && t == 0) {
+      a.tau[b] = -1;
+      DrawJob jb = {};
+      jb.kind = JOB_NONE;
+      a.ws.job[b] = jb;
+    }
+    return;
+  }
+  const int G = rr.G;
   int d = -1;
   float zt_d = 0.f, zd_d = 0.f, u = 0.f;
   if (w == 0 && lane < G) {
-    d = a.dtok[b * G + lane];
-    u = a.uni[(size_t(b) * (G + 1) + lane) * 2];
+    d = a.dtok[rr.d0 + lane];
+    u = a.uni[(size_t(rr.t0) + lane) * 2];
     if (d >= 0 && d < a.V) {
-      zt_d = a.zt[size_t(b * (G + 1) + lane) * a.V + d];
-      zd_d = a.zd[size_t(b * G + lane) * a.V + d];
+      zt_d = a.zt[size_t(rr.t0 + lane) * a.V + d];
+      zd_d = a.zd[size_t(rr.d0 + lane) * a.V + d];
     }
   }
   // rows j = 0..G: target rows, j = G + 1..2G: draft rows; thread j merges
@@ -751,7 +808,7 @@ __global__ __launch_bounds__(VT) void vb_decide_sums(VerifyArgs a) {
   // together
   const int n_my = 2 * G + 1;
   if (t < n_my) {
-    const int row = t <= G ? b * (G + 1) + t : a.n_trows + b * G + (t - G - 1);
+    const int row = t <= G ? rr.t0 + t : a.n_trows + rr.d0 + (t - G - 1);
     size_t slot0;
     const int nrec = row_records(a, row, slot0);
     float v = -INFINITY;
@@ -790,14 +847,14 @@ __global__ __launch_bounds__(VT) void vb_decide_sums(VerifyArgs a) {
     const int tau = rej ? __ffsll((long long)rej) - 1 : G;
     if (lane == 0) s_tau = tau;
     if (c == 0) {
-      if (lane < G && a.ratio) a.ratio[b * G + lane] = ratio;
+      if (lane < G && a.ratio) a.ratio[rr.d0 + lane] = ratio;
       if (lane == 0) a.tau[b] = tau;
       for (int i = lane; i <= G; i += 64) {
-        if (i < tau) a.out[b * (G + 1) + i] = a.dtok[b * G + i];
-        else if (i > tau) a.out[b * (G + 1) + i] = -1;
+        if (i < tau) a.out[rr.t0 + i] = a.dtok[rr.d0 + i];
+        else if (i > tau) a.out[rr.t0 + i] = -1;
       }
       for (int j = lane; j < n_my; j += 64) {
-        const int row = j <= G ? b * (G + 1) + j : a.n_trows + b * G + (j - G - 1);
+        const int row = j <= G ? rr.t0 + j : a.n_trows + rr.d0 + (j - G - 1);
         a.ws.rmax[row] = s_m[j];
         a.ws.rarg[row] = s_i[j];
         a.ws.rsum[row] = s_s[j];
@@ -806,7 +863,7 @@ __global__ __launch_bounds__(VT) void vb_decide_sums(VerifyArgs a) {
         DrawJob jb;
         jb.pos = tau;
         jb.kind = tau < G ? JOB_RESID : JOB_BONUS;
-        jb.u2 = a.uni[(size_t(b) * (G + 1) + tau) * 2 + 1];
+        jb.u2 = a.uni[(size_t(rr.t0) + tau) * 2 + 1];
         jb.mt = s_m[tau];
         jb.st = float(1.0 / s_s[tau]);
         jb.md = tau < G ? s_m[G + 1 + tau] : 0.f;
@@ -820,8 +877,8 @@ __global__ __launch_bounds__(VT) void vb_decide_sums(VerifyArgs a) {
   const int tau = s_tau;
   const bool resid = tau < G;
   DrawRow r;
-  r.zt = a.zt + size_t(b * (G + 1) + tau) * a.V;
-  r.zd = resid ? a.zd + size_t(b * G + tau) * a.V : nullptr;
+  r.zt = a.zt + size_t(rr.t0 + tau) * a.V;
+  r.zd = resid ? a.zd + size_t(rr.d0 + tau) * a.V : nullptr;
   r.mt = s_m[tau];
   r.st = float(1.0 / s_s[tau]);
   r.md = resid ? s_m[G + 1 + tau] : 0.f;
@@ -862,6 +919,33 @@ __global__ __launch_bounds__(VT) void vb_decide_sums(VerifyArgs a) {
     }
     sum = block_sum_f64(sum, s_d);
     if (t == 0) a.ws.jsum[size_t(b) * a.nch + c] = sum;
+  }
+  if (a.beta) {
+    // confidence labels: this chunk's sum of min(P_i, Q_i) for every drafted
+    // position i of the request (vb_draw_pick adds the chunks up)
+    for (int i = 0; i < G; ++i) {
+      DrawRow rb;
+      rb.zt = a.zt + size_t(rr.t0 + i) * a.V;
+      rb.zd = a.zd + size_t(rr.d0 + i) * a.V;
+      rb.mt = s_m[i];
+      rb.st = float(1.0 / s_s[i]);
+      rb.md = s_m[G + 1 + i];
+      rb.sd = float(1.0 / s_s[G + 1 + i]);
+      load_chunk<VEC>(rb.zt, start, a.V, t, xt);
+      load_chunk<VEC>(rb.zd, start, a.V, t, xd);
+      double sm = 0.0;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        const int e = start + slot_offset<VEC>(j, t);
+        if (e < a.V) {
+          const float pp = exp2_hw((xt[j] - rb.mt) * a.c2) * rb.st;
+          const float qq = exp2_hw((xd[j] - rb.md) * a.c2) * rb.sd;
+          sm += double(fminf(pp, qq));
+        }
+      }
+      sm = block_sum_f64(sm, s_d);
+      if (t == 0) a.ws.jbeta[size_t(rr.d0 + i) * a.nch + c] = sm;
+    }
   }
 }
 
@@ -1054,7 +1138,7 @@ __device__ __forceinline__ void draw_pick_rest(const VerifyArgs& a, const DrawRo
     mg = 0.0;
   }
   if (t == 0) {
-    a.out[b * (a.G + 1) + pos] = pick;
+    a.out[req_rows(a, b).t0 + pos] = pick;
     if (a.margin) a.margin[b] = float(mg);
   }
 }
@@ -1114,6 +1198,15 @@ __global__ __launch_bounds__(VT) void vb_draw_pick(VerifyArgs a) {
   __shared__ double s_sub[VEC ? PICK_FAST_NCH * NSUB : 1];
   __shared__ int s_done;
   const int b = blockIdx.x, t = threadIdx.x;
+  const ReqRows rr = req_rows(a, b);
+  if (!rr.ok) return;
+  if (a.beta && t < rr.G) {
+    // confidence label of drafted position t: its chunk sums in chunk order
+    const double* pb = a.ws.jbeta + size_t(rr.d0 + t) * a.nch;
+    double sm = 0.0;
+    for (int c = 0; c < a.nch; ++c) sm += pb[c];
+    a.beta[rr.d0 + t] = float(sm);
+  }
   // the job, this thread's chunk sum and the run sums are loaded together
   const DrawJob jb = a.ws.job[b];
   const double* cs = a.ws.jsum + size_t(b) * a.nch;
@@ -1166,7 +1259,7 @@ __global__ __launch_bounds__(VT) void vb_draw_pick(VerifyArgs a) {
           double mg = 0.0;
           const int pick = scan_run(a, r, resid, e0, bsub, tgt, mg);
           if (pick != INT32_MAX && t == 0) {
-            a.out[b * (a.G + 1) + pos] = pick;
+            a.out[rr.t0 + pos] = pick;
             if (a.margin) a.margin[b] = float(mg);
             s_done = 1;
           }
@@ -1179,7 +1272,7 @@ __global__ __launch_bounds__(VT) void vb_draw_pick(VerifyArgs a) {
       const int pick = sh.pick;
       if (pick != INT32_MAX) {
         if (t == 0) {
-          a.out[b * (a.G + 1) + pos] = pick;
+          a.out[rr.t0 + pos] = pick;
           if (a.margin) a.margin[b] = float(sh.mg);
         }
         return;
@@ -1222,13 +1315,15 @@ __global__ __launch_bounds__(VT) void vb_write_probs(VerifyArgs a) {
 static inline size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct VerifyLayout {
-  size_t cmax, carg, csum, ctv, cti, rmax, rarg, rsum, rkn, rki, rkp, job, jsum, jsub, total;
+  size_t cmax, carg, csum, ctv, cti, rmax, rarg, rsum, rkn, rki, rkp, job, jsum, jsub, jbeta, total;
 };
 
-static VerifyLayout verify_layout(int B, int G, int V, int top_k) {
+// n_trows target rows (B * (G + 1) without a row map), as many minus B draft rows
+static VerifyLayout verify_layout(int B, int n_trows, int V, int top_k, bool beta) {
   VerifyLayout L{};
   const size_t nch = (size_t(V) + VCH - 1) / VCH;
-  const size_t rows = size_t(B) * (2 * G + 1);
+  const size_t rows = 2 * size_t(n_trows) - size_t(B);
+  const size_t n_draft = size_t(n_trows) - size_t(B);
   // record slots: row + workgroup; the top-k pass uses rows * nch workgroups,
   // the streaming pass at most max(rows * nch, STATS_GRID)
   const size_t rc = rows + (rows * nch > size_t(STATS_GRID) ? rows * nch : size_t(STATS_GRID));
@@ -1248,31 +1343,33 @@ static VerifyLayout verify_layout(int B, int G, int V, int top_k) {
   L.job = o; o += al(size_t(B) * sizeof(DrawJob));
   L.jsum = o; o += al(size_t(B) * nch * 8);
   L.jsub = o; o += al(size_t(B) * nch * NSUB * 8);
+  L.jbeta = o; o += al(beta && top_k == 0 ? n_draft * nch * 8 : 0);
   L.total = o;
   return L;
 }
 
-size_t verify_ws_bytes(int B, int G, int V, int top_k) {
+size_t verify_ws_bytes(int B, int n_trows, int V, int top_k, bool beta) {
   if (B <= 0) return 0;
-  return verify_layout(B, G, V, top_k).total;
+  return verify_layout(B, n_trows, V, top_k, beta).total;
 }
 
 hipError_t launch_verify(const float* zt, const float* zd, const int* dtok, const float* uni,
-                         int B, int G, int V, float temperature, int top_k, float top_p,
-                         int* tau, int* out, float* tprob, float* dprob, float* ratio, float* margin,
-                         void* ws, hipStream_t stream) {
+                         const int* row_cu, int B, int n_trows, int G, int V, float temperature, int top_k,
+                         float top_p, int* tau, int* out, float* tprob, float* dprob, float* ratio, float* margin,
+                         float* beta, void* ws, hipStream_t stream) {
   if (B == 0) return hipSuccess;
   const bool greedy = temperature == 0.0f;
   const int k = (!greedy && top_k > 0 && top_k < V) ? top_k : 0;
-  VerifyLayout L = verify_layout(B, G, V, k);
+  VerifyLayout L = verify_layout(B, n_trows, V, k, beta != nullptr);
   char* w = static_cast<char*>(ws);
   VerifyArgs a{};
   a.zt = zt; a.zd = zd; a.dtok = dtok; a.uni = uni;
   a.B = B; a.G = G; a.V = V;
   a.nch = (V + VCH - 1) / VCH;
-  a.n_trows = B * (G + 1);
-  const bool draft_rows = !greedy || dprob != nullptr;
-  a.n_rows = a.n_trows + (draft_rows && zd ? B * G : 0);
+  a.n_trows = n_trows;
+  a.row_cu = row_cu;
+  const bool draft_rows = !greedy || dprob != nullptr || beta != nullptr;
+  a.n_rows = a.n_trows + (draft_rows && zd ? n_trows - B : 0);
   a.T = greedy ? 1.0f : temperature;
   a.c2 = float(1.4426950408889634 / double(a.T));
   a.greedy = greedy;
@@ -1280,6 +1377,7 @@ hipError_t launch_verify(const float* zt, const float* zd, const int* dtok, cons
   a.top_p = greedy ? 1.0f : top_p;
   a.need_sum = (!greedy && k == 0) || (greedy && (tprob || dprob));
   a.tau = tau; a.out = out; a.tprob = tprob; a.dprob = dprob; a.ratio = ratio; a.margin = margin;
+  a.beta = beta;
   a.ws.cmax = reinterpret_cast<float*>(w + L.cmax);
   a.ws.carg = reinterpret_cast<int*>(w + L.carg);
   a.ws.csum = reinterpret_cast<double*>(w + L.csum);
@@ -1294,6 +1392,7 @@ hipError_t launch_verify(const float* zt, const float* zd, const int* dtok, cons
   a.ws.job = reinterpret_cast<DrawJob*>(w + L.job);
   a.ws.jsum = reinterpret_cast<double*>(w + L.jsum);
   a.ws.jsub = reinterpret_cast<double*>(w + L.jsub);
+  a.ws.jbeta = reinterpret_cast<double*>(w + L.jbeta);
 
   const bool vec = (V & 3) == 0;
   const long long work = (long long)a.n_rows * a.nch;

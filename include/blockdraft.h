@@ -192,6 +192,72 @@ int verify_block(const float* target_logits, const float* draft_logits,
                  float* accept_ratio, float* sample_margin,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * verify_block_ragged -- verify_block with a drafted length per request and
+ * the confidence label of every drafted position (DSpark tutorial,
+ * confidence-scheduled verification: the prefix scheduler picks a verify
+ * length per request; the label of a position is 1 - 1/2 |P - Q|_1, which
+ * equals sum_x min(P(x), Q(x))).
+ *
+ * Rows are packed: request b owns target rows row_cu[b] .. row_cu[b+1] - 1
+ * (G_b + 1 of them) and draft rows row_cu[b] - b .. row_cu[b+1] - b - 2
+ * (G_b), with 0 <= G_b <= G_max.  Each request is decided exactly as
+ * verify_block decides one request with G = G_b.
+ *
+ * target_logits device fp32 [n_target_rows, V]; draft_logits device fp32
+ *             [n_target_rows - B, V] (may be NULL when greedy and neither
+ *             draft_probs nor beta is asked for).
+ * row_cu      device int32 [B + 1], row_cu[0] = 0, nondecreasing by at least
+ *             one per request, row_cu[B] = n_target_rows; a request whose
+ *             entries break this (rows outside the arrays, G_b outside
+ *             [0, G_max]) gets tau = -1 and no other output.
+ * draft_tokens device int32 [n_target_rows - B]; uniforms device fp32
+ *             [n_target_rows, 2] (row-wise as in verify_block).
+ * tau         device int32 [B]; out_tokens device int32 [n_target_rows]:
+ *             per request d_1..d_tau, the replacement or extra token, -1.
+ * target_probs, draft_probs, accept_ratio, sample_margin: as verify_block,
+ *             on the packed rows; optional.
+ * beta        optional device fp32 [n_target_rows - B]: sum_x min(P, Q) of
+ *             each drafted position under the verification distributions
+ *             (greedy: 1 when the two lowest-index maxima agree, else 0).
+ * n_target_rows, G_max: host values; n_target_rows <= B * (G_max + 1).
+ * Supported: 0 <= top_k <= 64; G_max <= 64; V >= 1.
+ * ------------------------------------------------------------------------ */
+size_t verify_block_ragged_workspace_size(int32_t B, int32_t n_target_rows, int32_t G_max, int32_t V,
+                                          int32_t top_k, int32_t want_beta);
+
+int verify_block_ragged(const float* target_logits, const float* draft_logits,
+                        const int32_t* draft_tokens, const float* uniforms, const int32_t* row_cu,
+                        int32_t B, int32_t n_target_rows, int32_t G_max, int32_t V,
+                        float temperature, int32_t top_k, float top_p,
+                        int32_t* tau, int32_t* out_tokens,
+                        float* target_probs, float* draft_probs,
+                        float* accept_ratio, float* sample_margin, float* beta,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * prefix_schedule -- the hardware-aware prefix scheduler (DSpark tutorial,
+ * confidence-scheduled verification), host code.
+ *
+ * Request r has L_r candidate drafted positions with conditional survival
+ * probabilities survival[survival_cu[r] .. survival_cu[r+1] - 1] (values in
+ * [0, 1]).  The scheduler chooses verify lengths ell[r] in [0, L_r] that
+ * maximise Theta = tau * SPS(B) greedily: candidates in order of cumulative
+ * survival (highest first; ties to the lower request, then position), each
+ * extending its request's length by one, until the first one that does not
+ * raise Theta.  B = sum_r (ell[r] + 1) tokens; tau = sum_r (1 + sum over the
+ * verified positions of their cumulative survival); SPS is the linear
+ * interpolation of the table (sps_b[j], sps_v[j]) (any order; clamped to the
+ * end values outside it).
+ *
+ * survival, survival_cu [R + 1], sps_b, sps_v [n_sps], ell [R]: host memory,
+ * owned by the caller.  theta (host, may be NULL) receives Theta.
+ * Errors: BD_E_SHAPE for R < 0 or n_sps < 1, BD_E_NULL for missing arrays.
+ * ------------------------------------------------------------------------ */
+int prefix_schedule(const float* survival, const int32_t* survival_cu, int32_t R,
+                    const float* sps_b, const float* sps_v, int32_t n_sps,
+                    int32_t* ell, double* theta);
+
 #ifdef __cplusplus
 }
 #endif

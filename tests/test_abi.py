@@ -126,3 +126,39 @@ def test_workspace_sizes_are_monotone(lib):
 def test_product_path_has_no_fallback(tmp_path):
     with pytest.raises(RuntimeError):
         bd.load(str(tmp_path / "missing.so"))
+
+
+def _ragged(lib, **kw):
+    a = dict(zt=1 << 20, zd=1 << 20, dt=1 << 20, u=1 << 20, cu=1 << 20, B=2, N=7, Gm=4, V=100, T=1.0, k=0, p=1.0,
+             tau=1 << 20, out=1 << 20, beta=None, ws=1 << 20, wsb=1 << 30)
+    a.update(kw)
+    return lib.verify_block_ragged(a["zt"], a["zd"], a["dt"], a["u"], a["cu"], a["B"], a["N"], a["Gm"], a["V"],
+                                   F(a["T"]), a["k"], F(a["p"]), a["tau"], a["out"], None, None, None, None,
+                                   a["beta"], a["ws"], a["wsb"], None)
+
+
+def test_ragged_verify_validation_codes(lib):
+    assert _ragged(lib, cu=None) == bd.BD_E_NULL
+    assert _ragged(lib, zt=None) == bd.BD_E_NULL
+    assert _ragged(lib, zd=None) == bd.BD_E_NULL                    # sampling needs draft logits
+    assert _ragged(lib, T=0.0, zd=None, beta=1 << 20) == bd.BD_E_NULL  # labels need draft logits
+    assert _ragged(lib, N=1) == bd.BD_E_SHAPE                       # fewer target rows than requests
+    assert _ragged(lib, N=11) == bd.BD_E_SHAPE                      # more than B * (G_max + 1)
+    assert _ragged(lib, Gm=65, N=7) == bd.BD_E_UNSUPPORTED
+    assert _ragged(lib, k=65) == bd.BD_E_UNSUPPORTED
+    assert _ragged(lib, wsb=16) == bd.BD_E_WORKSPACE
+    # greedy without drafts at all: only target rows; B = 0 is a no-op
+    assert _ragged(lib, B=0, N=0) == bd.BD_OK
+
+
+def test_ragged_workspace_grows_with_labels(lib):
+    a = lib.verify_block_ragged_workspace_size(4, 40, 15, 151936, 0, 0)
+    b = lib.verify_block_ragged_workspace_size(4, 40, 15, 151936, 0, 1)
+    assert 0 < a < b
+    assert lib.verify_block_ragged_workspace_size(4, 3, 15, 100, 0, 0) == 0   # N < B
+
+
+def test_prefix_schedule_validation_codes(lib):
+    c = ctypes.c_void_p
+    assert lib.prefix_schedule(None, None, -1, None, None, 1, None, None) == bd.BD_E_SHAPE
+    assert lib.prefix_schedule(None, None, 1, None, None, 1, None, None) == bd.BD_E_NULL
