@@ -317,6 +317,7 @@ def next_rows(a, cfg, r, bd, torch, dev, stream, q, kb, vb, kc, vc, cache_base, 
                                                                    cfg.top_k, cfg.top_p, workspace=wsq), n=10)
         table_b.append(float(zt_q.shape[0]))
         table_v.append(1e6 / t)
+    ex["overlap"] = overlap_rounds(cfg, r, bd, torch, dev, q, kb, vb, zt, zd, dtok, uni)
     surv = [np.full(G, c, np.float32) for c in rng.uniform(0.6, 0.95, B)]
     t0 = time.perf_counter()
     ell, theta = bd.prefix_schedule(surv, table_b, table_v)
@@ -325,6 +326,42 @@ def next_rows(a, cfg, r, bd, torch, dev, stream, q, kb, vb, kc, vc, cache_base, 
                                  survival="per request constant c_r ~ U(0.6, 0.95) (seed 5), G positions",
                                  chosen_tokens=int(sum(ell) + B), theta=round(theta, 1), host_us=round(host_us, 1))
     return ex
+
+
+def overlap_rounds(cfg, r, bd, torch, dev, q, kb, vb, zt, zd, dtok, uni, rounds=20):
+    """Rounds chained three ways at the workload's shape (see
+    block_drafting_amd.runner): the host waiting for tau every round, the
+    commit on the device with tokens read one round late, and the chained
+    round replayed from a HIP graph.  Caches get room for the extra blocks
+    and random bf16 context (only their shape matters for timing)."""
+    from block_drafting_amd.runner import RoundRunner, layout_with_room
+    base, cap, T_cap = layout_with_room(r.ctx_len, cfg.K, 4 * rounds + 4)
+    kc = torch.randn((cfg.L, T_cap, cfg.n_kv, cfg.hd), device=dev, dtype=torch.bfloat16).view(torch.int16)
+    vc = torch.randn((cfg.L, T_cap, cfg.n_kv, cfg.hd), device=dev, dtype=torch.bfloat16).view(torch.int16)
+    i16 = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev)
+    inp = dict(h=i16(r.h_round_bits), w=i16(r.w_bits), gains=i16(r.k_norm_bits), q=q, kb=kb, vb=vb, zt=zt, zd=zd,
+               dtok=dtok, uni=uni)
+    run = RoundRunner(cfg, inp, kc, vc, torch.from_numpy(base).to(dev), r.ctx_len, cap, 4 * rounds + 4)
+    out = {}
+    run.run_chained(2)
+    run.reset()
+    for name, fn in (("synced", run.run_synced), ("chained", run.run_chained)):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn(rounds)
+        torch.cuda.synchronize()
+        out[f"{name}_ms_per_round"] = round((time.perf_counter() - t0) * 1e3 / rounds, 4)
+        run.reset()
+    run.capture()
+    run.reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run.run_graph(rounds)
+    torch.cuda.synchronize()
+    out["graph_ms_per_round"] = round((time.perf_counter() - t0) * 1e3 / rounds, 4)
+    out["rounds"] = rounds
+    del kc, vc, run
+    return out
 
 
 def copy_calibration(torch, dev):

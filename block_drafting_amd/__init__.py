@@ -29,7 +29,7 @@ EXPORTS = (
     "draft_block_attn_workspace_size", "draft_block_attn",
     "verify_block_workspace_size", "verify_block",
     "verify_block_ragged_workspace_size", "verify_block_ragged",
-    "prefix_schedule",
+    "prefix_schedule", "commit_round",
 )
 
 
@@ -75,6 +75,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     L.verify_block_ragged_workspace_size.argtypes = [c_i32] * 6
     L.verify_block_ragged.restype = ctypes.c_int
     L.verify_block_ragged.argtypes = [c_p] * 5 + [c_i32] * 4 + [c_f, c_i32, c_f] + [c_p] * 7 + [c_p, c_sz, c_p]
+    L.commit_round.restype = ctypes.c_int
+    L.commit_round.argtypes = [c_p, c_i32, c_i32, c_p, c_p, c_p, c_p, c_p]
     L.prefix_schedule.restype = ctypes.c_int
     L.prefix_schedule.argtypes = [c_p, c_p, c_i32, c_p, c_p, c_i32, c_p, c_p]
     if path is None:
@@ -247,6 +249,17 @@ def verify_block_ragged(target_logits, draft_logits, draft_tokens, uniforms, row
     return tau, out_tokens
 
 
+def commit_round(tau, K: int, ctx_len, row_pos0=None, cap=None, done=None, stream=None):
+    """Commit a round on the device: ctx_len += tau + 1 in place (tau >= 0),
+    row_pos0 = the new ctx_len, done = tau < 0 or ctx_len + K > cap."""
+    for n, t in (("tau", tau), ("ctx_len", ctx_len), ("row_pos0", row_pos0), ("cap", cap), ("done", done)):
+        _typed(t, torch.int32, n)
+    st = load().commit_round(_ptr(tau), tau.shape[0], int(K), _ptr(ctx_len), _ptr(row_pos0), _ptr(cap), _ptr(done),
+                             _stream(stream))
+    _check(st)
+    return ctx_len
+
+
 def prefix_schedule(survival, sps_b, sps_v):
     """Host prefix scheduler. survival: list of per-request sequences of
     conditional survival probabilities; (sps_b, sps_v) the measured
@@ -269,6 +282,6 @@ def prefix_schedule(survival, sps_b, sps_v):
     return [int(x) for x in ell[:R]], float(theta.value)
 
 
-__all__ = ["inject_kv", "draft_block_attn", "verify_block", "verify_block_ragged", "prefix_schedule",
+__all__ = ["inject_kv", "draft_block_attn", "verify_block", "verify_block_ragged", "prefix_schedule", "commit_round",
            "inject_kv_workspace_size", "draft_block_attn_workspace_size", "verify_block_workspace_size",
            "verify_block_ragged_workspace_size", "BlockDraftError", "load", "last_error", "lib_path", "EXPORTS"]

@@ -214,6 +214,15 @@ int verify_block_ragged(const float* target_logits, const float* draft_logits,
                   "verify_block_ragged");
 }
 
+// ---------------------------------------------------------------- commit_round
+int commit_round(const int32_t* tau, int32_t B, int32_t K, int32_t* ctx_len, int32_t* row_pos0,
+                 const int32_t* cap, int32_t* done, hipStream_t stream) {
+  if (B < 0 || K < 0) return fail(BD_E_SHAPE, "commit_round: need B >= 0 and K >= 0 (got B=%d K=%d)", B, K);
+  if (B > 0 && (!tau || !ctx_len)) return fail(BD_E_NULL, "commit_round: tau and ctx_len are required");
+  if (B == 0) return ok();
+  return launched(bd::launch_commit(tau, B, K, ctx_len, row_pos0, cap, done, stream), "commit_round");
+}
+
 // ---------------------------------------------------------------- prefix_schedule
 int prefix_schedule(const float* survival, const int32_t* survival_cu, int32_t R, const float* sps_b,
                     const float* sps_v, int32_t n_sps, int32_t* ell, double* theta) {

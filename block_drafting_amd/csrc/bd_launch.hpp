@@ -27,6 +27,9 @@ hipError_t launch_verify(const float* zt, const float* zd, const int* dtok, cons
                          float top_p, int* tau, int* out, float* tprob, float* dprob, float* ratio, float* margin,
                          float* beta, void* ws, hipStream_t stream);
 
+hipError_t launch_commit(const int32_t* tau, int B, int K, int32_t* ctx_len, int32_t* row_pos0, const int32_t* cap,
+                         int32_t* done, hipStream_t stream);
+
 // prefix scheduler (host)
 int prefix_schedule(const float* surv, const int32_t* surv_cu, int R, const float* sps_b, const float* sps_v,
                     int n_sps, int32_t* ell, double* theta);

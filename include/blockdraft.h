@@ -236,6 +236,25 @@ int verify_block_ragged(const float* target_logits, const float* draft_logits,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * commit_round -- the bookkeeping between two rounds, on the device
+ * (DFlash/Spec V2 blog, A7: overlap scheduling, so the host never waits for
+ * the device between rounds).
+ *
+ * For each request b with tau[b] >= 0: ctx_len[b] += tau[b] + 1 (the
+ * accepted drafts plus the replacement / extra token are committed) and
+ * row_pos0[b] = the new ctx_len[b] (the next round's K injected rows start
+ * there).  tau[b] < 0 leaves ctx_len[b] as it is.  done[b] = 1 when
+ * tau[b] < 0 or when the next K rows would pass cap[b] (ctx_len + K > cap),
+ * else 0.
+ *
+ * tau device int32 [B]; ctx_len device int32 [B], updated in place;
+ * row_pos0, cap, done device int32 [B] or NULL (cap NULL: no limit).
+ * Errors: BD_E_SHAPE for B < 0 or K < 0, BD_E_NULL without tau / ctx_len.
+ * ------------------------------------------------------------------------ */
+int commit_round(const int32_t* tau, int32_t B, int32_t K, int32_t* ctx_len, int32_t* row_pos0,
+                 const int32_t* cap, int32_t* done, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * prefix_schedule -- the hardware-aware prefix scheduler (DSpark tutorial,
  * confidence-scheduled verification), host code.
  *

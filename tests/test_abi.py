@@ -162,3 +162,9 @@ def test_prefix_schedule_validation_codes(lib):
     c = ctypes.c_void_p
     assert lib.prefix_schedule(None, None, -1, None, None, 1, None, None) == bd.BD_E_SHAPE
     assert lib.prefix_schedule(None, None, 1, None, None, 1, None, None) == bd.BD_E_NULL
+
+
+def test_commit_round_validation_codes(lib):
+    assert lib.commit_round(None, 4, 16, None, None, None, None, None) == bd.BD_E_NULL
+    assert lib.commit_round(None, -1, 16, None, None, None, None, None) == bd.BD_E_SHAPE
+    assert lib.commit_round(None, 0, 16, None, None, None, None, None) == bd.BD_OK
