@@ -318,6 +318,8 @@ def next_rows(a, cfg, r, bd, torch, dev, stream, q, kb, vb, kc, vc, cache_base, 
         table_b.append(float(zt_q.shape[0]))
         table_v.append(1e6 / t)
     ex["overlap"] = overlap_rounds(cfg, r, bd, torch, dev, q, kb, vb, zt, zd, dtok, uni)
+    ex["inject_prefill"] = inject_prefill(cfg, r, bd, torch, dev, stream)
+    ex["draft_pass"] = draft_pass(cfg, r, bd, torch, dev, stream, kc, vc, cache_base, ctx_len, max_ctx)
     surv = [np.full(G, c, np.float32) for c in rng.uniform(0.6, 0.95, B)]
     t0 = time.perf_counter()
     ell, theta = bd.prefix_schedule(surv, table_b, table_v)
@@ -326,6 +328,75 @@ def next_rows(a, cfg, r, bd, torch, dev, stream, q, kb, vb, kc, vc, cache_base, 
                                  survival="per request constant c_r ~ U(0.6, 0.95) (seed 5), G positions",
                                  chosen_tokens=int(sum(ell) + B), theta=round(theta, 1), host_us=round(host_us, 1))
     return ex
+
+
+def draft_pass(cfg, r, bd, torch, dev, stream, kc, vc, cache_base, ctx_len, max_ctx, d_model=4096, ffn=12288):
+    """One whole draft step against the block size (DFlash/Spec V2 blog: one
+    drafter forward yields the block): inject_kv of the round's B*K rows plus
+    draft_forward through the L drafter layers and the LM head, random bf16
+    weights of the Qwen3-8B drafter shape (hidden 4096, MLP 12288), the
+    round's filled caches and contexts."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(21)
+    rnd = lambda *s, std=1.0: (torch.randn(s, generator=g, device=dev) * std).to(torch.bfloat16).view(torch.int16)
+    one = lambda n: torch.ones(n, device=dev).to(torch.bfloat16).view(torch.int16)
+    nq, nkv, hd, L, V, B = cfg.n_q, cfg.n_kv, cfg.hd, cfg.L, cfg.V, cfg.B
+    layers = [dict(g_attn=one(d_model), w_qkv=rnd((nq + 2 * nkv) * hd, d_model, std=d_model ** -0.5), g_q=one(hd),
+                   g_k=one(hd), w_o=rnd(d_model, nq * hd, std=(nq * hd) ** -0.5), g_mlp=one(d_model),
+                   w_gu=rnd(2 * ffn, d_model, std=d_model ** -0.5), w_down=rnd(d_model, ffn, std=ffn ** -0.5))
+              for _ in range(L)]
+    gf = one(d_model)
+    lm = rnd(V, d_model, std=d_model ** -0.5)
+    i16 = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev)
+    w_kv, gains = i16(r.w_bits), i16(r.k_norm_bits)
+    out = {}
+    for K in (4, 8, 16):
+        x = rnd(B * K, d_model)
+        logits = torch.empty((B * K, V), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, bd.draft_forward_workspace_size(B, K, d_model, nq, nkv, hd, ffn, max_ctx, cfg.window)),
+                         dtype=torch.uint8, device=dev)
+        t_f = _time_us(torch, stream, lambda: bd.draft_forward(x, layers, gf, lm, kc, vc, cache_base, ctx_len, max_ctx,
+                                                               K, nq, nkv, ffn, cfg.window, cfg.rope_theta, cfg.rms_eps,
+                                                               logits=logits, workspace=ws), n=10)
+        h = rnd(B * K, cfg.d_in)
+        cu = torch.arange(0, (B + 1) * K, K, dtype=torch.int32, device=dev)
+        wsi = torch.empty(max(1, bd.inject_kv_workspace_size(B * K, cfg.d_in, L, nkv, hd)), dtype=torch.uint8,
+                          device=dev)
+        t_i = _time_us(torch, stream, lambda: bd.inject_kv(h, w_kv, gains, cu, ctx_len, cache_base, kc, vc,
+                                                           cfg.rope_theta, cfg.rms_eps, workspace=wsi), n=10)
+        out[f"K={K}"] = dict(forward_ms=round(t_f / 1e3, 3), inject_ms=round(t_i / 1e3, 3),
+                             draft_pass_ms=round((t_f + t_i) / 1e3, 3))
+    out["weights_gb"] = round((sum(sum(v.numel() for v in w.values()) for w in layers) + lm.numel() + gf.numel())
+                              * 2 / 1e9, 2)
+    del layers, lm
+    torch.cuda.empty_cache()
+    return out
+
+
+def inject_prefill(cfg, r, bd, torch, dev, stream):
+    """Immediate materialization of every request's context in one call
+    (M = sum of the context lengths), random bf16 hidden states on the device."""
+    M = int(r.ctx_len.astype(np.int64).sum())
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    h = torch.randn((M, cfg.d_in), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+    i16 = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev)
+    w, g = i16(r.w_bits), i16(r.k_norm_bits)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(r.ctx_len.astype(np.int64))]).astype(np.int32)).to(dev)
+    p0 = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
+    cb = torch.from_numpy(r.cache_base).to(dev)
+    kc = torch.empty((cfg.L, r.T_cap, cfg.n_kv, cfg.hd), dtype=torch.int16, device=dev)
+    vc = torch.empty_like(kc)
+    ws = torch.empty(max(1, bd.inject_kv_workspace_size(M, cfg.d_in, cfg.L, cfg.n_kv, cfg.hd)), dtype=torch.uint8,
+                     device=dev)
+    t = _time_us(torch, stream, lambda: bd.inject_kv(h, w, g, cu, p0, cb, kc, vc, cfg.rope_theta, cfg.rms_eps,
+                                                     workspace=ws), n=3, warm=1)
+    flops = 2.0 * M * cfg.d_in * cfg.n_out
+    out = dict(rows=M, per_call_ms=round(t / 1e3, 3), achieved_tflops=round(flops / t / 1e6, 1),
+               frac=round(flops / t / 1e6 / BF16_PEAK_TFLOPS, 4))
+    del h, kc, vc, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def overlap_rounds(cfg, r, bd, torch, dev, q, kb, vb, zt, zd, dtok, uni, rounds=20):

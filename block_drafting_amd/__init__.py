@@ -30,6 +30,7 @@ EXPORTS = (
     "verify_block_workspace_size", "verify_block",
     "verify_block_ragged_workspace_size", "verify_block_ragged",
     "prefix_schedule", "commit_round",
+    "draft_forward_workspace_size", "draft_forward",
 )
 
 
@@ -75,6 +76,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     L.verify_block_ragged_workspace_size.argtypes = [c_i32] * 6
     L.verify_block_ragged.restype = ctypes.c_int
     L.verify_block_ragged.argtypes = [c_p] * 5 + [c_i32] * 4 + [c_f, c_i32, c_f] + [c_p] * 7 + [c_p, c_sz, c_p]
+    L.draft_forward_workspace_size.restype = c_sz
+    L.draft_forward_workspace_size.argtypes = [c_i32] * 9
+    L.draft_forward.restype = ctypes.c_int
+    L.draft_forward.argtypes = ([c_p] + [c_i32] * 9 + [c_p] * 7 + [c_i64, c_i32, c_i32, c_f, c_f, c_p, c_p, c_sz,
+                                                                   c_p])
     L.commit_round.restype = ctypes.c_int
     L.commit_round.argtypes = [c_p, c_i32, c_i32, c_p, c_p, c_p, c_p, c_p]
     L.prefix_schedule.restype = ctypes.c_int
@@ -249,6 +255,44 @@ def verify_block_ragged(target_logits, draft_logits, draft_tokens, uniforms, row
     return tau, out_tokens
 
 
+FORWARD_WEIGHTS = ("g_attn", "w_qkv", "g_q", "g_k", "w_o", "g_mlp", "w_gu", "w_down")
+
+
+def draft_forward_workspace_size(B, K, d_model, n_q, n_kv, hd, ffn, max_ctx, window) -> int:
+    return int(load().draft_forward_workspace_size(B, K, d_model, n_q, n_kv, hd, ffn, max_ctx, window))
+
+
+def draft_forward(x_in, layers, final_norm, lm_head, k_cache, v_cache, cache_base, ctx_len, max_ctx: int, K: int,
+                  n_q: int, n_kv: int, ffn: int, window: int = 0, rope_theta: float = 1e6, rms_eps: float = 1e-6,
+                  logits=None, workspace=None, stream=None):
+    """One drafter forward over the block. x_in [B*K, d] bf16 bits; layers: list of
+    dicts of bf16 tensors keyed by FORWARD_WEIGHTS; k_cache / v_cache [L, T_cap,
+    n_kv, hd]. Returns fp32 logits [B*K, V]."""
+    M, d = x_in.shape
+    B = M // K
+    L_ = len(layers)
+    V = lm_head.shape[0]
+    _, T_cap, _, hd = k_cache.shape
+    _bf16(x_in, "x_in"); _bf16(lm_head, "lm_head"); _bf16(final_norm, "final_norm")
+    _typed(cache_base, torch.int64, "cache_base"); _typed(ctx_len, torch.int32, "ctx_len")
+    ptrs = (ctypes.c_void_p * max(1, 8 * L_))()
+    for l, w in enumerate(layers):
+        for j, name in enumerate(FORWARD_WEIGHTS):
+            _bf16(w[name], name)
+            ptrs[8 * l + j] = _ptr(w[name])
+    if logits is None:
+        logits = torch.empty((M, V), dtype=torch.float32, device=x_in.device)
+    _typed(logits, torch.float32, "logits")
+    need = draft_forward_workspace_size(B, K, d, n_q, n_kv, hd, ffn, max_ctx, window)
+    ws, nb = _workspace(need, workspace, x_in.device)
+    st = load().draft_forward(_ptr(x_in), B, K, d, L_, n_q, n_kv, hd, ffn, V, ctypes.cast(ptrs, ctypes.c_void_p),
+                              _ptr(final_norm), _ptr(lm_head), _ptr(k_cache), _ptr(v_cache), _ptr(cache_base),
+                              _ptr(ctx_len), T_cap, int(max_ctx), int(window), float(rope_theta), float(rms_eps),
+                              _ptr(logits), _ptr(ws), nb, _stream(stream))
+    _check(st)
+    return logits
+
+
 def commit_round(tau, K: int, ctx_len, row_pos0=None, cap=None, done=None, stream=None):
     """Commit a round on the device: ctx_len += tau + 1 in place (tau >= 0),
     row_pos0 = the new ctx_len, done = tau < 0 or ctx_len + K > cap."""
@@ -283,5 +327,6 @@ def prefix_schedule(survival, sps_b, sps_v):
 
 
 __all__ = ["inject_kv", "draft_block_attn", "verify_block", "verify_block_ragged", "prefix_schedule", "commit_round",
+           "draft_forward", "draft_forward_workspace_size", "FORWARD_WEIGHTS",
            "inject_kv_workspace_size", "draft_block_attn_workspace_size", "verify_block_workspace_size",
            "verify_block_ragged_workspace_size", "BlockDraftError", "load", "last_error", "lib_path", "EXPORTS"]

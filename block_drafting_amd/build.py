@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libblockdraft.so")
-SOURCES = ("api.hip", "inject.hip", "attn.hip", "verify.hip", "schedule.hip", "commit.hip")
+SOURCES = ("api.hip", "inject.hip", "attn.hip", "verify.hip", "schedule.hip", "commit.hip", "forward.hip")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -56,7 +56,8 @@ def build(jobs: int = 4, verbose: bool = True, out: str = LIB, build_dir: str = 
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(lambda s: _compile(s, build_dir, defines), srcs))
     tmp = out + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # rocBLAS: the library GEMMs of the draft forward
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, "-lrocblas"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

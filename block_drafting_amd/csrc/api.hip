@@ -214,6 +214,51 @@ int verify_block_ragged(const float* target_logits, const float* draft_logits,
                   "verify_block_ragged");
 }
 
+// ---------------------------------------------------------------- draft_forward
+size_t draft_forward_workspace_size(int32_t B, int32_t K, int32_t d_model, int32_t n_q, int32_t n_kv, int32_t hd,
+                                    int32_t ffn, int32_t max_ctx, int32_t window) {
+  if (B <= 0 || K <= 0 || d_model <= 0 || n_q <= 0 || n_kv <= 0 || hd <= 0 || ffn <= 0 || max_ctx < 0 || window < 0 ||
+      n_q % n_kv)
+    return 0;
+  return bd::forward_ws_bytes(B, K, d_model, n_q, n_kv, hd, ffn, max_ctx, window);
+}
+
+int draft_forward(const uint16_t* x_in, int32_t B, int32_t K, int32_t d_model, int32_t L, int32_t n_q, int32_t n_kv,
+                  int32_t hd, int32_t ffn, int32_t V, const uint16_t* const* layer_weights,
+                  const uint16_t* final_norm, const uint16_t* lm_head, const uint16_t* k_cache,
+                  const uint16_t* v_cache, const int64_t* cache_base, const int32_t* ctx_len, int64_t T_cap,
+                  int32_t max_ctx, int32_t window, float rope_theta, float rms_eps, float* logits, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || K < 1 || d_model < 1 || L < 0 || n_q < 1 || n_kv < 1 || ffn < 1 || V < 1 || max_ctx < 0 ||
+      window < 0 || T_cap < 0)
+    return fail(BD_E_SHAPE, "draft_forward: need B, L, max_ctx, window, T_cap >= 0 and K, d_model, n_q, n_kv, ffn, "
+                "V >= 1");
+  if (n_q % n_kv) return fail(BD_E_SHAPE, "draft_forward: n_q (%d) must be a multiple of n_kv (%d)", n_q, n_kv);
+  if (!(rope_theta > 0.f) || !(rms_eps >= 0.f))
+    return fail(BD_E_SHAPE, "draft_forward: need rope_theta > 0 and rms_eps >= 0");
+  if (hd != 64 && hd != 128) return fail(BD_E_UNSUPPORTED, "draft_forward: hd must be 64 or 128 (got %d)", hd);
+  if (K > 64 || (n_q / n_kv) * K > 128)
+    return fail(BD_E_UNSUPPORTED, "draft_forward: need K <= 64 and (n_q/n_kv)*K <= 128");
+  if (!x_in || !final_norm || !lm_head || !logits || !cache_base || !ctx_len || (L > 0 && (!layer_weights ||
+      !k_cache || !v_cache)))
+    return fail(BD_E_NULL, "draft_forward: a required pointer is NULL");
+  for (int i = 0; i < 8 * L; ++i)
+    if (!layer_weights[i]) return fail(BD_E_NULL, "draft_forward: layer weight %d of layer %d is NULL", i % 8, i / 8);
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(BD_E_UNSUPPORTED, "draft_forward: the caches must be 16-byte aligned");
+  const size_t need = draft_forward_workspace_size(B, K, d_model, n_q, n_kv, hd, ffn, max_ctx, window);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(BD_E_WORKSPACE, "draft_forward: workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (need > 0 && !aligned16(workspace)) return fail(BD_E_UNSUPPORTED, "draft_forward: workspace must be 16-byte aligned");
+  if (B == 0) return ok();
+  const hipError_t e = bd::launch_forward(x_in, B, K, d_model, L, n_q, n_kv, hd, ffn, V, layer_weights, final_norm,
+                                          lm_head, k_cache, v_cache, cache_base, ctx_len, T_cap, max_ctx, window,
+                                          rope_theta, rms_eps, logits, workspace, stream);
+  if (e == hipErrorUnknown) return fail(BD_E_LAUNCH, "draft_forward: a library GEMM failed");
+  return launched(e, "draft_forward");
+}
+
 // ---------------------------------------------------------------- commit_round
 int commit_round(const int32_t* tau, int32_t B, int32_t K, int32_t* ctx_len, int32_t* row_pos0,
                  const int32_t* cap, int32_t* done, hipStream_t stream) {

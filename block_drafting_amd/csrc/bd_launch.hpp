@@ -30,6 +30,13 @@ hipError_t launch_verify(const float* zt, const float* zd, const int* dtok, cons
 hipError_t launch_commit(const int32_t* tau, int B, int K, int32_t* ctx_len, int32_t* row_pos0, const int32_t* cap,
                          int32_t* done, hipStream_t stream);
 
+size_t forward_ws_bytes(int B, int K, int d, int n_q, int n_kv, int hd, int ffn, int max_ctx, int window);
+hipError_t launch_forward(const uint16_t* x_in, int B, int K, int d, int L, int n_q, int n_kv, int hd, int ffn,
+                          int V, const uint16_t* const* lw, const uint16_t* g_final, const uint16_t* w_lm,
+                          const uint16_t* kc, const uint16_t* vc, const int64_t* cache_base, const int32_t* ctx_len,
+                          int64_t T_cap, int max_ctx, int window, float rope_theta, float eps, float* logits,
+                          void* ws, hipStream_t stream);
+
 // prefix scheduler (host)
 int prefix_schedule(const float* surv, const int32_t* surv_cu, int R, const float* sps_b, const float* sps_v,
                     int n_sps, int32_t* ell, double* theta);

@@ -236,6 +236,45 @@ int verify_block_ragged(const float* target_logits, const float* draft_logits,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * draft_forward -- one drafter forward over the block (DFlash/Spec V2 blog,
+ * A2: the drafter's layers attend to the injected context plus the block,
+ * and one forward yields every block position).  Qwen3-style layers with any
+ * (e.g. random-init) weights, to measure a whole draft pass.
+ *
+ * Per layer l (layer_weights[8 l + 0..7], device bf16):
+ *   g_attn [d]; w_qkv [(n_q + 2 n_kv) hd, d] (rows: Q heads, K heads, V
+ *   heads); g_q [hd], g_k [hd] (per-head RMSNorm gains of Q and K);
+ *   w_o [d, n_q hd]; g_mlp [d]; w_gu [2 ffn, d] (gate rows, then up rows);
+ *   w_down [d, ffn].
+ *   xn = RMSNorm(x, g_attn); q, k, v = xn W_qkv^T; q, k per-head RMSNorm and
+ *   RoPE (pairs d, d + hd/2, angle (ctx_len[b] + i) theta^(-2d/hd)) at block
+ *   position i; a = draft_block_attn(q, k, v, layer l's caches) (no flags);
+ *   x += a W_o^T; xn = RMSNorm(x, g_mlp); x += (SiLU(gate) * up) W_down^T.
+ * logits = RMSNorm(x, final_norm) lm_head^T, fp32.  Intermediates and the
+ * residual stream are bf16 (fp32 arithmetic inside each step).  The GEMMs run
+ * in rocBLAS on the given stream (calls from several host threads are
+ * serialised); the rest in this library's kernels.
+ *
+ * x_in        device bf16 [B K, d]: the block rows' input hidden states.
+ * layer_weights host array of 8 L device pointers (may be NULL when L = 0).
+ * final_norm  device bf16 [d]; lm_head device bf16 [V, d].
+ * k_cache, v_cache device bf16 [L, T_cap, n_kv, hd] (filled by inject_kv);
+ * cache_base, ctx_len, max_ctx, window: as draft_block_attn.
+ * logits      device fp32 [B K, V].
+ * Supported: hd in {64, 128}; K <= 64; (n_q / n_kv) K <= 128.
+ * ------------------------------------------------------------------------ */
+size_t draft_forward_workspace_size(int32_t B, int32_t K, int32_t d_model, int32_t n_q, int32_t n_kv, int32_t hd,
+                                    int32_t ffn, int32_t max_ctx, int32_t window);
+
+int draft_forward(const uint16_t* x_in, int32_t B, int32_t K, int32_t d_model, int32_t L,
+                  int32_t n_q, int32_t n_kv, int32_t hd, int32_t ffn, int32_t V,
+                  const uint16_t* const* layer_weights, const uint16_t* final_norm, const uint16_t* lm_head,
+                  const uint16_t* k_cache, const uint16_t* v_cache, const int64_t* cache_base,
+                  const int32_t* ctx_len, int64_t T_cap, int32_t max_ctx, int32_t window,
+                  float rope_theta, float rms_eps, float* logits,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * commit_round -- the bookkeeping between two rounds, on the device
  * (DFlash/Spec V2 blog, A7: overlap scheduling, so the host never waits for
  * the device between rounds).

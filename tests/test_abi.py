@@ -168,3 +168,19 @@ def test_commit_round_validation_codes(lib):
     assert lib.commit_round(None, 4, 16, None, None, None, None, None) == bd.BD_E_NULL
     assert lib.commit_round(None, -1, 16, None, None, None, None, None) == bd.BD_E_SHAPE
     assert lib.commit_round(None, 0, 16, None, None, None, None, None) == bd.BD_OK
+
+
+def test_draft_forward_validation_codes(lib):
+    def fwd(**kw):
+        a = dict(x=1 << 20, B=2, K=4, d=64, L=0, nq=4, nkv=2, hd=64, ffn=128, V=100, lw=None, gf=1 << 20, lm=1 << 20,
+                 kc=1 << 20, vc=1 << 20, base=1 << 20, ctx=1 << 20, T=100, maxc=50, W=0, ws=1 << 20, wsb=1 << 30)
+        a.update(kw)
+        return lib.draft_forward(a["x"], a["B"], a["K"], a["d"], a["L"], a["nq"], a["nkv"], a["hd"], a["ffn"], a["V"],
+                                 a["lw"], a["gf"], a["lm"], a["kc"], a["vc"], a["base"], a["ctx"], a["T"], a["maxc"],
+                                 a["W"], F(1e6), F(1e-6), 1 << 20, a["ws"], a["wsb"], None)
+    assert fwd(x=None) == bd.BD_E_NULL
+    assert fwd(L=1) == bd.BD_E_NULL              # layer weights missing
+    assert fwd(nq=3) == bd.BD_E_SHAPE
+    assert fwd(hd=96) == bd.BD_E_UNSUPPORTED
+    assert fwd(K=65) == bd.BD_E_UNSUPPORTED
+    assert fwd(wsb=16) == bd.BD_E_WORKSPACE

@@ -146,3 +146,43 @@ def test_full_size_8b_round_sampled_rows():
         ev = rel_err(bits_to_f64(gv[l, slots]), ov_[l])
         say(f"  layer {l}: K rel err {ek:.2e}  V rel err {ev:.2e}")
         assert ek <= TOL and ev <= TOL
+
+
+def test_prefill_scale_materialization_sampled_rows():
+    """Immediate materialization of a whole context batch (NEXT row): every
+    request's context at once, M = sum of the 8B round's context lengths
+    (about 74k rows) in one call; the oracle checks 12 sampled rows."""
+    import block_drafting_amd as bd
+    cfg = wl.CONFIGS["qwen3-8b"]
+    r = wl.make_round(cfg, parts=("inject",), random_gains=True)
+    ctx = r.ctx_len.astype(np.int64)
+    M = int(ctx.sum())
+    row_cu = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)
+    pos0 = np.zeros(cfg.B, np.int32)
+    say(f"prefill-scale inject M={M}")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    h = torch.randn((M, cfg.d_in), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+    kc = torch.full((cfg.L, r.T_cap, cfg.n_kv, cfg.hd), SENTINEL, dtype=torch.int16, device="cuda")
+    vc = torch.full_like(kc, SENTINEL)
+    bd.inject_kv(h, cuda_bits(r.w_bits), cuda_bits(r.k_norm_bits), torch.from_numpy(row_cu).cuda(),
+                 torch.from_numpy(pos0).cuda(), torch.from_numpy(r.cache_base).cuda(), kc, vc, cfg.rope_theta,
+                 cfg.rms_eps)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    rows = np.sort(np.concatenate([[0, M - 1, int(row_cu[1]), int(row_cu[1]) - 1], rng.integers(0, M, 8)]))
+    b_of = np.searchsorted(row_cu, rows, side="right") - 1
+    p_of = (rows - row_cu[b_of]).astype(np.int32)
+    slots = r.cache_base[b_of] + p_of
+    hr = host_bits(h[torch.from_numpy(rows).cuda()])
+    gk, gv = host_bits(kc[:, torch.from_numpy(slots).cuda()]), host_bits(vc[:, torch.from_numpy(slots).cuda()])
+    ok = np.zeros((cfg.L, len(rows), cfg.n_kv, cfg.hd))
+    ov_ = np.zeros((cfg.L, len(rows), cfg.n_kv, cfg.hd))
+    oi.inject_kv(bits_to_f64(hr), bits_to_f64(r.w_bits), bits_to_f64(r.k_norm_bits),
+                 np.arange(len(rows) + 1, dtype=np.int32), p_of, np.arange(len(rows)) - p_of, ok, ov_, cfg.L,
+                 cfg.n_kv, cfg.hd, cfg.rope_theta, cfg.rms_eps)
+    for l in range(cfg.L):
+        ek = rel_err(bits_to_f64(gk[l]), ok[l])
+        ev = rel_err(bits_to_f64(gv[l]), ov_[l])
+        say(f"  layer {l}: K rel err {ek:.2e}  V rel err {ev:.2e}")
+        assert ek <= TOL and ev <= TOL
