@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="qwen3-8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the measurements of the variants (causal attention, ragged verify, scheduler, "
+                         "chained rounds, prefill, whole draft pass), e.g. under a profiler")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for HBM counter scaling)")
     return ap.parse_args()
@@ -207,8 +210,8 @@ def main():
                     peak=dom["peak"], unit=dom["unit"], frac=round(dom["frac"], 4),
                     traffic=dom["traffic"])
 
-    extras = next_rows(a, cfg, r, bd, torch, dev, stream, q, kb, vb, kc, vc, cache_base, ctx_len, max_ctx, zt,
-                       zd, dtok, uni, att_bytes)
+    extras = None if a.no_extras else next_rows(a, cfg, r, bd, torch, dev, stream, q, kb, vb, kc, vc, cache_base,
+                                                ctx_len, max_ctx, zt, zd, dtok, uni, att_bytes)
 
     # ---------------------------------------------------------------- CPU baseline
     cpu = None
