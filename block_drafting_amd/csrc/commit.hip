@@ -10,8 +10,11 @@
 // them, one round late, from an asynchronous copy.
 //
 // Per request: tau + 1 tokens are committed (the accepted drafts and the
-// replacement / extra token), so ctx_len += tau + 1, and the next round
-// injects its K rows at positions ctx_len .. ctx_len + K - 1.  A request
+// replacement / extra token), so ctx_len += tau + 1.  The next round first
+// materializes the K rows this round verified (the target's hidden states of
+// the block) at the block's positions, old ctx_len .. + K - 1, so row_pos0
+// takes the old ctx_len; the committed ones are then inside the context the
+// next round's attention reads, the others are overwritten a round later.  A request
 // whose verify reported tau = -1 (invalid metadata) is left unchanged and
 // flagged done, as is one whose next K rows would not fit its slots.
 #include "bd_common.hpp"
@@ -24,11 +27,11 @@ __global__ __launch_bounds__(256) void commit_kernel(const int32_t* tau, int B, 
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= B) return;
   const int t = tau[b];
-  int c = ctx_len[b];
+  const int c0 = ctx_len[b];
   const bool ok = t >= 0;
-  if (ok) c += t + 1;
+  const int c = ok ? c0 + t + 1 : c0;
   ctx_len[b] = c;
-  if (row_pos0) row_pos0[b] = c;
+  if (row_pos0) row_pos0[b] = c0;
   if (done) done[b] = (!ok || (cap && (long long)c + K > (long long)cap[b])) ? 1 : 0;
 }
 

@@ -16,8 +16,11 @@ round N with the device work.  Three ways to chain rounds:
     once in a HIP graph and replayed, which also removes the per-kernel launch
     work from the host.
 
-All three produce the same results (the kernels and their inputs are the
-same); the runner only marshals buffers and streams.  Every round verifies
+Each round first materializes the K rows the previous round verified at that
+block's positions (row_pos0 = the context length before the previous commit),
+then attends to the context including the committed ones.  All three produce
+the same results (the kernels and their inputs are the same); the runner only
+marshals buffers and streams.  Every round verifies
 the same logits, so tau repeats, while the contexts grow by tau + 1 per
 round: the caches are laid out with room for ``rounds`` more blocks.
 """
@@ -95,10 +98,9 @@ class RoundRunner:
             self._round(commit=False)
             tau = self.tau.cpu().numpy()             # waits for the round
             log.append((tau.copy(), self.out_tok.cpu().numpy()))
+            self.row_pos0.copy_(torch.from_numpy(ctx.copy()))   # the verified block's positions
             ctx = ctx + np.where(tau >= 0, tau + 1, 0).astype(np.int32)
-            c = torch.from_numpy(ctx)
-            self.ctx_len.copy_(c)
-            self.row_pos0.copy_(c)
+            self.ctx_len.copy_(torch.from_numpy(ctx))
         torch.cuda.synchronize()
         return log
 
@@ -145,8 +147,8 @@ class RoundRunner:
         return log
 
     def reset(self, ctx_h: np.ndarray = None):
-        """Back to the starting contexts (the caches keep what was written;
-        every round rewrites the rows it reads)."""
+        """Back to the starting contexts (the caches keep what was written:
+        restore them too for a bit-identical rerun)."""
         c = torch.from_numpy((self.ctx0 if ctx_h is None else ctx_h).astype(np.int32).copy())
         self.ctx_len.copy_(c)
         self.row_pos0.copy_(c)

@@ -281,8 +281,10 @@ int draft_forward(const uint16_t* x_in, int32_t B, int32_t K, int32_t d_model, i
  *
  * For each request b with tau[b] >= 0: ctx_len[b] += tau[b] + 1 (the
  * accepted drafts plus the replacement / extra token are committed) and
- * row_pos0[b] = the new ctx_len[b] (the next round's K injected rows start
- * there).  tau[b] < 0 leaves ctx_len[b] as it is.  done[b] = 1 when
+ * row_pos0[b] = ctx_len[b] before the update: the next round materializes the K
+ * rows this round verified at the block's positions (DFlash/Spec V2 blog, A7,
+ * immediate materialization), so the committed ones lie inside the context
+ * the next round's attention reads.  tau[b] < 0 leaves ctx_len[b] as it is.  done[b] = 1 when
  * tau[b] < 0 or when the next K rows would pass cap[b] (ctx_len + K > cap),
  * else 0.
  *

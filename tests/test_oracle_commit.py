@@ -10,7 +10,7 @@ def test_hand_worked_example():
     # tau 15 -> +16 and 4016 + 16 > 4030: done
     ctx, pos, done = oc.commit_round([2, 0, -1, 15], [100, 0, 50, 4000], 16, cap=[200, 16, 100, 4030])
     assert list(ctx) == [103, 1, 50, 4016]
-    assert list(pos) == [103, 1, 50, 4016]
+    assert list(pos) == [100, 0, 50, 4000]      # the verified block's first position
     assert list(done) == [0, 1, 1, 1]
 
 
