@@ -40,7 +40,7 @@ KERNEL_SOURCES = {
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="qwen3-8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -179,6 +179,7 @@ def main():
 
     tau_h = tau.cpu().numpy()
     committed = int((tau_h + 1).sum())
+    decisions = verify_diagnostics(cfg, bd, torch, dev, zt, zd, dtok, uni, ws_ver, tau_h)
     rounds_s = a.steps / elapsed
     ms_step = 1e3 * elapsed / a.steps
 
@@ -238,6 +239,7 @@ def main():
         "accepted_tok_s": round(rounds_s * committed, 1),
         "drafted_accepted_tok_s": round(rounds_s * int(tau_h.sum()), 1),
         "tokens_per_round": committed,
+        "verify_decisions": decisions,
         "roofline": roofline,
         "stages": [{k: (round(v, 4) if isinstance(v, float) and k != "traffic" else v) for k, v in s.items()}
                    for s in stages],
@@ -449,6 +451,28 @@ def copy_calibration(torch, dev):
     return {"bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 5}
 
 
+def verify_diagnostics(cfg, bd, torch, dev, zt, zd, dtok, uni, ws, tau_h):
+    """The histogram of tau over the batch, and the decisions that sat close
+    to a boundary (DSpine article, "tuning and memory": batched verification
+    can flip near-tied tokens): accept tests with |u - P/Q| within 1e-6 of
+    the ratio's scale, and draws whose target fell within 1e-9 of a CDF step.
+    One extra, untimed verify call with the ratio and margin outputs."""
+    B, G = cfg.B, cfg.G
+    ratio = torch.full((B, G), float("nan"), dtype=torch.float32, device=dev)
+    margin = torch.full((B,), float("nan"), dtype=torch.float32, device=dev)
+    bd.verify_block(zt, zd, dtok, uni, cfg.temperature, cfg.top_k, cfg.top_p, accept_ratio=ratio,
+                    sample_margin=margin, workspace=ws)
+    torch.cuda.synchronize()
+    rt, mg = ratio.cpu().numpy(), margin.cpu().numpy()
+    u = uni.cpu().numpy()[:, :G, 0]
+    taken = np.arange(G)[None, :] <= np.minimum(tau_h, G - 1)[:, None]  # tests the chain evaluated
+    close = taken & np.isfinite(rt) & (np.abs(u - rt) <= 1e-6 * np.maximum(1.0, np.abs(rt)))
+    hist = np.bincount(np.clip(tau_h, 0, G), minlength=G + 1)
+    return {"tau_hist": [int(x) for x in hist], "mean_tau": round(float(tau_h.mean()), 3),
+            "near_tie_accept_tests": int(close.sum()),
+            "near_tie_draws": int((np.isfinite(mg) & (mg <= 1e-9)).sum())}
+
+
 def cpu_baseline(cfg, r, kc, vc, h, w):
     """The oracle, untuned, on one full round of the same workload on the host
     cores: projection of the B*K rows, every layer's attention for every
@@ -484,11 +508,22 @@ def cpu_baseline(cfg, r, kc, vc, h, w):
     ov.verify(r.z_target, r.z_draft, r.draft_tokens, r.uniforms, cfg.temperature, cfg.top_k, cfg.top_p)
     t3 = time.perf_counter()
     total = t3 - t0
+    # the verification again with every thread pool held to one thread
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t4 = time.perf_counter()
+            ov.verify(r.z_target, r.z_draft, r.draft_tokens, r.uniforms, cfg.temperature, cfg.top_k, cfg.top_p)
+            one = round(time.perf_counter() - t4, 3)
+    except Exception:  # pragma: no cover
+        one = None
     return {"value": round(1.0 / total, 5), "unit": "rounds/s", "cores": int(threads), "kind": "oracle",
             "sample": f"one full {cfg.name} round (inject M={B * K}, {L} attention layers x {B} requests, "
                       f"verify of {B} requests)",
             "seconds": {"inject_kv": round(t1 - t0, 3), "draft_block_attn": round(t2 - t1, 3),
-                        "verify_block": round(t3 - t2, 3), "round": round(total, 3)}}
+                        "verify_block": round(t3 - t2, 3), "round": round(total, 3)},
+            "verify_block_one_core_s": one}
 
 
 if __name__ == "__main__":
