@@ -170,6 +170,40 @@ def test_full_size_27b_window_sampled_requests():
         assert np.abs(gl[b] - ol[0]).max() <= 1e-3
 
 
+def test_full_size_sweep_layer_sampled_requests():
+    """Batch 128 with lognormal contexts (median 2048, clipped to [256, 16384]):
+    short and long items share the schedule, the longest spanning many
+    workgroups; the oracle checks the shortest, the longest and two others."""
+    import block_drafting_amd as bd
+    cfg = wl.CONFIGS["sweep-b128"]
+    r = wl.make_round(cfg, parts=("attn",))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(13)
+    shape = (r.T_cap, cfg.n_kv, cfg.hd)
+    kc = torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+    vc = torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+    q, kb, vb = r.q_bits[0], r.k_blk_bits[0], r.v_blk_bits[0]
+    max_ctx = int(r.ctx_len.max())
+    say(f"full-size sweep-b128 layer, T_cap={r.T_cap} max ctx={max_ctx}")
+    lse = torch.full((cfg.B, cfg.K, cfg.n_q), -7.0, dtype=torch.float32, device="cuda")
+    out, lse = bd.draft_block_attn(cuda_bits(q), cuda_bits(kb), cuda_bits(vb), kc, vc,
+                                   torch.from_numpy(r.cache_base).cuda(), torch.from_numpy(r.ctx_len).cuda(),
+                                   max_ctx, 0, lse=lse)
+    torch.cuda.synchronize()
+    go, gl = bits_to_f64(host_bits(out)), lse.cpu().numpy()
+    assert np.isfinite(go).all() and np.isfinite(gl).all()
+    for b in sorted({int(np.argmin(r.ctx_len)), int(np.argmax(r.ctx_len)), 17, 90}):
+        sub = slice(b, b + 1)
+        s0, s1 = int(r.cache_base[b]), int(r.cache_base[b] + r.ctx_len[b])
+        oo, ol = oa.block_attn(bits_to_f64(q[sub]), bits_to_f64(kb[sub]), bits_to_f64(vb[sub]),
+                               bits_to_f64(host_bits(kc[s0:s1])), bits_to_f64(host_bits(vc[s0:s1])),
+                               np.array([0]), r.ctx_len[sub], 0)
+        e = rel_err(go[b], oo[0])
+        say(f"  request {b} ctx={r.ctx_len[b]} rel err {e:.2e}")
+        assert e <= TOL
+        assert np.abs(gl[b] - ol[0]).max() <= 1e-3
+
+
 def test_one_long_item_many_partials():
     """One request, one KV head, 20000-token context: the item spans many
     workgroups, so the merge combines many partial records."""

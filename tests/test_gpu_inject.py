@@ -113,13 +113,13 @@ def test_deterministic_run_to_run():
     assert a == b
 
 
-def test_full_size_8b_round_sampled_rows():
-    """M = 512 rows (B = 32, K = 16), d_in = 20480, 5 layers x 8 heads x 128:
-    the full-size projection on the GPU; the oracle checks 8 rows."""
+def _full_size_sampled_rows(name, rows):
+    """One round's projection at the configuration's full size on the GPU
+    (every row of every request); the oracle checks the sampled rows."""
     import block_drafting_amd as bd
-    cfg = wl.CONFIGS["qwen3-8b"]
+    cfg = wl.CONFIGS[name]
     r = wl.make_round(cfg, parts=("inject",), random_gains=True)
-    say(f"full-size qwen3-8b inject M={cfg.B * cfg.K}")
+    say(f"full-size {name} inject M={cfg.B * cfg.K} d_in={cfg.d_in}")
     T_cap = r.T_cap
     kc = torch.full((cfg.L, T_cap, cfg.n_kv, cfg.hd), SENTINEL, dtype=torch.int16, device="cuda")
     vc = torch.full((cfg.L, T_cap, cfg.n_kv, cfg.hd), SENTINEL, dtype=torch.int16, device="cuda")
@@ -127,25 +127,47 @@ def test_full_size_8b_round_sampled_rows():
                  torch.from_numpy(r.row_cu).cuda(), torch.from_numpy(r.row_pos0).cuda(),
                  torch.from_numpy(r.cache_base).cuda(), kc, vc, cfg.rope_theta, cfg.rms_eps)
     torch.cuda.synchronize()
-    gk, gv = host_bits(kc), host_bits(vc)
-    rows = np.array([0, 15, 16, 100, 257, 300, 498, 511])
+    rows = np.asarray(rows)
+    b_of = rows // cfg.K
+    j_of = rows % cfg.K
+    pos0 = (r.row_pos0[b_of] + j_of).astype(np.int32)
+    slots = torch.from_numpy(r.cache_base[b_of] + pos0).cuda()
+    gk, gv = host_bits(kc[:, slots]), host_bits(vc[:, slots])
     w = bits_to_f64(r.w_bits)
     h = bits_to_f64(r.h_round_bits[rows])
     g = bits_to_f64(r.k_norm_bits)
-    b_of = rows // cfg.K
-    j_of = rows % cfg.K
     row_cu = np.arange(len(rows) + 1, dtype=np.int32)
-    pos0 = (r.row_pos0[b_of] + j_of).astype(np.int32)
-    slots = r.cache_base[b_of] + pos0
     ok = np.zeros((cfg.L, len(rows), cfg.n_kv, cfg.hd))
     ov_ = np.zeros((cfg.L, len(rows), cfg.n_kv, cfg.hd))
     oi.inject_kv(h, w, g, row_cu, pos0, np.arange(len(rows)) - pos0, ok, ov_, cfg.L, cfg.n_kv, cfg.hd,
                  cfg.rope_theta, cfg.rms_eps)
     for l in range(cfg.L):
-        ek = rel_err(bits_to_f64(gk[l, slots]), ok[l])
-        ev = rel_err(bits_to_f64(gv[l, slots]), ov_[l])
+        ek = rel_err(bits_to_f64(gk[l]), ok[l])
+        ev = rel_err(bits_to_f64(gv[l]), ov_[l])
         say(f"  layer {l}: K rel err {ek:.2e}  V rel err {ev:.2e}")
         assert ek <= TOL and ev <= TOL
+
+
+def test_full_size_8b_round_sampled_rows():
+    """M = 512 rows (B = 32, K = 16), d_in = 20480, 5 layers x 8 heads x 128:
+    the wide 512-row tiles split over d_in; the oracle checks 8 rows."""
+    _full_size_sampled_rows("qwen3-8b", [0, 15, 16, 100, 257, 300, 498, 511])
+
+
+def test_full_size_4b_round_all_rows():
+    """Batch 1 (M = 16, d_in = 12800): the small-M, weight-bound tiles; the
+    oracle checks every row."""
+    _full_size_sampled_rows("qwen3-4b", list(range(16)))
+
+
+def test_full_size_27b_round_sampled_rows():
+    """Batch 8 (M = 128, d_in = 25600, 524 MB of weights)."""
+    _full_size_sampled_rows("27b-long", [0, 1, 31, 64, 77, 127])
+
+
+def test_full_size_sweep_round_sampled_rows():
+    """Batch 128 (M = 2048: four 512-row tiles of the wide kernel)."""
+    _full_size_sampled_rows("sweep-b128", [0, 511, 512, 1000, 1535, 1536, 2047])
 
 
 def test_prefill_scale_materialization_sampled_rows():

@@ -263,3 +263,13 @@ def test_full_size_greedy_27b():
     o = ov.verify(r.z_target, None, r.draft_tokens, r.uniforms, 0.0)
     g = run_gpu(r.z_target, None, r.draft_tokens, None, 0.0)
     compare(o, g, r.uniforms, greedy=True, label="27b-long")
+
+
+def test_full_size_greedy_4b():
+    """Batch 1, 15 drafted tokens over the full vocabulary, greedy."""
+    say("full-size 4b verify")
+    r = wl.make_round(wl.CONFIGS["qwen3-4b"], parts=("verify",))
+    o = ov.verify(r.z_target, None, r.draft_tokens, r.uniforms, 0.0)
+    g = run_gpu(r.z_target, None, r.draft_tokens, None, 0.0)
+    compare(o, g, r.uniforms, greedy=True, label="qwen3-4b")
+    say(f"tau {g['tau']}")
