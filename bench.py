@@ -78,7 +78,7 @@ def main():
     a = parse()
     if a.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {a.gpus} is not supported "
-              "(the path shards by request, see the design notes)", file=sys.stderr)
+              "(the path would shard by request: one process per GPU over its own requests)", file=sys.stderr)
         sys.exit(2)
     import torch
     import workloads as wl
@@ -498,16 +498,23 @@ def cpu_baseline(cfg, r, kc, vc, h, w):
     vb = [f64(r.v_blk_bits[l]) for l in range(L)]
     k_o = np.zeros((L, r.T_cap, cfg.n_kv, cfg.hd))
     v_o = np.zeros((L, r.T_cap, cfg.n_kv, cfg.hd))
-    t0 = time.perf_counter()
-    oi.inject_kv(hh, ww, gg, r.row_cu, r.row_pos0, r.cache_base, k_o, v_o, L, cfg.n_kv, cfg.hd,
-                 cfg.rope_theta, cfg.rms_eps)
-    t1 = time.perf_counter()
-    for l in range(L):
-        oa.block_attn(q[l], kb[l], vb[l], caches[l][0], caches[l][1], r.cache_base, r.ctx_len, cfg.window)
-    t2 = time.perf_counter()
-    ov.verify(r.z_target, r.z_draft, r.draft_tokens, r.uniforms, cfg.temperature, cfg.top_k, cfg.top_p)
-    t3 = time.perf_counter()
-    total = t3 - t0
+    # whole rounds until about 10 s of host work (at most 8 rounds)
+    secs = np.zeros(3)
+    n = 0
+    while n < 8 and (n == 0 or secs.sum() < 10.0):
+        t0 = time.perf_counter()
+        oi.inject_kv(hh, ww, gg, r.row_cu, r.row_pos0, r.cache_base, k_o, v_o, L, cfg.n_kv, cfg.hd,
+                     cfg.rope_theta, cfg.rms_eps)
+        t1 = time.perf_counter()
+        for l in range(L):
+            oa.block_attn(q[l], kb[l], vb[l], caches[l][0], caches[l][1], r.cache_base, r.ctx_len, cfg.window)
+        t2 = time.perf_counter()
+        ov.verify(r.z_target, r.z_draft, r.draft_tokens, r.uniforms, cfg.temperature, cfg.top_k, cfg.top_p)
+        t3 = time.perf_counter()
+        secs += (t1 - t0, t2 - t1, t3 - t2)
+        n += 1
+    secs /= n
+    total = float(secs.sum())
     # the verification again with every thread pool held to one thread
     one = None
     try:
@@ -519,10 +526,10 @@ def cpu_baseline(cfg, r, kc, vc, h, w):
     except Exception:  # pragma: no cover
         one = None
     return {"value": round(1.0 / total, 5), "unit": "rounds/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one full {cfg.name} round (inject M={B * K}, {L} attention layers x {B} requests, "
-                      f"verify of {B} requests)",
-            "seconds": {"inject_kv": round(t1 - t0, 3), "draft_block_attn": round(t2 - t1, 3),
-                        "verify_block": round(t3 - t2, 3), "round": round(total, 3)},
+            "sample": f"{n} full {cfg.name} rounds (each: inject M={B * K}, {L} attention layers x {B} "
+                      f"requests, verify of {B} requests); seconds are per round",
+            "seconds": {"inject_kv": round(float(secs[0]), 3), "draft_block_attn": round(float(secs[1]), 3),
+                        "verify_block": round(float(secs[2]), 3), "round": round(total, 3)},
             "verify_block_one_core_s": one}
 
 
