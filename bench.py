@@ -77,7 +77,7 @@ def read_traffic(call: str):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {a.gpus} is not supported "
+        print(f"bench.py: the benchmark runs on one GPU only; --gpus {a.gpus} is not supported "
               "(the path would shard by request: one process per GPU over its own requests)", file=sys.stderr)
         sys.exit(2)
     import torch
