@@ -31,6 +31,7 @@ EXPORTS = (
     "verify_block_ragged_workspace_size", "verify_block_ragged",
     "prefix_schedule", "commit_round",
     "draft_forward_workspace_size", "draft_forward",
+    "select_block_workspace_size", "select_block",
 )
 
 
@@ -83,6 +84,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                                                    c_p])
     L.commit_round.restype = ctypes.c_int
     L.commit_round.argtypes = [c_p, c_i32, c_i32, c_p, c_p, c_p, c_p, c_p]
+    L.select_block_workspace_size.restype = c_sz
+    L.select_block_workspace_size.argtypes = [c_i32] * 3
+    L.select_block.restype = ctypes.c_int
+    L.select_block.argtypes = [c_p] * 4 + [c_i32] * 4 + [c_p] * 3 + [c_p, c_sz, c_p]
     L.prefix_schedule.restype = ctypes.c_int
     L.prefix_schedule.argtypes = [c_p, c_p, c_i32, c_p, c_p, c_i32, c_p, c_p]
     if path is None:
@@ -294,14 +299,43 @@ def draft_forward(x_in, layers, final_norm, lm_head, k_cache, v_cache, cache_bas
 
 
 def commit_round(tau, K: int, ctx_len, row_pos0=None, cap=None, done=None, stream=None):
-    """Commit a round on the device: ctx_len += tau + 1 in place (tau >= 0),
-    row_pos0 = the new ctx_len, done = tau < 0 or ctx_len + K > cap."""
+    """Commit a round on the device: row_pos0 = ctx_len before the update
+    (where the next round materializes this round's block), then
+    ctx_len += tau + 1 in place (tau >= 0); done = tau < 0 or ctx_len + K > cap."""
     for n, t in (("tau", tau), ("ctx_len", ctx_len), ("row_pos0", row_pos0), ("cap", cap), ("done", done)):
         _typed(t, torch.int32, n)
     st = load().commit_round(_ptr(tau), tau.shape[0], int(K), _ptr(ctx_len), _ptr(row_pos0), _ptr(cap), _ptr(done),
                              _stream(stream))
     _check(st)
     return ctx_len
+
+
+def select_block_workspace_size(B, G, V) -> int:
+    return int(load().select_block_workspace_size(B, G, V))
+
+
+def select_block(logits, anchor, trans_prev, trans_next, tokens=None, scores=None, candidates=None, workspace=None,
+                 stream=None):
+    """Choose the G drafted tokens of each request through the transition
+    cache. logits fp32 [B, G, V]; anchor int32 [B]; trans_prev / trans_next
+    bf16 bits [V, r]. Returns tokens int32 [B, G] (scores fp32 [B, G] and
+    candidates int32 [B, G, 16] are filled when given)."""
+    B, G, V = logits.shape
+    r = trans_prev.shape[1]
+    dev = logits.device
+    _typed(logits, torch.float32, "logits")
+    _typed(anchor, torch.int32, "anchor")
+    _bf16(trans_prev, "trans_prev")
+    _bf16(trans_next, "trans_next")
+    _typed(scores, torch.float32, "scores")
+    _typed(candidates, torch.int32, "candidates")
+    if tokens is None:
+        tokens = torch.empty((B, G), dtype=torch.int32, device=dev)
+    ws, nb = _workspace(select_block_workspace_size(B, G, V), workspace, dev)
+    st = load().select_block(_ptr(logits), _ptr(anchor), _ptr(trans_prev), _ptr(trans_next), B, G, V, r,
+                             _ptr(tokens), _ptr(scores), _ptr(candidates), _ptr(ws), nb, _stream(stream))
+    _check(st)
+    return tokens
 
 
 def prefix_schedule(survival, sps_b, sps_v):
@@ -329,4 +363,4 @@ def prefix_schedule(survival, sps_b, sps_v):
 __all__ = ["inject_kv", "draft_block_attn", "verify_block", "verify_block_ragged", "prefix_schedule", "commit_round",
            "draft_forward", "draft_forward_workspace_size", "FORWARD_WEIGHTS",
            "inject_kv_workspace_size", "draft_block_attn_workspace_size", "verify_block_workspace_size",
-           "verify_block_ragged_workspace_size", "BlockDraftError", "load", "last_error", "lib_path", "EXPORTS"]
+           "verify_block_ragged_workspace_size", "select_block", "select_block_workspace_size", "BlockDraftError", "load", "last_error", "lib_path", "EXPORTS"]

@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libblockdraft.so")
-SOURCES = ("api.hip", "inject.hip", "attn.hip", "verify.hip", "schedule.hip", "commit.hip", "forward.hip")
+SOURCES = ("api.hip", "inject.hip", "attn.hip", "verify.hip", "schedule.hip", "commit.hip", "forward.hip", "select.hip")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -259,6 +259,37 @@ int draft_forward(const uint16_t* x_in, int32_t B, int32_t K, int32_t d_model, i
   return launched(e, "draft_forward");
 }
 
+// ------------------------------------------------------------------ select_block
+size_t select_block_workspace_size(int32_t B, int32_t G, int32_t V) {
+  if (B <= 0 || G <= 0 || V < 16) return 0;
+  return bd::select_ws_bytes(B, G, V);
+}
+
+int select_block(const float* logits, const int32_t* anchor, const uint16_t* trans_prev, const uint16_t* trans_next,
+                 int32_t B, int32_t G, int32_t V, int32_t r, int32_t* tokens, float* scores, int32_t* candidates,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || G < 0) return fail(BD_E_SHAPE, "select_block: need B >= 0 and G >= 0 (got B=%d G=%d)", B, G);
+  if (V < 16 || V > 64 * 8192)
+    return fail(BD_E_UNSUPPORTED, "select_block: need 16 <= V <= 524288 (got %d)", V);
+  if (r < 8 || r > 256 || r % 8)
+    return fail(BD_E_UNSUPPORTED, "select_block: the rank r must be a multiple of 8 in [8, 256] (got %d)", r);
+  if (B == 0 || G == 0) return ok();
+  if (!logits || !anchor || !trans_prev || !trans_next || !tokens)
+    return fail(BD_E_NULL, "select_block: logits, anchor, trans_prev, trans_next and tokens are required");
+  if (!aligned16(trans_prev) || !aligned16(trans_next))
+    return fail(BD_E_UNSUPPORTED, "select_block: the transition tables must be 16-byte aligned");
+  if ((V & 3) == 0 && !aligned16(logits))
+    return fail(BD_E_UNSUPPORTED, "select_block: logits must be 16-byte aligned");
+  const size_t need = select_block_workspace_size(B, G, V);
+  if (!workspace || workspace_bytes < need)
+    return fail(BD_E_WORKSPACE, "select_block: workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(BD_E_UNSUPPORTED, "select_block: workspace must be 16-byte aligned");
+  return launched(bd::launch_select(logits, anchor, trans_prev, trans_next, B, G, V, r, tokens, scores, candidates,
+                                    workspace, stream),
+                  "select_block");
+}
+
 // ---------------------------------------------------------------- commit_round
 int commit_round(const int32_t* tau, int32_t B, int32_t K, int32_t* ctx_len, int32_t* row_pos0,
                  const int32_t* cap, int32_t* done, hipStream_t stream) {

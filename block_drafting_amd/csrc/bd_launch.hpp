@@ -37,6 +37,10 @@ hipError_t launch_forward(const uint16_t* x_in, int B, int K, int d, int L, int 
                           int64_t T_cap, int max_ctx, int window, float rope_theta, float eps, float* logits,
                           void* ws, hipStream_t stream);
 
+size_t select_ws_bytes(int B, int G, int V);
+hipError_t launch_select(const float* z, const int32_t* anchor, const uint16_t* E, const uint16_t* F, int B, int G,
+                         int V, int r, int32_t* tokens, float* scores, int32_t* cand, void* ws, hipStream_t stream);
+
 // prefix scheduler (host)
 int prefix_schedule(const float* surv, const int32_t* surv_cu, int R, const float* sps_b, const float* sps_v,
                     int n_sps, int32_t* ell, double* theta);

@@ -275,6 +275,42 @@ int draft_forward(const uint16_t* x_in, int32_t B, int32_t K, int32_t d_model, i
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * select_block -- the drafted tokens of a block chosen through a transition
+ * cache (DSpine article, "principle": 16 candidates per position, every
+ * pairing of adjacent positions' candidates scored at once into 16 x 16
+ * tables, then a left-to-right walk through the tables; DSpark tutorial,
+ * "semi-autoregressive generation": the previous token's influence is a
+ * low-rank offset to the position's logits).
+ *
+ * Score of token b at drafted position t after token a:
+ *   s_t(a, b) = logits[t][b] + sum_k trans_prev[a][k] * trans_next[b][k]
+ * (bf16 products added in fp32).  Candidates c_t: the 16 largest logits of
+ * position t (value desc, index asc).  Position 0's predecessor is anchor[b];
+ * table T_t[i][j] = s_t(c_{t-1}[i], c_t[j]).  Walk: j_0 = argmax_j s_0(anchor,
+ * c_0[j]), j_t = argmax_j T_t[j_{t-1}][j] (the lowest j on ties), token t =
+ * c_t[j_t].
+ *
+ * logits      device fp32 [B, G, V]: the drafter's base logits of the G
+ *             drafted positions (16-byte aligned when V % 4 == 0).
+ * anchor      device int32 [B]: the token before position 0 (an anchor
+ *             outside [0, V) gives that request tokens -1 and scores NaN).
+ * trans_prev, trans_next device bf16 [V, r], 16-byte aligned.
+ * tokens      device int32 [B, G] (out).
+ * scores      device fp32 [B, G] or NULL: the chosen table entries.
+ * candidates  device int32 [B, G, 16] or NULL: c_t.
+ * Workspace: select_block_workspace_size(B, G, V) bytes, 16-byte aligned.
+ * Supported: 16 <= V <= 524288; r a multiple of 8 in [8, 256].  NaN logits
+ * are undefined behaviour.
+ * Errors: BD_E_SHAPE (B, G < 0), BD_E_UNSUPPORTED (V, r, alignment), BD_E_NULL,
+ * BD_E_WORKSPACE, BD_E_LAUNCH.
+ * ------------------------------------------------------------------------ */
+size_t select_block_workspace_size(int32_t B, int32_t G, int32_t V);
+
+int select_block(const float* logits, const int32_t* anchor, const uint16_t* trans_prev, const uint16_t* trans_next,
+                 int32_t B, int32_t G, int32_t V, int32_t r, int32_t* tokens, float* scores, int32_t* candidates,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * commit_round -- the bookkeeping between two rounds, on the device
  * (DFlash/Spec V2 blog, A7: overlap scheduling, so the host never waits for
  * the device between rounds).

@@ -184,3 +184,24 @@ def test_draft_forward_validation_codes(lib):
     assert fwd(hd=96) == bd.BD_E_UNSUPPORTED
     assert fwd(K=65) == bd.BD_E_UNSUPPORTED
     assert fwd(wsb=16) == bd.BD_E_WORKSPACE
+
+
+def test_select_block_validation_codes(lib):
+    P = 1 << 20  # never dereferenced: every case fails before any launch
+
+    def sel(**kw):
+        a = dict(z=P, an=P, e=P, f=P, B=2, G=3, V=1000, r=64, tok=P, ws=P, wsb=1 << 30)
+        a.update(kw)
+        return lib.select_block(a["z"], a["an"], a["e"], a["f"], a["B"], a["G"], a["V"], a["r"], a["tok"], None, None,
+                                a["ws"], a["wsb"], None)
+    assert sel(B=-1) == bd.BD_E_SHAPE
+    assert sel(V=15) == bd.BD_E_UNSUPPORTED       # fewer tokens than candidates
+    assert sel(V=600000) == bd.BD_E_UNSUPPORTED
+    assert sel(r=12) == bd.BD_E_UNSUPPORTED       # rank not a multiple of 8
+    assert sel(r=512) == bd.BD_E_UNSUPPORTED
+    assert sel(tok=None) == bd.BD_E_NULL
+    assert sel(e=P + 2) == bd.BD_E_UNSUPPORTED    # tables must be 16-byte aligned
+    assert sel(wsb=16) == bd.BD_E_WORKSPACE
+    assert sel(B=0, z=None, tok=None) == bd.BD_OK  # nothing to do
+    assert lib.select_block_workspace_size(2, 3, 1000) > 0
+    assert lib.select_block_workspace_size(0, 3, 1000) == 0
