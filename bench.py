@@ -322,6 +322,7 @@ def next_rows(a, cfg, r, bd, torch, dev, stream, q, kb, vb, kc, vc, cache_base, 
                                                                    cfg.top_k, cfg.top_p, workspace=wsq), n=10)
         table_b.append(float(zt_q.shape[0]))
         table_v.append(1e6 / t)
+    ex["select_block"] = select_block(cfg, bd, torch, dev, stream, zd)
     ex["overlap"] = overlap_rounds(cfg, r, bd, torch, dev, q, kb, vb, zt, zd, dtok, uni)
     ex["inject_prefill"] = inject_prefill(cfg, r, bd, torch, dev, stream)
     ex["draft_pass"] = draft_pass(cfg, r, bd, torch, dev, stream, kc, vc, cache_base, ctx_len, max_ctx)
@@ -333,6 +334,25 @@ def next_rows(a, cfg, r, bd, torch, dev, stream, q, kb, vb, kc, vc, cache_base, 
                                  survival="per request constant c_r ~ U(0.6, 0.95) (seed 5), G positions",
                                  chosen_tokens=int(sum(ell) + B), theta=round(theta, 1), host_us=round(host_us, 1))
     return ex
+
+
+def select_block(cfg, bd, torch, dev, stream, zd, rank=256):
+    """Transition-cache selection of the drafted tokens (DSpine article,
+    "principle") over the round's draft logits [B, G, V] with random rank-256
+    bf16 transition factors. Algorithmic bytes: the logits, plus the 16 E rows
+    and 16 F rows each position's table reads, plus the outputs."""
+    B, G, V = zd.shape
+    g = torch.Generator(device=dev)
+    g.manual_seed(31)
+    E = (0.1 * torch.randn((V, rank), generator=g, device=dev)).to(torch.bfloat16).view(torch.int16)
+    F = (0.1 * torch.randn((V, rank), generator=g, device=dev)).to(torch.bfloat16).view(torch.int16)
+    anchor = torch.randint(0, V, (B,), generator=g, device=dev, dtype=torch.int32)
+    tok = torch.empty((B, G), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(1, bd.select_block_workspace_size(B, G, V)), dtype=torch.uint8, device=dev)
+    t = _time_us(torch, stream, lambda: bd.select_block(zd, anchor, E, F, tokens=tok, workspace=ws))
+    nbytes = 4.0 * B * G * V + 2.0 * B * G * 32 * rank * 2 + 4.0 * B * G
+    return dict(workload=f"B={B} G={G} V={V} r={rank}, the round's draft logits", per_call_us=round(t, 2),
+                achieved_gbs=round(nbytes / t / 1e3, 1), frac=round(nbytes / t / 1e3 / HBM_PEAK_GBS, 4))
 
 
 def draft_pass(cfg, r, bd, torch, dev, stream, kc, vc, cache_base, ctx_len, max_ctx, d_model=4096, ffn=12288):

@@ -51,14 +51,80 @@ struct SelArgs {
   int32_t* cand_out;      // [B][G][NC] or NULL
 };
 
-// the total order: larger value first, then lower index
-__device__ __forceinline__ bool sel_better(float v, int i, float w, int j) { return v > w || (v == w && i < j); }
+// the total order: larger value first, then lower index (no short circuit:
+// the compiler keeps it a select rather than a branch)
+__device__ __forceinline__ bool sel_better(float v, int i, float w, int j) {
+  return (v > w) | ((v == w) & (i < j));
+}
 
-// element of slot s (0..31) of thread t in a chunk starting at `start`
+// The value of lane l ^ J, without the LDS permute path: DPP row moves for
+// J <= 8 (quad permutations; 4 = half-mirror then reversed quad, 8 = mirror
+// then half-mirror), v_permlane16_swap / v_permlane32_swap for 16 and 32.
+template <int J>
+__device__ __forceinline__ int xor_lane(int x) {
+  if constexpr (J == 1) {
+    return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad_perm [1, 0, 3, 2]
+  } else if constexpr (J == 2) {
+    return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm [2, 3, 0, 1]
+  } else if constexpr (J == 4) {
+    const int y = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);  // row_half_mirror: l ^ 7
+    return __builtin_amdgcn_mov_dpp(y, 0x1B, 0xF, 0xF, false);          // quad_perm [3, 2, 1, 0]: ^ 3
+  } else if constexpr (J == 8) {
+    const int y = __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false);  // row_mirror: l ^ 15
+    return __builtin_amdgcn_mov_dpp(y, 0x141, 0xF, 0xF, false);         // row_half_mirror: ^ 7
+  } else if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return ((threadIdx.x >> 4) & 1) ? int(r[0]) : int(r[1]);
+  } else {
+    static_assert(J == 32, "xor distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (threadIdx.x & 32) ? int(r[0]) : int(r[1]);
+  }
+}
+template <int J>
+__device__ __forceinline__ float xor_lane(float x) {
+  return __int_as_float(xor_lane<J>(__float_as_int(x)));
+}
+// keep the better of this lane's (v, i) and lane l ^ J's
+template <int J>
+__device__ __forceinline__ void keep_better(float& v, int& i) {
+  const float v2 = xor_lane<J>(v);
+  const int i2 = xor_lane<J>(i);
+  const bool t = sel_better(v2, i2, v, i);
+  v = t ? v2 : v;
+  i = t ? i2 : i;
+}
+
+// element of slot s (0..SPT-1) of thread t in a chunk starting at `start`
 template <bool VEC>
 __device__ __forceinline__ int sel_slot(int start, int s, int t) {
   return VEC ? start + 4 * ((s >> 2) * ST + t) + (s & 3) : start + s * ST + t;
 }
+
+// one (value, index) per lane, sorted best first across the wave (bitonic
+// network over the lanes)
+template <int K, int J>
+__device__ __forceinline__ void bitonic_step(float& sv, int& si) {
+  const int lane = threadIdx.x & 63;
+  const float ov = xor_lane<J>(sv);
+  const int oi = xor_lane<J>(si);
+  const bool lower = (lane & J) == 0, desc = (lane & K) == 0;
+  // in a descending run the lower lane keeps the better of the pair
+  const bool take = (lower == desc) ? sel_better(ov, oi, sv, si) : sel_better(sv, si, ov, oi);
+  sv = take ? ov : sv;
+  si = take ? oi : si;
+}
+template <int K, int J>
+__device__ __forceinline__ void bitonic_merge(float& sv, int& si) {
+  bitonic_step<K, J>(sv, si);
+  if constexpr (J > 1) bitonic_merge<K, J / 2>(sv, si);
+}
+template <int K>
+__device__ __forceinline__ void bitonic_sort(float& sv, int& si) {
+  if constexpr (K > 2) bitonic_sort<K / 2>(sv, si);
+  bitonic_merge<K, K / 2>(sv, si);
+}
+__device__ __forceinline__ void wave_sort_best_first(float& sv, int& si) { bitonic_sort<64>(sv, si); }
 
 // ------------------------------------------------------------- chunk top-16
 template <bool VEC>
@@ -89,92 +155,86 @@ __global__ __launch_bounds__(ST) void sel_chunk_top(SelArgs a) {
       x[s] = e < a.V ? zr[e] : -INFINITY;
     }
   }
-  // this lane's best valid element
-  float bv = -INFINITY;
-  int bi = INT32_MAX;
+  // Elements past V read as -inf at their own index (>= V), so they rank
+  // after every real element: no bounds checks below.  This lane's best: its
+  // slots increase with the index, so the first strict maximum is the lowest
+  // index among equals.
+  float bv = x[0];
+  int bs = 0;
 #pragma unroll
-  for (int s = 0; s < SPT; ++s) {
-    const int e = sel_slot<VEC>(start, s, t);
-    if (e < a.V && sel_better(x[s], e, bv, bi)) { bv = x[s]; bi = e; }
+  for (int s = 1; s < SPT; ++s) {
+    const bool gt = x[s] > bv;
+    bv = gt ? x[s] : bv;
+    bs = gt ? s : bs;
   }
-  // the wave's lane maxima sorted best first (bitonic network over the lanes)
+  int bi = VEC ? start + 4 * ((bs >> 2) * ST + t) + (bs & 3) : start + bs * ST + t;
+  // the wave's lane maxima sorted best first
   float sv = bv;
   int si = bi;
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1)
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const float ov = __shfl_xor(sv, j);
-      const int oi = __shfl_xor(si, j);
-      const bool lower = (lane & j) == 0, desc = (lane & k) == 0;
-      // in a descending run the lower lane keeps the better of the pair
-      const bool take = (lower == desc) ? sel_better(ov, oi, sv, si) : sel_better(sv, si, ov, oi);
-      if (take) { sv = ov; si = oi; }
-    }
-  const float tv = __shfl(sv, NC - 1);
-  const int ti = __shfl(si, NC - 1);
-  // candidates: valid elements not worse than the threshold
-  int cnt = 0;
+  wave_sort_best_first(sv, si);
+  const float tv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), NC - 1));
+  const int ti = __builtin_amdgcn_readlane(si, NC - 1);
+  // candidates: elements not worse than the threshold, appended slot by slot
+  // (a ballot per slot; most slots hold none)
+  if (t == 0) s_over = 0;
+  __syncthreads();
+  int total = 0;
 #pragma unroll
   for (int s = 0; s < SPT; ++s) {
     const int e = sel_slot<VEC>(start, s, t);
-    cnt += (e < a.V && !sel_better(tv, ti, x[s], e)) ? 1 : 0;
-  }
-  int inc = cnt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(inc, o);
-    if (lane >= o) inc += y;
-  }
-  const int total = __shfl(inc, 63);
-  if (t == 0) s_over = 0;
-  __syncthreads();
-  if (lane == 0) s_n[w] = total;
-  if (total > WCAP) {
-    if (lane == 0) s_over = 1;
-  } else {
-    int pos = w * WCAP + inc - cnt;
-#pragma unroll
-    for (int s = 0; s < SPT; ++s) {
-      const int e = sel_slot<VEC>(start, s, t);
-      if (e < a.V && !sel_better(tv, ti, x[s], e)) { s_v[pos] = x[s]; s_i[pos] = e; ++pos; }
+    const bool p = (x[s] > tv) | ((x[s] == tv) & (e <= ti));
+    const unsigned long long m = __ballot(p);
+    if (m) {
+      const int below = __builtin_amdgcn_mbcnt_hi(unsigned(m >> 32), __builtin_amdgcn_mbcnt_lo(unsigned(m), 0u));
+      const int pos = total + below;
+      if (p && pos < WCAP) { s_v[w * WCAP + pos] = x[s]; s_i[w * WCAP + pos] = e; }
+      total += __popcll(m);
     }
   }
+  if (lane == 0) s_n[w] = total;
+  if (total > WCAP && lane == 0) s_over = 1;
   __syncthreads();
   float* ov = a.ctv + (size_t(row) * a.nch + c) * NC;
   int* oi = a.cti + (size_t(row) * a.nch + c) * NC;
   if (!s_over) {
-    // exact ranks among the kept candidates (keys are distinct: ranks are)
-    const int wt = t / WCAP, k = t % WCAP;
-    if (k < s_n[wt]) {
-      const float v = s_v[t];
-      const int i = s_i[t];
-      int rank = 0;
-      for (int w2 = 0; w2 < 4; ++w2)
-        for (int k2 = 0; k2 < s_n[w2]; ++k2) rank += sel_better(s_v[w2 * WCAP + k2], s_i[w2 * WCAP + k2], v, i) ? 1 : 0;
-      if (rank < NC) { ov[rank] = v; oi[rank] = i; }
+    // each wave sorts its candidates (one per lane, empty lanes last): its 16
+    // best are the first 16 lanes; then wave 0 sorts the four lists of 16
+    float v = -INFINITY;
+    int i = INT32_MAX;
+    if (lane < s_n[w]) { v = s_v[w * WCAP + lane]; i = s_i[w * WCAP + lane]; }
+    wave_sort_best_first(v, i);
+    __syncthreads();
+    if (lane < NC) { s_v[w * NC + lane] = v; s_i[w * NC + lane] = i; }
+    __syncthreads();
+    if (w == 0) {
+      v = s_v[lane];
+      i = s_i[lane];
+      wave_sort_best_first(v, i);
+      // fewer than NC elements in the chunk: the list ends in empty entries
+      if (lane < NC) {
+        const bool real = i < a.V;
+        ov[lane] = real ? v : -INFINITY;
+        oi[lane] = real ? i : INT32_MAX;
+      }
     }
-    // fewer than NC valid elements in the chunk: the rest of the list is empty
-    const int n = s_n[0] + s_n[1] + s_n[2] + s_n[3];
-    if (t >= n && t < NC) { ov[t] = -INFINITY; oi[t] = INT32_MAX; }
     return;
   }
   // exact selection, one element per round (ties beyond WCAP per wave)
-  unsigned taken = 0u;
+  unsigned long long taken = 0ull;
   for (int r = 0; r < NC; ++r) {
     float v = -INFINITY;
     int i = INT32_MAX;
 #pragma unroll
     for (int s = 0; s < SPT; ++s) {
       const int e = sel_slot<VEC>(start, s, t);
-      if (e < a.V && !(taken >> s & 1u) && sel_better(x[s], e, v, i)) { v = x[s]; i = e; }
+      if (!(taken >> s & 1ull) && sel_better(x[s], e, v, i)) { v = x[s]; i = e; }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float v2 = __shfl_xor(v, o);
-      const int i2 = __shfl_xor(i, o);
-      if (sel_better(v2, i2, v, i)) { v = v2; i = i2; }
-    }
+    keep_better<32>(v, i);
+    keep_better<16>(v, i);
+    keep_better<8>(v, i);
+    keep_better<4>(v, i);
+    keep_better<2>(v, i);
+    keep_better<1>(v, i);
     if (lane == 0) { s_rv[w] = v; s_ri[w] = i; }
     __syncthreads();
     v = s_rv[0];
@@ -182,55 +242,89 @@ __global__ __launch_bounds__(ST) void sel_chunk_top(SelArgs a) {
     for (int w2 = 1; w2 < 4; ++w2)
       if (sel_better(s_rv[w2], s_ri[w2], v, i)) { v = s_rv[w2]; i = s_ri[w2]; }
     __syncthreads();
-    if (t == 0) { ov[r] = i == INT32_MAX ? -INFINITY : v; oi[r] = i; }
+    if (t == 0) {
+      const bool real = i < a.V;
+      ov[r] = real ? v : -INFINITY;
+      oi[r] = real ? i : INT32_MAX;
+    }
 #pragma unroll
     for (int s = 0; s < SPT; ++s)
-      if (sel_slot<VEC>(start, s, t) == i) taken |= 1u << s;
+      if (sel_slot<VEC>(start, s, t) == i) taken |= 1ull << s;
   }
 }
 
 // ------------------------------------------------------------- tables
-// the NC best of a row's chunk lists (rank counting over nch * NC entries)
-__device__ __forceinline__ void merge_row(const SelArgs& a, int row, float* s_mv, int* s_mi, int* out_i,
-                                          float* out_v) {
-  const int n = a.nch * NC;
-  const float* gv = a.ctv + size_t(row) * n;
-  const int* gi = a.cti + size_t(row) * n;
-  for (int e = threadIdx.x; e < n; e += ST) { s_mv[e] = gv[e]; s_mi[e] = gi[e]; }
-  __syncthreads();
-  for (int e = threadIdx.x; e < n; e += ST) {
-    const float v = s_mv[e];
-    const int i = s_mi[e];
-    if (i == INT32_MAX) continue;  // empty list entry
-    int rank = 0;
-    for (int k = 0; k < n; ++k) rank += sel_better(s_mv[k], s_mi[k], v, i) ? 1 : 0;
-    if (rank < NC) {
-      out_i[rank] = i;
-      if (out_v) out_v[rank] = v;
+// The NC best of a row's chunk lists (each sorted best first, already in
+// LDS), merged by one wave: lane l holds the head of list l; each round the
+// best head is taken and its lane moves to its next entry.
+__device__ __forceinline__ void merge_lists(int nch, const float* s_mv, const int* s_mi, int* out_i, float* out_v) {
+  const int lane = threadIdx.x & 63;
+  int h = 0;  // this lane's position in its list
+  float hv = -INFINITY;
+  int hi = INT32_MAX;
+  if (lane < nch) { hv = s_mv[lane * NC]; hi = s_mi[lane * NC]; }
+  for (int r = 0; r < NC; ++r) {
+    float v = hv;
+    int i = hi;
+    keep_better<32>(v, i);
+    keep_better<16>(v, i);
+    keep_better<8>(v, i);
+    keep_better<4>(v, i);
+    keep_better<2>(v, i);
+    keep_better<1>(v, i);
+    if (lane == 0) {
+      out_i[r] = i;
+      if (out_v) out_v[r] = v;
+    }
+    if (hi == i && i != INT32_MAX) {  // indices are unique across the lists
+      ++h;
+      hv = h < NC ? s_mv[lane * NC + h] : -INFINITY;
+      hi = h < NC ? s_mi[lane * NC + h] : INT32_MAX;
     }
   }
-  __syncthreads();
 }
 
 __global__ __launch_bounds__(ST) void sel_table(SelArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char sel_lds[];
-  // [nch * NC] merge values and indices, then E rows [NC][r] and F rows [NC][r]
+  // [2][nch * NC] list values and indices, then E rows [NC][r] and F rows [NC][r]
   float* s_mv = reinterpret_cast<float*>(sel_lds);
-  int* s_mi = reinterpret_cast<int*>(s_mv + a.nch * NC);
-  uint16_t* s_E = reinterpret_cast<uint16_t*>(s_mi + a.nch * NC);
+  int* s_mi = reinterpret_cast<int*>(s_mv + 2 * a.nch * NC);
+  uint16_t* s_E = reinterpret_cast<uint16_t*>(s_mi + 2 * a.nch * NC);
   uint16_t* s_F = s_E + NC * a.r;
   __shared__ int s_prev[NC], s_cur[NC];
   __shared__ float s_z[NC];
   const int t = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int row = b * a.G + t;
-  merge_row(a, row, s_mv, s_mi, s_cur, s_z);
-  int n_prev = NC;
-  if (t > 0) {
-    merge_row(a, row - 1, s_mv, s_mi, s_prev, nullptr);
-  } else {
-    n_prev = 1;
-    if (tid == 0) s_prev[0] = a.anchor[b];
+  // the chunk lists of this position (first half of the buffers) and of the
+  // one before (second half) in one round of loads; wave 0 merges this
+  // position's, wave 1 the previous one's
+  const int n = a.nch * NC;
+  const int nrows = t > 0 ? 2 : 1;
+  {
+    constexpr int PER = 2 * 64 * NC / ST;  // at most 64 chunks per row
+    float bv[PER];
+    int bi[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + u * ST;
+      if (e < nrows * n) {
+        const size_t src = size_t(row - e / n) * n + e % n;
+        bv[u] = a.ctv[src];
+        bi[u] = a.cti[src];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + u * ST;
+      if (e < nrows * n) { s_mv[e] = bv[u]; s_mi[e] = bi[u]; }
+    }
   }
+  if (t == 0 && tid == 0) s_prev[0] = a.anchor[b];
+  __syncthreads();
+  const int n_prev = t > 0 ? NC : 1;
+  if (tid < 64) merge_lists(a.nch, s_mv, s_mi, s_cur, s_z);
+  else if (tid < 128 && t > 0) merge_lists(a.nch, s_mv + n, s_mi + n, s_prev, nullptr);
+  __syncthreads();
   if (tid < NC) {
     a.cand[size_t(row) * NC + tid] = s_cur[tid];
     if (a.cand_out) a.cand_out[size_t(row) * NC + tid] = s_cur[tid];
@@ -240,16 +334,30 @@ __global__ __launch_bounds__(ST) void sel_table(SelArgs a) {
   // outside the vocabulary reads as a zero row; its request is flagged by
   // sel_walk)
   const int pr = a.r / 8;  // 16-byte pieces per row
-  for (int e = tid; e < 2 * NC * pr; e += ST) {
-    const int which = e / (NC * pr), rr = (e / pr) % NC, p = e % pr;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (which == 0) {
-      const int tok = s_prev[rr < n_prev ? rr : 0];
-      if (tok >= 0 && tok < a.V) v = *reinterpret_cast<const uint4*>(a.E + size_t(tok) * a.r + p * 8);
-      *reinterpret_cast<uint4*>(s_E + rr * a.r + p * 8) = v;
-    } else {
-      v = *reinterpret_cast<const uint4*>(a.F + size_t(s_cur[rr]) * a.r + p * 8);
-      *reinterpret_cast<uint4*>(s_F + rr * a.r + p * 8) = v;
+  {
+    constexpr int PER = 2 * NC * 32 / ST;  // r <= 256: at most 32 pieces per row
+    uint4 buf[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + u * ST;
+      buf[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (e < 2 * NC * pr) {
+        const int which = e / (NC * pr), rr = (e / pr) % NC, p = e % pr;
+        if (which == 0) {
+          const int tok = s_prev[rr < n_prev ? rr : 0];
+          if (tok >= 0 && tok < a.V) buf[u] = *reinterpret_cast<const uint4*>(a.E + size_t(tok) * a.r + p * 8);
+        } else {
+          buf[u] = *reinterpret_cast<const uint4*>(a.F + size_t(s_cur[rr]) * a.r + p * 8);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + u * ST;
+      if (e < 2 * NC * pr) {
+        const int which = e / (NC * pr), rr = (e / pr) % NC, p = e % pr;
+        *reinterpret_cast<uint4*>((which == 0 ? s_E : s_F) + rr * a.r + p * 8) = buf[u];
+      }
     }
   }
   __syncthreads();
@@ -277,7 +385,7 @@ __global__ __launch_bounds__(ST) void sel_table(SelArgs a) {
 constexpr int WALK_GROUP = 32;  // positions whose tables are in LDS at once
 
 __global__ __launch_bounds__(64) void sel_walk(SelArgs a) {
-  __shared__ float s_t[WALK_GROUP * NC * NC];
+  __shared__ __attribute__((aligned(16))) float s_t[WALK_GROUP * NC * NC];
   __shared__ int s_c[WALK_GROUP * NC];
   __shared__ int s_j;
   const int b = blockIdx.x, lane = threadIdx.x;
@@ -288,28 +396,44 @@ __global__ __launch_bounds__(64) void sel_walk(SelArgs a) {
   for (int t0 = 0; t0 < a.G; t0 += WALK_GROUP) {
     const int ng = min(WALK_GROUP, a.G - t0);
     __syncthreads();
-    for (int e = lane; e < ng * NC * NC; e += 64) {
-      const int tt = t0 + e / (NC * NC), ij = e % (NC * NC);
-      // position 0 has row 0 only
-      s_t[e] = (tt == 0 && ij >= NC) ? 0.f : a.tab[(r0 + t0) * NC * NC + e];
-    }
-    for (int e = lane; e < ng * NC; e += 64) s_c[e] = a.cand[(r0 + t0) * NC + e];
+    // every load of the group in flight before the first LDS store (position
+    // 0's rows past the first are never read)
+    const float4* src = reinterpret_cast<const float4*>(a.tab + (r0 + t0) * NC * NC);
+    const int n4 = ng * NC * NC / 4;  // at most 64 per lane
+    constexpr int PER = WALK_GROUP * NC * NC / 4 / 64;
+    float4 buf[PER];
+    int cbuf[WALK_GROUP * NC / 64];
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if (lane + u * 64 < n4) buf[u] = src[lane + u * 64];
+#pragma unroll
+    for (int u = 0; u < WALK_GROUP * NC / 64; ++u)
+      if (lane + u * 64 < ng * NC) cbuf[u] = a.cand[(r0 + t0) * NC + lane + u * 64];
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if (lane + u * 64 < n4) reinterpret_cast<float4*>(s_t)[lane + u * 64] = buf[u];
+#pragma unroll
+    for (int u = 0; u < WALK_GROUP * NC / 64; ++u)
+      if (lane + u * 64 < ng * NC) s_c[lane + u * 64] = cbuf[u];
     __syncthreads();
-    if (lane == 0) {
-      int jp = s_j;
-      for (int u = 0; u < ng; ++u) {
-        const int t = t0 + u;
-        const float* rowp = s_t + (u * NC + (t == 0 ? 0 : jp)) * NC;
-        int j = 0;
-        float best = rowp[0];
-        for (int k = 1; k < NC; ++k)
-          if (rowp[k] > best) { best = rowp[k]; j = k; }  // first maximum
-        a.tokens[r0 + t] = ok ? s_c[u * NC + j] : -1;
-        if (a.scores) a.scores[r0 + t] = ok ? best : NAN;
-        jp = j;
+    // 16 lanes read the visited row at once; the best (lowest j on ties) wins
+    int jp = s_j;
+    for (int u = 0; u < ng; ++u) {
+      const int t = t0 + u;
+      const int j = lane & (NC - 1);
+      float v = s_t[(u * NC + (t == 0 ? 0 : jp)) * NC + j];
+      int jj = j;
+      keep_better<8>(v, jj);
+      keep_better<4>(v, jj);
+      keep_better<2>(v, jj);
+      keep_better<1>(v, jj);
+      if (lane == 0) {
+        a.tokens[r0 + t] = ok ? s_c[u * NC + jj] : -1;
+        if (a.scores) a.scores[r0 + t] = ok ? v : NAN;
       }
-      s_j = jp;
+      jp = jj;
     }
+    if (lane == 0) s_j = jp;
   }
 }
 
@@ -342,7 +466,7 @@ hipError_t launch_select(const float* z, const int32_t* anchor, const uint16_t* 
   const dim3 g1(a.nch, unsigned(rows));
   if ((V & 3) == 0) hipLaunchKernelGGL(sel_chunk_top<true>, g1, dim3(ST), 0, stream, a);
   else hipLaunchKernelGGL(sel_chunk_top<false>, g1, dim3(ST), 0, stream, a);
-  const size_t lds2 = size_t(a.nch) * NC * 8 + size_t(2) * NC * r * 2;
+  const size_t lds2 = size_t(2) * a.nch * NC * 8 + size_t(2) * NC * r * 2;
   hipLaunchKernelGGL(sel_table, dim3(G, B), dim3(ST), lds2, stream, a);
   hipLaunchKernelGGL(sel_walk, dim3(B), dim3(64), 0, stream, a);
   return hipGetLastError();
