@@ -173,16 +173,16 @@ __global__ __launch_bounds__(ST) void sel_chunk_top(SelArgs a) {
   int si = bi;
   wave_sort_best_first(sv, si);
   const float tv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), NC - 1));
-  const int ti = __builtin_amdgcn_readlane(si, NC - 1);
-  // candidates: elements not worse than the threshold, appended slot by slot
-  // (a ballot per slot; most slots hold none)
+  // candidates: elements at or above the threshold's value (equal values past
+  // its index come along too, which only adds candidates), appended slot by
+  // slot (one compare and a ballot per slot; most slots hold none)
   if (t == 0) s_over = 0;
   __syncthreads();
   int total = 0;
 #pragma unroll
   for (int s = 0; s < SPT; ++s) {
     const int e = sel_slot<VEC>(start, s, t);
-    const bool p = (x[s] > tv) | ((x[s] == tv) & (e <= ti));
+    const bool p = x[s] >= tv;
     const unsigned long long m = __ballot(p);
     if (m) {
       const int below = __builtin_amdgcn_mbcnt_hi(unsigned(m >> 32), __builtin_amdgcn_mbcnt_lo(unsigned(m), 0u));
@@ -202,7 +202,8 @@ __global__ __launch_bounds__(ST) void sel_chunk_top(SelArgs a) {
     float v = -INFINITY;
     int i = INT32_MAX;
     if (lane < s_n[w]) { v = s_v[w * WCAP + lane]; i = s_i[w * WCAP + lane]; }
-    wave_sort_best_first(v, i);
+    // a wave with at most NC candidates keeps them all (the final sort orders them)
+    if (s_n[w] > NC) wave_sort_best_first(v, i);
     __syncthreads();
     if (lane < NC) { s_v[w * NC + lane] = v; s_i[w * NC + lane] = i; }
     __syncthreads();
