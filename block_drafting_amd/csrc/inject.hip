@@ -138,7 +138,7 @@ __global__ __launch_bounds__(GT) void ik_gemm(GemmArgs g) {
 // waves of 64 x 64 or 4 of 128 x 128 measured slower).  Both
 // operands reach LDS straight from global memory (global_load_lds, 16 bytes per
 // lane) through rings of SA (H) and SW (W) stages of BK-wide d_in steps; in
-// iteration k a wave issues its W loads of step k + SW - 1, then its H loads of
+// iteration k a loading wave issues its W loads of step k + SW - 1, then its H loads of
 // step k + SA - 1 (SW >= SA, so the W loads of a step are always older than its
 // H loads).  A row is BK / 8 pieces of 16 bytes; the pieces of each 256-byte
 // line are XOR-permuted so the operand reads (16 lanes: 16 rows, one piece
@@ -166,8 +166,17 @@ constexpr int WBK = BD_GEMM_WIDE_BK, WSA = BD_GEMM_WIDE_SA, WSW = BD_GEMM_WIDE_S
 static_assert(WSW >= WSA && WSA >= 2, "ring depths");
 constexpr int WA_BYTES = WBM * WBK * 2;
 constexpr int WW_BYTES = WBN * WBK * 2;
-constexpr int WA_PW = WA_BYTES / 1024 / WNW;  // H loads per wave per step
-constexpr int WW_PW = WW_BYTES / 1024 / WNW;  // W loads per wave per step
+// Waves that issue the operand loads: one per SIMD, so each SIMD's other
+// wave never stalls on a load issue and keeps the matrix pipe busy while its
+// partner waits (measured: about 1.5% faster than every wave issuing its
+// share, and two loading waves slower).
+#ifndef BD_GEMM_WIDE_LOAD_WAVES
+#define BD_GEMM_WIDE_LOAD_WAVES 4
+#endif
+constexpr int WLW = BD_GEMM_WIDE_LOAD_WAVES;
+static_assert(WLW <= WNW && (WBN * WBK * 2 / 1024) % WLW == 0, "loading waves");
+constexpr int WA_PW = WA_BYTES / 1024 / WLW;  // H loads per loading wave per step
+constexpr int WW_PW = WW_BYTES / 1024 / WLW;  // W loads per loading wave per step
 static_assert(WSA * WA_BYTES + WSW * WW_BYTES <= 160 * 1024, "LDS");
 
 // byte offset of piece c (16 bytes) of row `row` in a stage
@@ -216,11 +225,11 @@ __global__ __launch_bounds__(WNT) void ik_gemm_wide(GemmArgs g) {
   const uint32_t lW = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ringW)));
 
   // per-lane byte offsets of this wave's loads from the step's first column:
-  // load q of the wave fills piece slots 64 (w + WNW q) + lane of a stage
+  // load q of a loading wave fills piece slots 64 (w + WLW q) + lane of a stage
   uint32_t offA[WA_PW], offW[WW_PW];
 #pragma unroll
   for (int q = 0; q < WA_PW; ++q) {
-    const int ps = (w + WNW * q) * 64 + lane;
+    const int ps = (w + WLW * q) * 64 + lane;
     // the (row, piece) that wpiece places at slot ps
     constexpr int RPL = 16 / P;
     const int line = ps >> 4, lc = (ps & 15) ^ (line & (P - 1));
@@ -230,7 +239,7 @@ __global__ __launch_bounds__(WNT) void ik_gemm_wide(GemmArgs g) {
   }
 #pragma unroll
   for (int q = 0; q < WW_PW; ++q) {
-    const int ps = (w + WNW * q) * 64 + lane;
+    const int ps = (w + WLW * q) * 64 + lane;
     constexpr int RPL = 16 / P;
     const int line = ps >> 4, lc = (ps & 15) ^ (line & (P - 1));
     const int row = line * RPL + lc / P, c = lc % P;
@@ -247,20 +256,20 @@ __global__ __launch_bounds__(WNT) void ik_gemm_wide(GemmArgs g) {
 
   // prologue: the iterations before the loop, W steps 0 .. SW - SA - 1 alone,
   // then (W step j + SW - 1, H step j + SA - 1) for j = -(SA - 1) .. -1
-  for (int k = 0; k < WSW - WSA && k < ns; ++k)
+  for (int k = 0; k < WSW - WSA && k < ns && w < WLW; ++k)
 #pragma unroll
     for (int q = 0; q < WW_PW; ++q)
-      dma16<true>(Wbase + size_t(k) * WBK, offW[q], lW + (k % WSW) * WW_BYTES + (w + WNW * q) * 1024);
-  for (int j = -(WSA - 1); j < 0; ++j) {
+      dma16<true>(Wbase + size_t(k) * WBK, offW[q], lW + (k % WSW) * WW_BYTES + (w + WLW * q) * 1024);
+  for (int j = -(WSA - 1); j < 0 && w < WLW; ++j) {
     const int kw = j + WSW - 1, ka = j + WSA;
     if (kw < ns)
 #pragma unroll
       for (int q = 0; q < WW_PW; ++q)
-        dma16<true>(Wbase + size_t(kw) * WBK, offW[q], lW + (kw % WSW) * WW_BYTES + (w + WNW * q) * 1024);
+        dma16<true>(Wbase + size_t(kw) * WBK, offW[q], lW + (kw % WSW) * WW_BYTES + (w + WLW * q) * 1024);
     if (ka - 1 < ns && ka - 1 >= 0)
 #pragma unroll
       for (int q = 0; q < WA_PW; ++q)
-        dma16<false>(Abase + size_t(ka - 1) * WBK, offA[q], lA + ((ka - 1) % WSA) * WA_BYTES + (w + WNW * q) * 1024);
+        dma16<false>(Abase + size_t(ka - 1) * WBK, offA[q], lA + ((ka - 1) % WSA) * WA_BYTES + (w + WLW * q) * 1024);
   }
   for (int k = 0; k < ns; ++k) {
     vm_wait_le<(WSA - 2) * (WA_PW + WW_PW)>(wide_younger(k, ns));
@@ -270,11 +279,12 @@ __global__ __launch_bounds__(WNT) void ik_gemm_wide(GemmArgs g) {
     // issue overlaps the MFMAs instead of stalling the SIMD after the barrier
     const int kw = k + WSW - 1, ka = k + WSA - 1;
     auto refill = [&](int d) {
+      if (w >= WLW) return;
       if (d < WW_PW) {
-        if (kw < ns) dma16<true>(Wbase + size_t(kw) * WBK, offW[d], lW + (kw % WSW) * WW_BYTES + (w + WNW * d) * 1024);
+        if (kw < ns) dma16<true>(Wbase + size_t(kw) * WBK, offW[d], lW + (kw % WSW) * WW_BYTES + (w + WLW * d) * 1024);
       } else {
         const int q = d - WW_PW;
-        if (ka < ns) dma16<false>(Abase + size_t(ka) * WBK, offA[q], lA + (ka % WSA) * WA_BYTES + (w + WNW * q) * 1024);
+        if (ka < ns) dma16<false>(Abase + size_t(ka) * WBK, offA[q], lA + (ka % WSA) * WA_BYTES + (w + WLW * q) * 1024);
       }
     };
     constexpr int NDMA = WW_PW + WA_PW;
