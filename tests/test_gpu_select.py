@@ -35,13 +35,18 @@ def run_gpu(z, anchor, Eb, Fb):
     return tok.cpu().numpy(), sc.cpu().numpy(), cd.cpu().numpy()
 
 
-def check(z, anchor, Eb, Fb, label=""):
+def check(z, anchor, Eb, Fb, label="", reqs=None):
+    """GPU on the whole batch; the oracle on the requests `reqs` (all by
+    default): selection is independent per request."""
     B, G, V = z.shape
     say(f"select_block {label} B={B} G={G} V={V} r={Eb.shape[1]}")
     gt, gs, gc = run_gpu(z, anchor, Eb, Fb)
+    anchor = np.asarray(anchor)
+    if reqs is not None:
+        z, anchor, gt, gs, gc = z[reqs], anchor[reqs], gt[reqs], gs[reqs], gc[reqs]
+        B = len(reqs)
     E, F = bits_to_f64(Eb), bits_to_f64(Fb)
     z64 = np.asarray(z, np.float32).astype(np.float64)
-    anchor = np.asarray(anchor)
     # the oracle defines valid anchors only; an invalid one is checked for its flag
     ot, osc, oc, otab = osel.select_block(z64, np.where((anchor >= 0) & (anchor < V), anchor, 0), E, F)
     np.testing.assert_array_equal(gc, oc)
@@ -146,6 +151,19 @@ def test_full_size_8b_draft_logits():
     Eb, Fb = tables(rng, cfg.V, 256, 0.1)
     anchor = rng.integers(0, cfg.V, cfg.B)
     check(r.z_draft, anchor, Eb, Fb, label="8B draft logits")
+
+
+def test_full_size_batch_128_sampled_requests():
+    """The batch-128 workload's draft logits (lognormal contexts, G = 15,
+    V = 151936), rank-256 tables: the whole batch on the GPU, every 8th
+    request and the last against the oracle."""
+    cfg = wl.CONFIGS["sweep-b128"]
+    z_draft = wl.streams(0)["z_draft"].standard_normal((cfg.B, cfg.G, cfg.V), dtype=np.float32)
+    rng = np.random.default_rng(10)
+    Eb, Fb = tables(rng, cfg.V, 256, 0.1)
+    anchor = rng.integers(0, cfg.V, cfg.B)
+    reqs = np.unique(np.r_[np.arange(0, cfg.B, 8), cfg.B - 1])
+    check(z_draft, anchor, Eb, Fb, label="batch-128 draft logits", reqs=reqs)
 
 
 def test_deterministic_run_to_run():
