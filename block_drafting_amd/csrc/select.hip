@@ -13,14 +13,17 @@
 //
 // Three launches:
 //   sel_chunk_top  (chunk, row): the chunk's 16 best logits (value desc, index
-//                  asc).  Per wave the 16th best lane maximum bounds the
-//                  wave's 16 best from below, so only elements at or above it
-//                  are ranked; a wave with more than WCAP of them (ties) sends
-//                  the chunk to an exact 16-round selection.
+//                  asc).  The chunk's 16th best lane maximum bounds its 16
+//                  best from below (found by a bitwise search over
+//                  order-preserving keys, per wave and then over the waves'
+//                  survivors), so only elements at or above it are ranked, in
+//                  one wave-wide sort; more than WCAP of them in a wave, or
+//                  more than 64 in all (ties), sends the chunk to an exact
+//                  16-round selection.
 //   sel_table      (position, request): merges the chunk lists of its position
 //                  and of the one before, stages the predecessors' E rows and
 //                  the candidates' F rows in LDS and computes the position's
-//                  16 x 16 table (one entry per thread).
+//                  16 x 16 table on the matrix cores.
 //   sel_walk       (request): the tables, 32 positions at a time, in LDS; one
 //                  lane walks them.
 #include "bd_common.hpp"
@@ -34,7 +37,8 @@ constexpr int ST = 256;        // threads of a workgroup
 constexpr int SCH = 8192;      // logits per chunk
 constexpr int SPT = SCH / ST;  // 32 per thread
 constexpr int NC = 16;         // candidates per position
-constexpr int WCAP = 64;       // threshold candidates a wave may keep
+constexpr int WCAP = 64;
+constexpr int SEL_ROW_PAD = 8;  // bf16 elements of padding per staged E / F row       // threshold candidates a wave may keep
 
 struct SelArgs {
   const float* z;         // [B * G][V] base logits of the drafted positions
@@ -126,6 +130,30 @@ __device__ __forceinline__ void bitonic_sort(float& sv, int& si) {
 }
 __device__ __forceinline__ void wave_sort_best_first(float& sv, int& si) { bitonic_sort<64>(sv, si); }
 
+// Order-preserving 32-bit keys of finite or infinite floats: a < b exactly
+// when key(a) < key(b), with -0 taken as +0 so that equal values get equal
+// keys.  key_value inverts it (giving +0 for either zero).
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// The NC-th largest of the wave's 64 keys (one per lane), found bit by bit
+// from the top: the largest T with at least NC keys >= T, which is always one
+// of the keys.  One compare and one ballot count per bit.
+__device__ __forceinline__ uint32_t wave_nth_key(uint32_t k) {
+  uint32_t T = 0;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = T | (1u << b);
+    if (__popcll(__ballot(k >= c)) >= NC) T = c;
+  }
+  return T;
+}
+
 // ------------------------------------------------------------- chunk top-16
 template <bool VEC>
 __global__ __launch_bounds__(ST) void sel_chunk_top(SelArgs a) {
@@ -135,6 +163,8 @@ __global__ __launch_bounds__(ST) void sel_chunk_top(SelArgs a) {
   __shared__ int s_over;
   __shared__ float s_rv[4];
   __shared__ int s_ri[4];
+  __shared__ uint32_t s_k[4 * NC];
+  __shared__ uint32_t s_tk;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int c = blockIdx.x, row = blockIdx.y;
   const int start = c * SCH;
@@ -168,16 +198,30 @@ __global__ __launch_bounds__(ST) void sel_chunk_top(SelArgs a) {
     bs = gt ? s : bs;
   }
   int bi = VEC ? start + 4 * ((bs >> 2) * ST + t) + (bs & 3) : start + bs * ST + t;
-  // the wave's lane maxima sorted best first
-  float sv = bv;
-  int si = bi;
-  wave_sort_best_first(sv, si);
-  const float tv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), NC - 1));
-  // candidates: elements at or above the threshold's value (equal values past
-  // its index come along too, which only adds candidates), appended slot by
-  // slot (one compare and a ballot per slot; most slots hold none)
+  // The chunk's 16th largest lane maximum bounds its 16 best from below (16
+  // elements are at least that large).  Each wave finds its own 16th largest
+  // lane maximum and hands its 16 lane maxima at or above it to wave 0, which
+  // takes the 16th largest of those 64: every one of the chunk's 16 largest
+  // lane maxima is among its wave's 16 largest.
+  {
+    const uint32_t kb = order_key(bv);
+    const uint32_t tw = wave_nth_key(kb);
+    const bool p = kb >= tw;  // at least NC lanes
+    const unsigned long long m = __ballot(p);
+    const int pos = __builtin_amdgcn_mbcnt_hi(unsigned(m >> 32), __builtin_amdgcn_mbcnt_lo(unsigned(m), 0u));
+    if (p && pos < NC) s_k[w * NC + pos] = kb;
+  }
   if (t == 0) s_over = 0;
   __syncthreads();
+  if (w == 0) {
+    const uint32_t tc = wave_nth_key(s_k[lane]);
+    if (lane == 0) s_tk = tc;
+  }
+  __syncthreads();
+  const float tv = key_value(s_tk);
+  // candidates: elements at or above the bound (equal values past its index
+  // come along too, which only adds candidates), appended slot by slot (one
+  // compare and a ballot per slot; most slots hold none)
   int total = 0;
 #pragma unroll
   for (int s = 0; s < SPT; ++s) {
@@ -196,20 +240,19 @@ __global__ __launch_bounds__(ST) void sel_chunk_top(SelArgs a) {
   __syncthreads();
   float* ov = a.ctv + (size_t(row) * a.nch + c) * NC;
   int* oi = a.cti + (size_t(row) * a.nch + c) * NC;
-  if (!s_over) {
-    // each wave sorts its candidates (one per lane, empty lanes last): its 16
-    // best are the first 16 lanes; then wave 0 sorts the four lists of 16
-    float v = -INFINITY;
-    int i = INT32_MAX;
-    if (lane < s_n[w]) { v = s_v[w * WCAP + lane]; i = s_i[w * WCAP + lane]; }
-    // a wave with at most NC candidates keeps them all (the final sort orders them)
-    if (s_n[w] > NC) wave_sort_best_first(v, i);
-    __syncthreads();
-    if (lane < NC) { s_v[w * NC + lane] = v; s_i[w * NC + lane] = i; }
-    __syncthreads();
+  const int n0 = s_n[0], n01 = n0 + s_n[1], n012 = n01 + s_n[2], nall = n012 + s_n[3];
+  if (!s_over && nall <= 64) {
+    // wave 0 sorts all candidates (one per lane, the four lists one after
+    // the other, empty lanes last) and keeps the first 16
     if (w == 0) {
-      v = s_v[lane];
-      i = s_i[lane];
+      float v = -INFINITY;
+      int i = INT32_MAX;
+      if (lane < nall) {
+        const int ww = (lane >= n0) + (lane >= n01) + (lane >= n012);
+        const int off = lane - (ww == 0 ? 0 : ww == 1 ? n0 : ww == 2 ? n01 : n012);
+        v = s_v[ww * WCAP + off];
+        i = s_i[ww * WCAP + off];
+      }
       wave_sort_best_first(v, i);
       // fewer than NC elements in the chunk: the list ends in empty entries
       if (lane < NC) {
@@ -287,11 +330,14 @@ __device__ __forceinline__ void merge_lists(int nch, const float* s_mv, const in
 
 __global__ __launch_bounds__(ST) void sel_table(SelArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char sel_lds[];
-  // [2][nch * NC] list values and indices, then E rows [NC][r] and F rows [NC][r]
+  // [2][nch * NC] list values and indices, then E rows [NC][r + pad] and F rows [NC][r + pad]
   float* s_mv = reinterpret_cast<float*>(sel_lds);
   int* s_mi = reinterpret_cast<int*>(s_mv + 2 * a.nch * NC);
   uint16_t* s_E = reinterpret_cast<uint16_t*>(s_mi + 2 * a.nch * NC);
-  uint16_t* s_F = s_E + NC * a.r;
+  // rows padded by 16 bytes: the 16 candidate rows one read phase touches
+  // then start 4 banks apart and cover all 64 banks
+  const int rs = (a.r + 31) / 32 * 32 + SEL_ROW_PAD;
+  uint16_t* s_F = s_E + NC * rs;
   __shared__ int s_prev[NC], s_cur[NC];
   __shared__ float s_z[NC];
   const int t = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
@@ -301,26 +347,33 @@ __global__ __launch_bounds__(ST) void sel_table(SelArgs a) {
   // position's, wave 1 the previous one's
   const int n = a.nch * NC;
   const int nrows = t > 0 ? 2 : 1;
+  int anc = 0;  // position 0's predecessor, loaded with the lists
+  if (t == 0 && tid == 0) anc = a.anchor[b];
   {
     constexpr int PER = 2 * 64 * NC / ST;  // at most 64 chunks per row
     float bv[PER];
     int bi[PER];
+    // unconditional loads (past the end: the last entry again), so that all
+    // are in flight together; only the LDS stores are conditional
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int e = tid + u * ST;
-      if (e < nrows * n) {
-        const size_t src = size_t(row - e / n) * n + e % n;
-        bv[u] = a.ctv[src];
-        bi[u] = a.cti[src];
-      }
+      const int e = min(tid + u * ST, nrows * n - 1);
+      const size_t src = size_t(row - e / n) * n + e % n;
+      bv[u] = a.ctv[src];
+      bi[u] = a.cti[src];
     }
+    // the values are needed here, so no load is moved into the conditional
+    // stores below (which would wait for each in turn)
+#pragma unroll
+    for (int u = 0; u < PER; ++u) asm volatile("" : "+v"(bv[u]), "+v"(bi[u]));
+    asm volatile("" : "+v"(anc));
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int e = tid + u * ST;
       if (e < nrows * n) { s_mv[e] = bv[u]; s_mi[e] = bi[u]; }
     }
   }
-  if (t == 0 && tid == 0) s_prev[0] = a.anchor[b];
+  if (t == 0 && tid == 0) s_prev[0] = anc;
   __syncthreads();
   const int n_prev = t > 0 ? NC : 1;
   if (tid < 64) merge_lists(a.nch, s_mv, s_mi, s_cur, s_z);
@@ -334,51 +387,54 @@ __global__ __launch_bounds__(ST) void sel_table(SelArgs a) {
   // rows of E for the predecessors and of F for the candidates (an anchor
   // outside the vocabulary reads as a zero row; its request is flagged by
   // sel_walk)
-  const int pr = a.r / 8;  // 16-byte pieces per row
+  // Rows are staged with r rounded up to 32 (zeros past r), the MFMA's k
+  // step, plus the bank padding.
+  const int pr = a.r / 8;                 // 16-byte pieces per row
+  const int pr32 = (a.r + 31) / 32 * 4;   // the same, zero-padded to 32 elements
   {
     constexpr int PER = 2 * NC * 32 / ST;  // r <= 256: at most 32 pieces per row
     uint4 buf[PER];
+    // one unconditional load per piece from a valid row (clamped index, an
+    // invalid anchor's row replaced by zeros afterwards), all in flight together
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int e = tid + u * ST;
-      buf[u] = make_uint4(0u, 0u, 0u, 0u);
-      if (e < 2 * NC * pr) {
-        const int which = e / (NC * pr), rr = (e / pr) % NC, p = e % pr;
-        if (which == 0) {
-          const int tok = s_prev[rr < n_prev ? rr : 0];
-          if (tok >= 0 && tok < a.V) buf[u] = *reinterpret_cast<const uint4*>(a.E + size_t(tok) * a.r + p * 8);
-        } else {
-          buf[u] = *reinterpret_cast<const uint4*>(a.F + size_t(s_cur[rr]) * a.r + p * 8);
-        }
-      }
+      const int e = min(tid + u * ST, 2 * NC * pr32 - 1);
+      const int which = e / (NC * pr32), rr = (e / pr32) % NC, p = e % pr32;
+      const int tok = which == 0 ? s_prev[rr < n_prev ? rr : 0] : s_cur[rr];
+      const bool valid = tok >= 0 && tok < a.V;
+      const uint16_t* base = which == 0 ? a.E : a.F;
+      const uint4 v = *reinterpret_cast<const uint4*>(base + size_t(valid ? tok : 0) * a.r + min(p, pr - 1) * 8);
+      buf[u] = valid && p < pr ? v : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
+    for (int u = 0; u < PER; ++u) asm volatile("" : "+v"(buf[u].x), "+v"(buf[u].y), "+v"(buf[u].z), "+v"(buf[u].w));
+#pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int e = tid + u * ST;
-      if (e < 2 * NC * pr) {
-        const int which = e / (NC * pr), rr = (e / pr) % NC, p = e % pr;
-        *reinterpret_cast<uint4*>((which == 0 ? s_E : s_F) + rr * a.r + p * 8) = buf[u];
+      if (e < 2 * NC * pr32) {
+        const int which = e / (NC * pr32), rr = (e / pr32) % NC, p = e % pr32;
+        *reinterpret_cast<uint4*>((which == 0 ? s_E : s_F) + rr * rs + p * 8) = buf[u];
       }
     }
   }
   __syncthreads();
-  // entry (i, j) = z(c_j) + E[p_i] . F[c_j], the products added in order k
-  const int i = tid / NC, j = tid % NC;
-  if (i < n_prev) {
-    const uint16_t* er = s_E + i * a.r;
-    const uint16_t* fr = s_F + j * a.r;
-    float dot = 0.f;
-    for (int k = 0; k < a.r; k += 8) {
-      const uint4 ev = *reinterpret_cast<const uint4*>(er + k);
-      const uint4 fv = *reinterpret_cast<const uint4*>(fr + k);
-      const uint32_t ew[4] = {ev.x, ev.y, ev.z, ev.w}, fw[4] = {fv.x, fv.y, fv.z, fv.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        dot = fmaf(bf16_to_f32(uint16_t(ew[q] & 0xffffu)), bf16_to_f32(uint16_t(fw[q] & 0xffffu)), dot);
-        dot = fmaf(bf16_to_f32(uint16_t(ew[q] >> 16)), bf16_to_f32(uint16_t(fw[q] >> 16)), dot);
-      }
+  // entry (i, j) = z(c_j) + E[p_i] . F[c_j]: one 16 x 16 product over k on
+  // the matrix cores (16x16x32 bf16, fp32 accumulation).  Lane l supplies row
+  // l % 16 of E and of F, k octet l / 16 of each 32-step, and receives
+  // entries (4 (l / 16) + q, l % 16), q = 0..3.
+  if (tid < 64) {
+    const int lr = tid & 15, kq = tid >> 4;
+    floatx4 d = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < pr32 * 8; k0 += 32) {
+      const bf16x8 ea = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(s_E + lr * rs + k0 + 8 * kq));
+      const bf16x8 fb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(s_F + lr * rs + k0 + 8 * kq));
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ea, fb, d, 0, 0, 0);
     }
-    a.tab[(size_t(row) * NC + i) * NC + j] = s_z[j] + dot;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = 4 * kq + q;
+      if (i < n_prev) a.tab[(size_t(row) * NC + i) * NC + lr] = s_z[lr] + d[q];
+    }
   }
 }
 
@@ -404,18 +460,18 @@ __global__ __launch_bounds__(64) void sel_walk(SelArgs a) {
     constexpr int PER = WALK_GROUP * NC * NC / 4 / 64;
     float4 buf[PER];
     int cbuf[WALK_GROUP * NC / 64];
+    // unconditional loads (past the group: its last entry again) so that all
+    // are in flight together
 #pragma unroll
-    for (int u = 0; u < PER; ++u)
-      if (lane + u * 64 < n4) buf[u] = src[lane + u * 64];
+    for (int u = 0; u < PER; ++u) buf[u] = src[min(lane + u * 64, n4 - 1)];
 #pragma unroll
-    for (int u = 0; u < WALK_GROUP * NC / 64; ++u)
-      if (lane + u * 64 < ng * NC) cbuf[u] = a.cand[(r0 + t0) * NC + lane + u * 64];
+    for (int u = 0; u < WALK_GROUP * NC / 64; ++u) cbuf[u] = a.cand[(r0 + t0) * NC + min(lane + u * 64, ng * NC - 1)];
+    // (the LDS arrays hold a whole group: entries past this one's end are
+    // written too and never read)
 #pragma unroll
-    for (int u = 0; u < PER; ++u)
-      if (lane + u * 64 < n4) reinterpret_cast<float4*>(s_t)[lane + u * 64] = buf[u];
+    for (int u = 0; u < PER; ++u) reinterpret_cast<float4*>(s_t)[lane + u * 64] = buf[u];
 #pragma unroll
-    for (int u = 0; u < WALK_GROUP * NC / 64; ++u)
-      if (lane + u * 64 < ng * NC) s_c[lane + u * 64] = cbuf[u];
+    for (int u = 0; u < WALK_GROUP * NC / 64; ++u) s_c[lane + u * 64] = cbuf[u];
     __syncthreads();
     // 16 lanes read the visited row at once; the best (lowest j on ties) wins
     int jp = s_j;
@@ -467,7 +523,7 @@ hipError_t launch_select(const float* z, const int32_t* anchor, const uint16_t* 
   const dim3 g1(a.nch, unsigned(rows));
   if ((V & 3) == 0) hipLaunchKernelGGL(sel_chunk_top<true>, g1, dim3(ST), 0, stream, a);
   else hipLaunchKernelGGL(sel_chunk_top<false>, g1, dim3(ST), 0, stream, a);
-  const size_t lds2 = size_t(2) * a.nch * NC * 8 + size_t(2) * NC * r * 2;
+  const size_t lds2 = size_t(2) * a.nch * NC * 8 + size_t(2) * NC * ((r + 31) / 32 * 32 + SEL_ROW_PAD) * 2;
   hipLaunchKernelGGL(sel_table, dim3(G, B), dim3(ST), lds2, stream, a);
   hipLaunchKernelGGL(sel_walk, dim3(B), dim3(64), 0, stream, a);
   return hipGetLastError();
