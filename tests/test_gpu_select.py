@@ -91,6 +91,8 @@ def tables(rng, V, r, std):
     (2, 7, 1000, 64, 1),
     (4, 15, 20000, 256, 2),     # several chunks, a ragged last one
     (2, 3, 40001, 32, 3),       # V % 4 != 0: scalar loads
+    (3, 6, 9000, 40, 11),       # ranks that are no multiple of the 32-element k step
+    (2, 5, 17000, 200, 12),
 ])
 def test_random_parity(B, G, V, r, seed):
     rng = np.random.default_rng(seed)
