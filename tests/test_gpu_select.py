@@ -168,6 +168,31 @@ def test_full_size_batch_128_sampled_requests():
     check(z_draft, anchor, Eb, Fb, label="batch-128 draft logits", reqs=reqs)
 
 
+def test_largest_vocabulary_merges_64_chunk_lists():
+    """V = 524288, the largest supported vocabulary: 64 chunk lists per
+    position, one per lane of the merging wave."""
+    rng = np.random.default_rng(13)
+    B, G, V, r = 2, 3, 524288, 64
+    z = rng.standard_normal((B, G, V)).astype(np.float32)
+    Eb, Fb = tables(rng, V, r, 0.15)
+    check(z, rng.integers(0, V, B), Eb, Fb, label="largest vocabulary")
+
+
+@pytest.mark.parametrize("B,G", [(0, 5), (3, 0)])
+def test_empty_batch_is_a_no_op(B, G):
+    """No request or no drafted position: nothing is launched and the
+    caller's buffers are untouched."""
+    import block_drafting_amd as bd
+    V, r = 1000, 8
+    rng = np.random.default_rng(14)
+    Eb, Fb = tables(rng, V, r, 0.15)
+    z = torch.zeros((B, G, V), dtype=torch.float32, device="cuda")
+    tok = torch.full((B, G), -7, dtype=torch.int32, device="cuda")
+    bd.select_block(z, torch.zeros(B, dtype=torch.int32, device="cuda"), cuda_bits(Eb), cuda_bits(Fb), tokens=tok)
+    torch.cuda.synchronize()
+    assert (tok.cpu().numpy() == -7).all()
+
+
 def test_deterministic_run_to_run():
     rng = np.random.default_rng(8)
     z = rng.standard_normal((4, 9, 30000)).astype(np.float32)
