@@ -116,13 +116,60 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return ia < ib;
 }
 
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    float ov = __shfl_xor(v, o);
-    int oi = __shfl_xor(i, o);
-    if (better(ov, oi, v, i)) { v = ov; i = oi; }
+// Value of lane l ^ J, for every lane, without the LDS permute: DPP row
+// moves within rows of 16 lanes, the gfx950 permlane swaps across them.
+template <int J>
+__device__ __forceinline__ int xor_lane(int x) {
+  if constexpr (J == 1) {
+    return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad_perm [1, 0, 3, 2]
+  } else if constexpr (J == 2) {
+    return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm [2, 3, 0, 1]
+  } else if constexpr (J == 4) {
+    const int y = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);  // row_half_mirror: l ^ 7
+    return __builtin_amdgcn_mov_dpp(y, 0x1B, 0xF, 0xF, false);          // quad_perm [3, 2, 1, 0]: ^ 3
+  } else if constexpr (J == 8) {
+    const int y = __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false);  // row_mirror: l ^ 15
+    return __builtin_amdgcn_mov_dpp(y, 0x141, 0xF, 0xF, false);         // row_half_mirror: ^ 7
+  } else if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return ((threadIdx.x >> 4) & 1) ? int(r[0]) : int(r[1]);
+  } else {
+    static_assert(J == 32, "xor distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (threadIdx.x & 32) ? int(r[0]) : int(r[1]);
   }
+}
+template <int J>
+__device__ __forceinline__ float xor_lane(float x) {
+  return __int_as_float(xor_lane<J>(__float_as_int(x)));
+}
+
+// Lane s's value (s the same in every lane).
+__device__ __forceinline__ int lane_value(int x, int s) { return __builtin_amdgcn_readlane(x, s); }
+__device__ __forceinline__ float lane_value(float x, int s) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), s));
+}
+__device__ __forceinline__ double lane_value(double x, int s) {
+  const long long u = __double_as_longlong(x);
+  const unsigned lo = unsigned(__builtin_amdgcn_readlane(int(u), s));
+  const unsigned hi = unsigned(__builtin_amdgcn_readlane(int(u >> 32), s));
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// every lane gets the wave's best (value, index) pair (lowest index on ties)
+template <int J>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+  const float ov = xor_lane<J>(v);
+  const int oi = xor_lane<J>(i);
+  if (better(ov, oi, v, i)) { v = ov; i = oi; }
+}
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_step<32>(v, i);
+  argmax_step<16>(v, i);
+  argmax_step<8>(v, i);
+  argmax_step<4>(v, i);
+  argmax_step<2>(v, i);
+  argmax_step<1>(v, i);
 }
 
 }  // namespace bd

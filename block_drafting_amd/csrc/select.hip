@@ -64,31 +64,6 @@ __device__ __forceinline__ bool sel_better(float v, int i, float w, int j) {
 // The value of lane l ^ J, without the LDS permute path: DPP row moves for
 // J <= 8 (quad permutations; 4 = half-mirror then reversed quad, 8 = mirror
 // then half-mirror), v_permlane16_swap / v_permlane32_swap for 16 and 32.
-template <int J>
-__device__ __forceinline__ int xor_lane(int x) {
-  if constexpr (J == 1) {
-    return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad_perm [1, 0, 3, 2]
-  } else if constexpr (J == 2) {
-    return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm [2, 3, 0, 1]
-  } else if constexpr (J == 4) {
-    const int y = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);  // row_half_mirror: l ^ 7
-    return __builtin_amdgcn_mov_dpp(y, 0x1B, 0xF, 0xF, false);          // quad_perm [3, 2, 1, 0]: ^ 3
-  } else if constexpr (J == 8) {
-    const int y = __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false);  // row_mirror: l ^ 15
-    return __builtin_amdgcn_mov_dpp(y, 0x141, 0xF, 0xF, false);         // row_half_mirror: ^ 7
-  } else if constexpr (J == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    return ((threadIdx.x >> 4) & 1) ? int(r[0]) : int(r[1]);
-  } else {
-    static_assert(J == 32, "xor distance");
-    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return (threadIdx.x & 32) ? int(r[0]) : int(r[1]);
-  }
-}
-template <int J>
-__device__ __forceinline__ float xor_lane(float x) {
-  return __int_as_float(xor_lane<J>(__float_as_int(x)));
-}
 // keep the better of this lane's (v, i) and lane l ^ J's
 template <int J>
 __device__ __forceinline__ void keep_better(float& v, int& i) {

@@ -540,7 +540,9 @@ __device__ __forceinline__ void merge_stats(const VerifyArgs& a, int row, int la
   }
 }
 
-__device__ void merge_row(const VerifyArgs& a, int row, int lane) {
+// s_v / s_i: LDS room for the row's nrec * k chunk-list entries (used with a
+// top-k filter only, by a one-wave workgroup)
+__device__ void merge_row(const VerifyArgs& a, int row, int lane, float* s_v = nullptr, int* s_i = nullptr) {
   float v;
   int i;
   double S;
@@ -564,45 +566,98 @@ __device__ void merge_row(const VerifyArgs& a, int row, int lane) {
     double* kp = a.ws.rkp + size_t(row) * TOPK_MAX;
     float kv_lane = -INFINITY;  // lane r keeps the r-th kept value
     int kept = 0;
-    for (int r = 0; r < k; ++r) {
-      float bv = -INFINITY;
-      int bi = INT32_MAX;
-      for (int j = lane; j < ncand; j += 64) {
-        float x = cv[j];
-        int id = ci[j];
-        if (id == INT32_MAX) continue;
-        if ((pi < 0 || better(pv, pi, x, id)) && better(x, id, bv, bi)) { bv = x; bi = id; }
+    if (s_v && nrec <= 64) {
+      // the chunk lists are sorted best first: a k-way merge, lane l holding
+      // list l's head and the round's winner advancing (the lists staged in
+      // LDS, loaded eight per lane at a time)
+      for (int j0 = 0; j0 < ncand; j0 += 8 * 64) {
+        float vb8[8];
+        int ib8[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int jc = min(j0 + lane + 64 * c, ncand - 1);
+          vb8[c] = cv[jc];
+          ib8[c] = ci[jc];
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) asm volatile("" : "+v"(vb8[c]), "+v"(ib8[c]));
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          if (j0 + lane + 64 * c < ncand) { s_v[j0 + lane + 64 * c] = vb8[c]; s_i[j0 + lane + 64 * c] = ib8[c]; }
       }
-      wave_argmax(bv, bi);
-      if (bi == INT32_MAX) break;
-      if (lane == r) { kv_lane = bv; ki[r] = bi; }
-      pv = bv; pi = bi;
-      ++kept;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      int h = 0;
+      float hv = lane < nrec ? s_v[lane * k] : -INFINITY;
+      int hi = lane < nrec ? s_i[lane * k] : INT32_MAX;
+      for (int r = 0; r < k; ++r) {
+        float bv = hv;
+        int bi = hi;
+        wave_argmax(bv, bi);
+        if (bi == INT32_MAX) break;
+        if (hi == bi) {  // indices are distinct: exactly one lane wins
+          ++h;
+          hv = h < k ? s_v[lane * k + h] : -INFINITY;
+          hi = h < k ? s_i[lane * k + h] : INT32_MAX;
+        }
+        if (lane == r) { kv_lane = bv; ki[r] = bi; }
+        ++kept;
+      }
+    } else {
+      // each round the best candidate strictly after the previous pick
+      for (int r = 0; r < k; ++r) {
+        float bv = -INFINITY;
+        int bi = INT32_MAX;
+        for (int j = lane; j < ncand; j += 64) {
+          float x = cv[j];
+          int id = ci[j];
+          if (id == INT32_MAX) continue;
+          if ((pi < 0 || better(pv, pi, x, id)) && better(x, id, bv, bi)) { bv = x; bi = id; }
+        }
+        wave_argmax(bv, bi);
+        if (bi == INT32_MAX) break;
+        if (lane == r) { kv_lane = bv; ki[r] = bi; }
+        pv = bv; pi = bi;
+        ++kept;
+      }
     }
     // softmax over the kept set in fp64: x_j = z_j / T, e_j = exp(x_j - x_0)
-    double x0 = double(__shfl(kv_lane, 0)) / double(a.T);
+    double x0 = double(lane_value(kv_lane, 0)) / double(a.T);
     double e = 0.0;
     if (lane < kept) e = exp(double(kv_lane) / double(a.T) - x0);
     // sum in kept order (lane 0 first), the same sequential order everywhere
     double tot = 0.0;
-    for (int r = 0; r < kept; ++r) tot += __shfl(e, r);
+    for (int r = 0; r < kept; ++r) tot += lane_value(e, r);
     double p = (lane < kept) ? e / tot : 0.0;
     int n = kept;
     if (a.top_p < 1.0f) {
       double run = 0.0;
       n = kept;
       for (int r = 0; r < kept; ++r) {
-        run += __shfl(p, r);
+        run += lane_value(p, r);
         if (run >= double(a.top_p)) { n = r + 1; break; }
       }
       if (n < 1) n = 1;
       double tot2 = 0.0;
-      for (int r = 0; r < n; ++r) tot2 += __shfl(p, r);
+      for (int r = 0; r < n; ++r) tot2 += lane_value(p, r);
       p = (lane < n) ? p / tot2 : 0.0;
     }
     if (lane < n) kp[lane] = p;
     if (lane == 0) a.ws.rkn[row] = n;
   }
+}
+
+// Kept probability, in the row whose kept list lane s holds as (kid, kpd)
+// for s < nd, of the token `tok` this lane asks for (0 when not kept).
+__device__ __forceinline__ double kept_lookup(int tok, int kid, double kpd, int nd) {
+  double q = 0.0;
+  for (int s = 0; s < nd; ++s) {
+    const int ts = lane_value(kid, s);
+    const double ps = lane_value(kpd, s);
+    if (ts == tok) q = ps;
+  }
+  return q;
 }
 
 __device__ __forceinline__ double kept_prob(const VerifyArgs& a, int row, int tok) {
@@ -616,6 +671,25 @@ __device__ __forceinline__ double kept_prob(const VerifyArgs& a, int row, int to
 
 constexpr int DT = 1024;  // threads of the decision workgroup (16 waves)
 
+// One wave per (request, row): the row's statistics records merged, and with
+// a top-k filter its kept list (k rounds of a wave-wide argmax).  Spread over
+// the whole chip rather than one workgroup per request.
+__global__ __launch_bounds__(64) void vb_merge_rows(VerifyArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char mr_lds[];  // [nrec * k] values, then indices
+  const int b = blockIdx.x, lane = threadIdx.x, j = blockIdx.y;
+  const ReqRows rr = req_rows(a, b);
+  if (!rr.ok) return;
+  const int G = rr.G;
+  const bool drafts = a.n_rows > a.n_trows;
+  const int n_my = (G + 1) + (drafts ? G : 0);
+  if (j >= n_my) return;
+  const int row = j <= G ? rr.t0 + j : a.n_trows + rr.d0 + (j - G - 1);
+  size_t slot0;
+  const int nrec = row_records(a, row, slot0);
+  float* s_v = reinterpret_cast<float*>(mr_lds);
+  merge_row(a, row, lane, s_v, reinterpret_cast<int*>(s_v + nrec * a.topk));
+}
+
 __global__ __launch_bounds__(DT) void vb_decide(VerifyArgs a) {
   const int b = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -627,13 +701,54 @@ __global__ __launch_bounds__(DT) void vb_decide(VerifyArgs a) {
   const int G = rr.G;
   const bool drafts = a.n_rows > a.n_trows;
   // rows of this request: G+1 target rows, then G draft rows when present
-  const int n_my = (G + 1) + (drafts ? G : 0);
-  for (int j = w; j < n_my; j += DT / 64) {
-    int row = j <= G ? rr.t0 + j : a.n_trows + rr.d0 + (j - G - 1);
-    merge_row(a, row, lane);
+  if (a.topk == 0) {
+    // no kept lists: the rows' merges are short, done here
+    const int n_my = (G + 1) + (drafts ? G : 0);
+    for (int j = w; j < n_my; j += DT / 64) {
+      const int row = j <= G ? rr.t0 + j : a.n_trows + rr.d0 + (j - G - 1);
+      merge_row(a, row, lane);
+    }
+    __threadfence_block();
+    __syncthreads();
   }
-  __threadfence_block();
+  // with a top-k filter the rows were merged by vb_merge_rows; with sampling, P(d) and Q(d) of
+  // each drafted token from its rows' kept lists, one wave per position
+  __shared__ double s_pq[2 * 64];  // [position] P(d), then [G + position] Q(d)
+  if (!a.greedy) {
+    for (int i = w; i < G; i += DT / 64) {
+      const int d = a.dtok[rr.d0 + i];
+      const int trow = rr.t0 + i, drow = a.n_trows + rr.d0 + i;
+      const int nt = a.ws.rkn[trow], nd = a.ws.rkn[drow];
+      const int kit = lane < nt ? a.ws.rki[size_t(trow) * TOPK_MAX + lane] : -1;
+      const double kpt = lane < nt ? a.ws.rkp[size_t(trow) * TOPK_MAX + lane] : 0.0;
+      const int kid = lane < nd ? a.ws.rki[size_t(drow) * TOPK_MAX + lane] : -2;
+      const double kpd = lane < nd ? a.ws.rkp[size_t(drow) * TOPK_MAX + lane] : 0.0;
+      const unsigned long long ft = __ballot(lane < nt && kit == d);
+      const unsigned long long fd = __ballot(lane < nd && kid == d);
+      if (lane == 0) {
+        s_pq[i] = ft ? lane_value(kpt, __ffsll((long long)ft) - 1) : 0.0;
+        s_pq[G + i] = fd ? lane_value(kpd, __ffsll((long long)fd) - 1) : 0.0;
+      }
+    }
+  }
   __syncthreads();
+  if (!a.greedy && a.beta) {
+    // label of position i: sum over P's kept support of min(P, Q), in the
+    // order of P's kept list; one wave per position
+    for (int i = w; i < G; i += DT / 64) {
+      const int trow = rr.t0 + i, drow = a.n_trows + rr.d0 + i;
+      const int nt = a.ws.rkn[trow], nd = a.ws.rkn[drow];
+      const int kit = lane < nt ? a.ws.rki[size_t(trow) * TOPK_MAX + lane] : -1;
+      const double kpt = lane < nt ? a.ws.rkp[size_t(trow) * TOPK_MAX + lane] : 0.0;
+      const int kid = lane < nd ? a.ws.rki[size_t(drow) * TOPK_MAX + lane] : -2;
+      const double kpd = lane < nd ? a.ws.rkp[size_t(drow) * TOPK_MAX + lane] : 0.0;
+      const double q = kept_lookup(kit, kid, kpd, nd);
+      const double m = fmin(kpt, q);
+      double sm = 0.0;
+      for (int s2 = 0; s2 < nt; ++s2) sm += lane_value(m, s2);
+      if (lane == 0) a.beta[rr.d0 + i] = float(sm);
+    }
+  }
   if (w != 0) return;
 
   // decisions, one lane per drafted position (G <= 64)
@@ -651,22 +766,13 @@ __global__ __launch_bounds__(DT) void vb_decide(VerifyArgs a) {
     } else {
       double p = 0.0, q = 0.0;
       if (d >= 0 && d < a.V) {
-        p = kept_prob(a, trow, d);
-        q = kept_prob(a, drow, d);
+        p = s_pq[lane];      // target row of position lane
+        q = s_pq[G + lane];  // draft row of position lane
       }
       float p32 = float(p), q32 = float(q);
       ratio = p32 / q32;
       float u = a.uni[(size_t(rr.t0) + lane) * 2];
       acc = u < ratio;
-      if (a.beta) {
-        // sum over P's kept support of min(P, Q) (outside it min is 0)
-        const int n = a.ws.rkn[trow];
-        const int* ki = a.ws.rki + size_t(trow) * TOPK_MAX;
-        const double* kp = a.ws.rkp + size_t(trow) * TOPK_MAX;
-        double sm = 0.0;
-        for (int j = 0; j < n; ++j) sm += fmin(kp[j], kept_prob(a, drow, ki[j]));
-        a.beta[rr.d0 + lane] = float(sm);
-      }
     }
     if (a.ratio) a.ratio[rr.d0 + lane] = ratio;
   }
@@ -688,50 +794,47 @@ __global__ __launch_bounds__(DT) void vb_decide(VerifyArgs a) {
   // top-k: draw over the kept support (full-vocabulary sampling runs
   // vb_decide_sums instead of this kernel)
   const float u2 = a.uni[(size_t(rr.t0) + tau) * 2 + 1];
-  {
-    if (lane != 0) return;
-    // draw over P's kept support in vocabulary order
-    const int n = a.ws.rkn[trow];
-    const int* ki = a.ws.rki + size_t(trow) * TOPK_MAX;
-    const double* kp = a.ws.rkp + size_t(trow) * TOPK_MAX;
-    int idx[TOPK_MAX];
-    double wgt[TOPK_MAX];
-    for (int j = 0; j < n; ++j) { idx[j] = ki[j]; wgt[j] = kp[j]; }
-    // insertion sort by index
-    for (int j = 1; j < n; ++j) {
-      int ii = idx[j]; double ww = wgt[j]; int m = j - 1;
-      while (m >= 0 && idx[m] > ii) { idx[m + 1] = idx[m]; wgt[m + 1] = wgt[m]; --m; }
-      idx[m + 1] = ii; wgt[m + 1] = ww;
-    }
-    double Z = 0.0;
-    if (tau < G) {
-      const int drow = a.n_trows + rr.d0 + tau;
-      for (int j = 0; j < n; ++j) {
-        double r = wgt[j] - kept_prob(a, drow, idx[j]);
-        wgt[j] = r > 0.0 ? r : 0.0;
-        Z += wgt[j];
-      }
-      if (Z == 0.0) {
-        for (int j = 0; j < n; ++j) { wgt[j] = kept_prob(a, trow, idx[j]); Z += wgt[j]; }
-      }
-    } else {
-      for (int j = 0; j < n; ++j) Z += wgt[j];
-    }
-    const double tgt = double(u2) * Z;
-    int pick = -1;
-    double run = 0.0, mg = 0.0;
-    for (int j = 0; j < n; ++j) {
-      double prev = run;
-      run += wgt[j];
-      if (run > tgt) { pick = j; mg = fmin(tgt - prev, run - tgt); break; }
-    }
-    if (pick < 0) {
-      for (int j = n - 1; j >= 0; --j)
-        if (wgt[j] > 0.0) { pick = j; break; }
-      if (pick < 0) pick = n - 1;
-      mg = 0.0;
-    }
-    a.out[rr.t0 + tau] = idx[pick];
+  // draw over P's kept support in vocabulary order, the whole wave: lane s
+  // holds kept entry s; its rank by index orders the sequential sums
+  const int n = a.ws.rkn[trow];
+  const int idx = lane < n ? a.ws.rki[size_t(trow) * TOPK_MAX + lane] : INT32_MAX;
+  const double pw = lane < n ? a.ws.rkp[size_t(trow) * TOPK_MAX + lane] : 0.0;
+  int rank = 0;
+  for (int s2 = 0; s2 < n; ++s2) rank += lane_value(idx, s2) < idx;
+  double wt = pw;
+  if (tau < G) {
+    const int drow = a.n_trows + rr.d0 + tau;
+    const int nd = a.ws.rkn[drow];
+    const int kid = lane < nd ? a.ws.rki[size_t(drow) * TOPK_MAX + lane] : -2;
+    const double kpd = lane < nd ? a.ws.rkp[size_t(drow) * TOPK_MAX + lane] : 0.0;
+    const double r = pw - kept_lookup(idx, kid, kpd, nd);
+    wt = r > 0.0 ? r : 0.0;
+  }
+  // the lane holding rank k
+  auto at_rank = [&](int k2) { return __ffsll((long long)__ballot(lane < n && rank == k2)) - 1; };
+  double Z = 0.0;
+  for (int k2 = 0; k2 < n; ++k2) Z += lane_value(wt, at_rank(k2));
+  if (tau < G && Z == 0.0) {
+    wt = pw;  // the residual vanished: draw from P itself
+    for (int k2 = 0; k2 < n; ++k2) Z += lane_value(wt, at_rank(k2));
+  }
+  const double tgt = double(u2) * Z;
+  int pick = -1;
+  double run = 0.0, mg = 0.0;
+  for (int k2 = 0; k2 < n; ++k2) {
+    const double prev = run;
+    run += lane_value(wt, at_rank(k2));
+    if (run > tgt) { pick = k2; mg = fmin(tgt - prev, run - tgt); break; }
+  }
+  if (pick < 0) {
+    for (int k2 = n - 1; k2 >= 0; --k2)
+      if (lane_value(wt, at_rank(k2)) > 0.0) { pick = k2; break; }
+    if (pick < 0) pick = n - 1;
+    mg = 0.0;
+  }
+  const int tok = lane_value(idx, at_rank(pick));
+  if (lane == 0) {
+    a.out[rr.t0 + tau] = tok;
     if (a.margin) a.margin[b] = float(mg);
   }
 }
@@ -1416,6 +1519,12 @@ hipError_t launch_verify(const float* zt, const float* zd, const int* dtok, cons
     if (vec) hipLaunchKernelGGL(vb_draw_pick<true>, dim3(B), dim3(VT), 0, stream, a);
     else hipLaunchKernelGGL(vb_draw_pick<false>, dim3(B), dim3(VT), 0, stream, a);
   } else {
+    if (k > 0) {
+      // one wave per (request, row); LDS for a row's chunk lists (one record
+      // per chunk with a top-k filter)
+      const size_t lds = size_t(a.nch) * k * 8;
+      hipLaunchKernelGGL(vb_merge_rows, dim3(B, 2 * a.G + 1), dim3(64), lds, stream, a);
+    }
     hipLaunchKernelGGL(vb_decide, dim3(B), dim3(DT), 0, stream, a);
   }
   if (tprob || dprob)
