@@ -322,6 +322,17 @@ def next_rows(a, cfg, r, bd, torch, dev, stream, q, kb, vb, kc, vc, cache_base, 
                                                                    cfg.top_k, cfg.top_p, workspace=wsq), n=10)
         table_b.append(float(zt_q.shape[0]))
         table_v.append(1e6 / t)
+    # the same rows under the filtered sampling setting the DSpine article
+    # measures with (temperature 1, top-k 20, top-p 0.95)
+    wsk = torch.empty(max(1, bd.verify_block_workspace_size(B, G, V, 20)), dtype=torch.uint8, device=dev)
+    tk = torch.empty(B, dtype=torch.int32, device=dev)
+    ok_ = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+    t_k = _time_us(torch, stream, lambda: bd.verify_block(zt, zd, dtok, uni, 1.0, 20, 0.95, tau=tk, out_tokens=ok_,
+                                                          workspace=wsk))
+    kbytes = 4.0 * V * (B * (G + 1) + B * G)
+    ex["verify_block_topk"] = dict(workload=f"B={B} G={G} V={V}, T=1 top-k 20 top-p 0.95",
+                                   per_call_us=round(t_k, 2), achieved_gbs=round(kbytes / t_k / 1e3, 1),
+                                   frac=round(kbytes / t_k / 1e3 / HBM_PEAK_GBS, 4))
     ex["select_block"] = select_block(cfg, bd, torch, dev, stream, zd)
     ex["overlap"] = overlap_rounds(cfg, r, bd, torch, dev, q, kb, vb, zt, zd, dtok, uni)
     ex["inject_prefill"] = inject_prefill(cfg, r, bd, torch, dev, stream)

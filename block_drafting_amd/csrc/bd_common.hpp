@@ -156,6 +156,60 @@ __device__ __forceinline__ double lane_value(double x, int s) {
   return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
+// (value desc, index asc) order without branches
+__device__ __forceinline__ bool sel_better(float v, int i, float w, int j) {
+  return (v > w) | ((v == w) & (i < j));
+}
+
+// Wave-wide bitonic sort of one (value, index) pair per lane, best first:
+// lane 0 ends with the best.
+template <int K, int J>
+__device__ __forceinline__ void bitonic_step(float& sv, int& si) {
+  const int lane = threadIdx.x & 63;
+  const float ov = xor_lane<J>(sv);
+  const int oi = xor_lane<J>(si);
+  const bool lower = (lane & J) == 0, desc = (lane & K) == 0;
+  // in a descending run the lower lane keeps the better of the pair
+  const bool take = (lower == desc) ? sel_better(ov, oi, sv, si) : sel_better(sv, si, ov, oi);
+  sv = take ? ov : sv;
+  si = take ? oi : si;
+}
+template <int K, int J>
+__device__ __forceinline__ void bitonic_merge(float& sv, int& si) {
+  bitonic_step<K, J>(sv, si);
+  if constexpr (J > 1) bitonic_merge<K, J / 2>(sv, si);
+}
+template <int K>
+__device__ __forceinline__ void bitonic_sort(float& sv, int& si) {
+  if constexpr (K > 2) bitonic_sort<K / 2>(sv, si);
+  bitonic_merge<K, K / 2>(sv, si);
+}
+__device__ __forceinline__ void wave_sort_best_first(float& sv, int& si) { bitonic_sort<64>(sv, si); }
+
+// Order-preserving 32-bit keys of finite or infinite floats: a < b exactly
+// when key(a) < key(b), with -0 taken as +0 so that equal values get equal
+// keys.  key_value inverts it (giving +0 for either zero).
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// The n-th largest (1 <= n <= 64) of the wave's 64 keys (one per lane),
+// found bit by bit from the top: the largest T with at least n keys >= T,
+// which is always one of the keys.  One compare and one ballot count per bit.
+__device__ __forceinline__ uint32_t wave_nth_key(uint32_t k, int n) {
+  uint32_t T = 0;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = T | (1u << b);
+    if (__popcll(__ballot(k >= c)) >= n) T = c;
+  }
+  return T;
+}
+
 // every lane gets the wave's best (value, index) pair (lowest index on ties)
 template <int J>
 __device__ __forceinline__ void argmax_step(float& v, int& i) {

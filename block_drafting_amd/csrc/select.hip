@@ -57,13 +57,6 @@ struct SelArgs {
 
 // the total order: larger value first, then lower index (no short circuit:
 // the compiler keeps it a select rather than a branch)
-__device__ __forceinline__ bool sel_better(float v, int i, float w, int j) {
-  return (v > w) | ((v == w) & (i < j));
-}
-
-// The value of lane l ^ J, without the LDS permute path: DPP row moves for
-// J <= 8 (quad permutations; 4 = half-mirror then reversed quad, 8 = mirror
-// then half-mirror), v_permlane16_swap / v_permlane32_swap for 16 and 32.
 // keep the better of this lane's (v, i) and lane l ^ J's
 template <int J>
 __device__ __forceinline__ void keep_better(float& v, int& i) {
@@ -82,53 +75,6 @@ __device__ __forceinline__ int sel_slot(int start, int s, int t) {
 
 // one (value, index) per lane, sorted best first across the wave (bitonic
 // network over the lanes)
-template <int K, int J>
-__device__ __forceinline__ void bitonic_step(float& sv, int& si) {
-  const int lane = threadIdx.x & 63;
-  const float ov = xor_lane<J>(sv);
-  const int oi = xor_lane<J>(si);
-  const bool lower = (lane & J) == 0, desc = (lane & K) == 0;
-  // in a descending run the lower lane keeps the better of the pair
-  const bool take = (lower == desc) ? sel_better(ov, oi, sv, si) : sel_better(sv, si, ov, oi);
-  sv = take ? ov : sv;
-  si = take ? oi : si;
-}
-template <int K, int J>
-__device__ __forceinline__ void bitonic_merge(float& sv, int& si) {
-  bitonic_step<K, J>(sv, si);
-  if constexpr (J > 1) bitonic_merge<K, J / 2>(sv, si);
-}
-template <int K>
-__device__ __forceinline__ void bitonic_sort(float& sv, int& si) {
-  if constexpr (K > 2) bitonic_sort<K / 2>(sv, si);
-  bitonic_merge<K, K / 2>(sv, si);
-}
-__device__ __forceinline__ void wave_sort_best_first(float& sv, int& si) { bitonic_sort<64>(sv, si); }
-
-// Order-preserving 32-bit keys of finite or infinite floats: a < b exactly
-// when key(a) < key(b), with -0 taken as +0 so that equal values get equal
-// keys.  key_value inverts it (giving +0 for either zero).
-__device__ __forceinline__ uint32_t order_key(float v) {
-  const uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_value(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-
-// The NC-th largest of the wave's 64 keys (one per lane), found bit by bit
-// from the top: the largest T with at least NC keys >= T, which is always one
-// of the keys.  One compare and one ballot count per bit.
-__device__ __forceinline__ uint32_t wave_nth_key(uint32_t k) {
-  uint32_t T = 0;
-#pragma unroll
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t c = T | (1u << b);
-    if (__popcll(__ballot(k >= c)) >= NC) T = c;
-  }
-  return T;
-}
-
 // ------------------------------------------------------------- chunk top-16
 template <bool VEC>
 __global__ __launch_bounds__(ST) void sel_chunk_top(SelArgs a) {
@@ -180,7 +126,7 @@ __global__ __launch_bounds__(ST) void sel_chunk_top(SelArgs a) {
   // lane maxima is among its wave's 16 largest.
   {
     const uint32_t kb = order_key(bv);
-    const uint32_t tw = wave_nth_key(kb);
+    const uint32_t tw = wave_nth_key(kb, NC);
     const bool p = kb >= tw;  // at least NC lanes
     const unsigned long long m = __ballot(p);
     const int pos = __builtin_amdgcn_mbcnt_hi(unsigned(m >> 32), __builtin_amdgcn_mbcnt_lo(unsigned(m), 0u));
@@ -189,7 +135,7 @@ __global__ __launch_bounds__(ST) void sel_chunk_top(SelArgs a) {
   if (t == 0) s_over = 0;
   __syncthreads();
   if (w == 0) {
-    const uint32_t tc = wave_nth_key(s_k[lane]);
+    const uint32_t tc = wave_nth_key(s_k[lane], NC);
     if (lane == 0) s_tk = tc;
   }
   __syncthreads();

@@ -355,6 +355,8 @@ __global__ __launch_bounds__(VT) void vb_stats(VerifyArgs a) {
   __shared__ int s_ci[4 * CAND_PER_WAVE];
   __shared__ int s_cn[4];
   __shared__ int s_over;
+  __shared__ uint32_t s_kk[4 * 64];  // per wave: its k largest lane-maximum keys
+  __shared__ uint32_t s_tk;
 
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int row = blockIdx.x / a.nch;
@@ -394,62 +396,72 @@ __global__ __launch_bounds__(VT) void vb_stats(VerifyArgs a) {
 
   if (a.topk > 0) {
     const int k = a.topk;
-    // Per wave: the k-th largest lane maximum bounds the chunk's k best that
-    // live in this wave from below (the wave alone has k elements at least as
-    // large), so only elements >= it can be among them.
-    float srt = wave_sort_desc(lane_best);
-    float thr = __shfl(srt, k - 1);
-    int cnt = 0;
-#pragma unroll
-    for (int s = 0; s < VPT; ++s) {
-      int e = start + slot_offset<VEC>(s, t);
-      cnt += (e < a.V && x[s] >= thr) ? 1 : 0;
+    // The chunk's k-th largest lane maximum bounds its k best from below (k
+    // elements are at least that large).  Each wave finds its own k-th
+    // largest lane maximum by a bitwise search over order-preserving keys and
+    // hands its k lane maxima at or above it to wave 0, which takes the k-th
+    // largest of those 4k: the chunk's k largest lane maxima are among them.
+    {
+      const uint32_t kb = order_key(lane_best);
+      const uint32_t tw = wave_nth_key(kb, k);
+      const bool p = kb >= tw;  // at least k lanes
+      const unsigned long long m = __ballot(p);
+      const int pos = __builtin_amdgcn_mbcnt_hi(unsigned(m >> 32), __builtin_amdgcn_mbcnt_lo(unsigned(m), 0u));
+      if (p && pos < k) s_kk[w * 64 + pos] = kb;
     }
-    // exclusive prefix of cnt over the wave
-    int incl = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    int total = __shfl(incl, 63);
     if (t == 0) s_over = 0;
     __syncthreads();
-    if (total > CAND_PER_WAVE) {
-      if (lane == 0) s_over = 1;
-    } else {
-      int pos = incl - cnt;
+    if (w == 0) {
+      uint32_t k4[4];
 #pragma unroll
-      for (int s = 0; s < VPT; ++s) {
-        int e = start + slot_offset<VEC>(s, t);
-        if (e < a.V && x[s] >= thr) {
-          s_cv[w * CAND_PER_WAVE + pos] = x[s];
-          s_ci[w * CAND_PER_WAVE + pos] = e;
-          ++pos;
-        }
+      for (int w2 = 0; w2 < 4; ++w2) k4[w2] = lane < k ? s_kk[w2 * 64 + lane] : 0u;  // key 0: no element
+      uint32_t T = 0;
+#pragma unroll
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) cnt += __popcll(__ballot(k4[w2] >= cand));
+        if (cnt >= k) T = cand;
       }
-      if (lane == 0) s_cn[w] = total;
+      if (lane == 0) s_tk = T;
     }
+    __syncthreads();
+    const float thr = key_value(s_tk);
+    // candidates: elements at or above the bound, appended per wave by a
+    // ballot per slot (at most CAND_PER_WAVE per wave)
+    int total = 0;
+#pragma unroll
+    for (int s = 0; s < VPT; ++s) {
+      const int e = start + slot_offset<VEC>(s, t);
+      const bool p = (e < a.V) & (x[s] >= thr);
+      const unsigned long long m = __ballot(p);
+      if (m) {
+        const int pos = total + __builtin_amdgcn_mbcnt_hi(unsigned(m >> 32), __builtin_amdgcn_mbcnt_lo(unsigned(m), 0u));
+        if (p && pos < CAND_PER_WAVE) { s_cv[w * CAND_PER_WAVE + pos] = x[s]; s_ci[w * CAND_PER_WAVE + pos] = e; }
+        total += __popcll(m);
+      }
+    }
+    if (lane == 0) s_cn[w] = total;
+    if (total > CAND_PER_WAVE && lane == 0) s_over = 1;
     __syncthreads();
     float* ov = a.ws.ctv + rc * k;
     int* oi = a.ws.cti + rc * k;
-    if (!s_over) {
-      // rank every candidate against all others (strict total order)
-      for (int cidx = t; cidx < 4 * CAND_PER_WAVE; cidx += VT) {
-        int cw = cidx / CAND_PER_WAVE, cj = cidx - cw * CAND_PER_WAVE;
-        if (cj >= s_cn[cw]) continue;
-        float v = s_cv[cidx];
-        int id = s_ci[cidx];
-        int rank = 0;
-        for (int w2 = 0; w2 < 4; ++w2)
-          for (int j2 = 0; j2 < s_cn[w2]; ++j2) {
-            int o = w2 * CAND_PER_WAVE + j2;
-            rank += better(s_cv[o], s_ci[o], v, id) ? 1 : 0;
-          }
-        if (rank < k) { ov[rank] = v; oi[rank] = id; }
+    const int n0 = s_cn[0], n01 = n0 + s_cn[1], n012 = n01 + s_cn[2], n_all = n012 + s_cn[3];
+    if (!s_over && n_all <= 64) {
+      // wave 0 sorts all candidates best first (empty lanes last) and keeps k
+      if (w == 0) {
+        float v = -INFINITY;
+        int id = INT32_MAX;
+        if (lane < n_all) {
+          const int ww = (lane >= n0) + (lane >= n01) + (lane >= n012);
+          const int off = lane - (ww == 0 ? 0 : ww == 1 ? n0 : ww == 2 ? n01 : n012);
+          v = s_cv[ww * CAND_PER_WAVE + off];
+          id = s_ci[ww * CAND_PER_WAVE + off];
+        }
+        wave_sort_best_first(v, id);
+        if (lane < k) { ov[lane] = v; oi[lane] = id; }
       }
-      int n_all = s_cn[0] + s_cn[1] + s_cn[2] + s_cn[3];
-      for (int r = n_all + t; r < k; r += VT) { ov[r] = -INFINITY; oi[r] = INT32_MAX; }
     } else {
       // exact fallback: k rounds, each taking the best element strictly
       // after the previous pick in (value desc, index asc) order
