@@ -462,6 +462,37 @@ __global__ __launch_bounds__(VT) void vb_stats(VerifyArgs a) {
         wave_sort_best_first(v, id);
         if (lane < k) { ov[lane] = v; oi[lane] = id; }
       }
+    } else if (!s_over) {
+      // more than 64 in all (k near 64): each wave sorts its own list, then
+      // wave 0 takes the k best by a 4-way merge (lane q < 4 holding list q's
+      // head, the round's winner advancing)
+      float v = -INFINITY;
+      int id = INT32_MAX;
+      if (lane < s_cn[w]) { v = s_cv[w * CAND_PER_WAVE + lane]; id = s_ci[w * CAND_PER_WAVE + lane]; }
+      wave_sort_best_first(v, id);
+      __syncthreads();
+      s_cv[w * CAND_PER_WAVE + lane] = v;  // sorted, empty entries last
+      s_ci[w * CAND_PER_WAVE + lane] = id;
+      __syncthreads();
+      if (w == 0) {
+        int hq = 0;
+        float hv = lane < 4 ? s_cv[lane * CAND_PER_WAVE] : -INFINITY;
+        int hi = lane < 4 ? s_ci[lane * CAND_PER_WAVE] : INT32_MAX;
+        float ov_l = -INFINITY;
+        int oi_l = INT32_MAX;
+        for (int r = 0; r < k; ++r) {
+          float bv = hv;
+          int bi = hi;
+          wave_argmax(bv, bi);
+          if (lane == r) { ov_l = bv; oi_l = bi; }
+          if (bi != INT32_MAX && hi == bi) {  // indices are distinct: one lane wins
+            ++hq;
+            hv = hq < CAND_PER_WAVE ? s_cv[lane * CAND_PER_WAVE + hq] : -INFINITY;
+            hi = hq < CAND_PER_WAVE ? s_ci[lane * CAND_PER_WAVE + hq] : INT32_MAX;
+          }
+        }
+        if (lane < k) { ov[lane] = ov_l; oi[lane] = oi_l; }
+      }
     } else {
       // exact fallback: k rounds, each taking the best element strictly
       // after the previous pick in (value desc, index asc) order
