@@ -147,7 +147,8 @@ def test_sampling_parity(B, G, V, sigma, T, seed):
 
 @pytest.mark.parametrize("B,G,V,k,p,seed", [(8, 15, 30000, 20, 0.95, 20), (4, 7, 151936, 64, 1.0, 21),
                                             (4, 7, 5000, 1, 0.9, 22), (6, 5, 12345, 20, 0.5, 23),
-                                            (3, 2, 10, 5, 0.8, 24)])
+                                            (3, 2, 10, 5, 0.8, 24), (4, 7, 151936, 40, 0.9, 25),
+                                            (2, 5, 151936, 50, 1.0, 26)])
 def test_topk_topp_parity(B, G, V, k, p, seed):
     say(f"top-k B={B} G={G} V={V} k={k} p={p}")
     zt, zd, dt, u = synth(B, G, V, 0.3, seed, T=1.0, top_k=k)
