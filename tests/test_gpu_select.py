@@ -93,6 +93,7 @@ def tables(rng, V, r, std):
     (2, 3, 40001, 32, 3),       # V % 4 != 0: scalar loads
     (3, 6, 9000, 40, 11),       # ranks that are no multiple of the 32-element k step
     (2, 5, 17000, 200, 12),
+    (1, 1, 5000, 16, 15),       # one request, one drafted position: only the anchor row
 ])
 def test_random_parity(B, G, V, r, seed):
     rng = np.random.default_rng(seed)
