@@ -141,6 +141,9 @@ int verify_block(const float* target_logits, const float* draft_logits,
   if (!(temperature >= 0.f) || temperature == INFINITY || top_p != top_p)
     return fail(BD_E_SHAPE, "verify_block: temperature must be finite and >= 0, top_p not NaN");
   if (top_k > 64) return fail(BD_E_UNSUPPORTED, "verify_block: top_k must be <= 64 (got %d)", top_k);
+  if (temperature > 0.f && top_p < 1.f && (top_k == 0 || top_k >= V))
+    return fail(BD_E_UNSUPPORTED, "verify_block: a top-p filter needs a top-k filter with 0 < top_k < V "
+                "(got top_k=%d, V=%d, top_p=%g)", top_k, V, double(top_p));
   if (G > 64) return fail(BD_E_UNSUPPORTED, "verify_block: G must be <= 64 (got %d)", G);
   if ((long long)B * (2 * G + 1) * ((V + 8191) / 8192) > 0x7fffffffLL)
     return fail(BD_E_UNSUPPORTED, "verify_block: too many (row, chunk) pairs");
@@ -188,6 +191,9 @@ int verify_block_ragged(const float* target_logits, const float* draft_logits,
   if (!(temperature >= 0.f) || temperature == INFINITY || top_p != top_p)
     return fail(BD_E_SHAPE, "verify_block_ragged: temperature must be finite and >= 0, top_p not NaN");
   if (top_k > 64) return fail(BD_E_UNSUPPORTED, "verify_block_ragged: top_k must be <= 64 (got %d)", top_k);
+  if (temperature > 0.f && top_p < 1.f && (top_k == 0 || top_k >= V))
+    return fail(BD_E_UNSUPPORTED, "verify_block_ragged: a top-p filter needs a top-k filter with 0 < top_k < V "
+                "(got top_k=%d, V=%d, top_p=%g)", top_k, V, double(top_p));
   if (G_max > 64) return fail(BD_E_UNSUPPORTED, "verify_block_ragged: G_max must be <= 64 (got %d)", G_max);
   if ((2LL * n_target_rows - B) * ((V + 8191) / 8192) > 0x7fffffffLL)
     return fail(BD_E_UNSUPPORTED, "verify_block_ragged: too many (row, chunk) pairs");

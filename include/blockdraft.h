@@ -179,7 +179,10 @@ int draft_block_attn(const uint16_t* q, const uint16_t* k_blk, const uint16_t* v
  *             (greedy: 1 on a match, else 0).
  * sample_margin optional device fp32 [B]: distance of u' * total to the
  *             nearer running-sum boundary of the drawn token (greedy: +inf).
- * Supported: 0 <= top_k <= 64; G <= 64; V >= 1.
+ * Supported: 0 <= top_k <= 64; G <= 64; V >= 1.  A top-p filter (top_p < 1
+ * with temperature > 0) is supported only together with a top-k filter
+ * (0 < top_k < V), whose kept set bounds the tokens top-p sorts; without one
+ * the call returns BD_E_UNSUPPORTED (there is no full-vocabulary top-p).
  * ------------------------------------------------------------------------ */
 size_t verify_block_workspace_size(int32_t B, int32_t G, int32_t V, int32_t top_k);
 
@@ -221,7 +224,8 @@ int verify_block(const float* target_logits, const float* draft_logits,
  *             each drafted position under the verification distributions
  *             (greedy: 1 when the two lowest-index maxima agree, else 0).
  * n_target_rows, G_max: host values; n_target_rows <= B * (G_max + 1).
- * Supported: 0 <= top_k <= 64; G_max <= 64; V >= 1.
+ * Supported: 0 <= top_k <= 64; G_max <= 64; V >= 1; top-p only with a top-k
+ * filter, as verify_block.
  * ------------------------------------------------------------------------ */
 size_t verify_block_ragged_workspace_size(int32_t B, int32_t n_target_rows, int32_t G_max, int32_t V,
                                           int32_t top_k, int32_t want_beta);

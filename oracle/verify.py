@@ -95,6 +95,34 @@ def inverse_cdf(weights: np.ndarray, u: float):
     return x, margin
 
 
+def draw_weights(P_i: np.ndarray, Q_i=None) -> np.ndarray:
+    """Weights of the replacement / extra draw at one position: max(0, P - Q)
+    at a rejection (P itself if those all vanish), P alone when every draft
+    was kept (Q_i is None)."""
+    if Q_i is None:
+        return np.asarray(P_i, dtype=np.float64)
+    w = np.maximum(0.0, np.asarray(P_i, np.float64) - np.asarray(Q_i, np.float64))
+    if w.sum() == 0.0:
+        w = np.asarray(P_i, dtype=np.float64)
+    return w
+
+
+def cdf_distance(weights: np.ndarray, u: float, x: int) -> float:
+    """Distance of u * sum(w) to token x's interval [cumsum(w)[x-1], cumsum(w)[x])
+    of the inverse-CDF draw (0 when x is the token drawn; +inf for a token of
+    zero weight, which the draw can never emit)."""
+    w = np.asarray(weights, dtype=np.float64)
+    if not (0 <= x < len(w)) or w[x] <= 0.0:
+        return float("inf")
+    c = np.cumsum(w)
+    t = float(np.float64(u) * c[-1])
+    lo = c[x - 1] if x > 0 else 0.0
+    hi = c[x]
+    if lo <= t < hi:
+        return 0.0
+    return float(min(abs(t - lo), abs(t - hi)))
+
+
 def verify(z_target, z_draft, draft_tokens, uniforms, temperature: float,
            top_k: int = 0, top_p: float = 1.0, want_probs: bool = False):
     """Verify a batch of drafted blocks.
@@ -161,12 +189,7 @@ def verify(z_target, z_draft, draft_tokens, uniforms, temperature: float,
                 break
         tau[b] = t
         out[b, :t] = d[:t]
-        if t < G:
-            w = np.maximum(0.0, P[t] - Q[t])
-            if w.sum() == 0.0:
-                w = P[t]
-        else:
-            w = P[G]
+        w = draw_weights(P[t], Q[t] if t < G else None)
         x, mg = inverse_cdf(w, float(np.float32(uniforms[b, t, 1])))
         out[b, t] = x
         margin[b] = mg

@@ -60,6 +60,13 @@ def test_verify_validation_codes(lib):
     assert _verify(lib, T=-1.0) == bd.BD_E_SHAPE
     assert _verify(lib, T=float("nan")) == bd.BD_E_SHAPE
     assert _verify(lib, k=65) == bd.BD_E_UNSUPPORTED
+    # top-p without a top-k filter (k = 0 or k >= V) is not supported when sampling
+    assert _verify(lib, k=0, p=0.9) == bd.BD_E_UNSUPPORTED
+    assert _verify(lib, V=50, k=50, p=0.9) == bd.BD_E_UNSUPPORTED
+    assert _verify(lib, V=50, k=60, p=0.9) == bd.BD_E_UNSUPPORTED
+    assert "top-p" in bd.last_error()
+    assert _verify(lib, B=0, k=20, p=0.9) == bd.BD_OK
+    assert _verify(lib, B=0, T=0.0, zd=None, u=None, k=0, p=0.9) == bd.BD_OK   # greedy ignores the filters
     assert _verify(lib, G=65) == bd.BD_E_UNSUPPORTED
     assert _verify(lib, zt=(1 << 20) + 4) == bd.BD_E_UNSUPPORTED   # misaligned logits
     assert _verify(lib, wsb=16) == bd.BD_E_WORKSPACE
@@ -146,6 +153,7 @@ def test_ragged_verify_validation_codes(lib):
     assert _ragged(lib, N=11) == bd.BD_E_SHAPE                      # more than B * (G_max + 1)
     assert _ragged(lib, Gm=65, N=7) == bd.BD_E_UNSUPPORTED
     assert _ragged(lib, k=65) == bd.BD_E_UNSUPPORTED
+    assert _ragged(lib, k=0, p=0.95) == bd.BD_E_UNSUPPORTED          # top-p needs a top-k filter
     assert _ragged(lib, wsb=16) == bd.BD_E_WORKSPACE
     # greedy without drafts at all: only target rows; B = 0 is a no-op
     assert _ragged(lib, B=0, N=0) == bd.BD_OK

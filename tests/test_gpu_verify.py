@@ -12,7 +12,7 @@ import torch
 
 import workloads as wl
 from oracle import verify as ov
-from tests.helpers import say
+from tests.helpers import check_request, f32, say
 
 pytestmark = pytest.mark.gpu
 
@@ -50,28 +50,38 @@ def run_gpu(zt, zd, dt, u, T, k=0, p=1.0, probs=False):
     return res
 
 
-def compare(o, g, u, greedy, label=""):
-    """Exact agreement per request, except requests with a near-tie decision."""
+def oracle_verify(zt, zd, dt, u, T, k=0, p=1.0, **kw):
+    """The oracle with the temperature and top-p the kernel receives (fp32)."""
+    return ov.verify(zt, zd, dt, u, f32(T), k, f32(p), **kw)
+
+
+def compare(o, g, u, greedy, label="", zt=None, zd=None, T=1.0, k=0, p=1.0):
+    """Decision-exact agreement per request (tests.helpers.check_request):
+    only the first decision where the paths part may differ, and only as a
+    near tie on that very decision.  Prints and checks the excused count."""
     B = len(o["tau"])
-    near = 0
+    G = o["out_tokens"].shape[1] - 1
+    kinds = []
     for b in range(B):
-        same = o["tau"][b] == g["tau"][b] and (o["out_tokens"][b] == g["out_tokens"][b]).all()
-        if same:
-            continue
-        assert not greedy, f"{label}: greedy request {b} differs: {o['out_tokens'][b]} vs {g['out_tokens'][b]}"
-        t = min(o["tau"][b], g["tau"][b])
-        tie = False
-        for i in range(t + 1):
-            if i < len(g["accept_ratio"][b]) and (abs(float(u[b, i, 0]) - float(g["accept_ratio"][b, i])) < NEAR or
-                                                  abs(float(u[b, i, 0]) - float(o["accept_ratio"][b, i])) < NEAR):
-                tie = True
-        if o["sample_margin"][b] < NEAR or g["sample_margin"][b] < NEAR:
-            tie = True
-        assert tie, (f"{label}: request {b} differs outside a near-tie: oracle tau={o['tau'][b]} "
-                     f"{o['out_tokens'][b]} gpu tau={g['tau'][b]} {g['out_tokens'][b]}")
-        near += 1
-    say(f"{label}: {B} requests, {near} near-tie differences, oracle near-ties {int(o['near_ties'].sum())}")
-    return near
+        def weights(t, b=b):
+            P = ov.filtered_probs(zt[b, t], f32(T), k, f32(p))
+            Q = ov.filtered_probs(zd[b, t], f32(T), k, f32(p)) if t < G else None
+            return ov.draw_weights(P, Q)
+        uu = u[b] if u is not None else np.zeros((G + 1, 2), np.float32)
+        kind = check_request(label, b, greedy, int(o["tau"][b]), int(g["tau"][b]), o["out_tokens"][b],
+                             g["out_tokens"][b], o["accept_ratio"][b], g["accept_ratio"][b], uu[:G, 0], uu[:, 1],
+                             weights, NEAR)
+        if kind is not None:
+            kinds.append((b, kind))
+    oracle_near = set(np.nonzero(o["near_ties"] > 0)[0].tolist())
+    for b, kind in kinds:
+        # a draw flip lies within 1e-6 of the oracle's own boundary, so the
+        # oracle counted it; an accept flip may be near only on the kernel's ratio
+        if kind == "draw":
+            assert b in oracle_near, f"{label}: excused draw of request {b} not among the oracle's near ties"
+    say(f"{label}: {B} requests, {len(kinds)} excused near-tie differences {kinds}, "
+        f"oracle near-tie requests {len(oracle_near)}")
+    return len(kinds)
 
 
 def check_ratios(o, g):
@@ -139,9 +149,9 @@ def test_greedy_config_tiny_inputs():
 def test_sampling_parity(B, G, V, sigma, T, seed):
     say(f"sampling B={B} G={G} V={V} T={T}")
     zt, zd, dt, u = synth(B, G, V, sigma, seed, T=T)
-    o = ov.verify(zt, zd, dt, u, T)
+    o = oracle_verify(zt, zd, dt, u, T)
     g = run_gpu(zt, zd, dt, u, T)
-    compare(o, g, u, greedy=False, label="sampling")
+    compare(o, g, u, greedy=False, label="sampling", zt=zt, zd=zd, T=T)
     check_ratios(o, g)
 
 
@@ -152,9 +162,9 @@ def test_sampling_parity(B, G, V, sigma, T, seed):
 def test_topk_topp_parity(B, G, V, k, p, seed):
     say(f"top-k B={B} G={G} V={V} k={k} p={p}")
     zt, zd, dt, u = synth(B, G, V, 0.3, seed, T=1.0, top_k=k)
-    o = ov.verify(zt, zd, dt, u, 1.0, k, p)
+    o = oracle_verify(zt, zd, dt, u, 1.0, k, p)
     g = run_gpu(zt, zd, dt, u, 1.0, k, p)
-    compare(o, g, u, greedy=False, label="topk")
+    compare(o, g, u, greedy=False, label="topk", zt=zt, zd=zd, T=1.0, k=k, p=p)
     check_ratios(o, g)
 
 
@@ -167,16 +177,16 @@ def test_topk_with_tied_logits():
     dt = rng.integers(0, 40, (B, G)).astype(np.int32)
     u = rng.random((B, G + 1, 2), dtype=np.float32)
     for k, p in ((20, 0.95), (64, 1.0)):
-        o = ov.verify(zt, zd, dt, u, 1.0, k, p)
+        o = oracle_verify(zt, zd, dt, u, 1.0, k, p)
         g = run_gpu(zt, zd, dt, u, 1.0, k, p)
-        compare(o, g, u, greedy=False, label=f"topk ties k={k}")
+        compare(o, g, u, greedy=False, label=f"topk ties k={k}", zt=zt, zd=zd, T=1.0, k=k, p=p)
 
 
 @pytest.mark.parametrize("T,k,p", [(0.0, 0, 1.0), (1.0, 0, 1.0), (0.8, 20, 0.95)])
 def test_probabilities_within_1e5(T, k, p):
     say(f"probs T={T} k={k}")
     zt, zd, dt, u = synth(2, 3, 20000, 0.5, 40, T=max(T, 1.0), top_k=k)
-    o = ov.verify(zt, zd, dt, u, T, k, p, want_probs=True)
+    o = oracle_verify(zt, zd, dt, u, T, k, p, want_probs=True)
     if T == 0.0:
         # greedy: plain softmax of the raw logits for both rows
         o["draft_probs"] = np.stack([np.stack([ov.softmax(zd[b, i]) for i in range(3)]) for b in range(2)])
@@ -214,8 +224,8 @@ def test_gpu_lossless_chi_square(V, k, p):
     N = 200_000
     zt1 = (rng.standard_normal((2, V)) * 1.2).astype(np.float32)
     zd1 = (rng.standard_normal((1, V)) * 1.2).astype(np.float32)
-    P = ov.filtered_probs(zt1[0], 1.0, k, p)
-    Q = ov.filtered_probs(zd1[0], 1.0, k, p)
+    P = ov.filtered_probs(zt1[0], 1.0, k, f32(p))
+    Q = ov.filtered_probs(zd1[0], 1.0, k, f32(p))
     dt = rng.choice(V, size=(N, 1), p=Q).astype(np.int32)
     u = rng.random((N, 2, 2), dtype=np.float32)
     zt = np.broadcast_to(zt1, (N, 2, V)).copy()
@@ -238,9 +248,9 @@ def test_full_size_8b_sampling():
     """The batch-32 temperature-1 workload at full size (every request)."""
     say("full-size qwen3-8b verify")
     r = wl.make_round(wl.CONFIGS["qwen3-8b"], parts=("verify",))
-    o = ov.verify(r.z_target, r.z_draft, r.draft_tokens, r.uniforms, 1.0)
+    o = oracle_verify(r.z_target, r.z_draft, r.draft_tokens, r.uniforms, 1.0)
     g = run_gpu(r.z_target, r.z_draft, r.draft_tokens, r.uniforms, 1.0)
-    compare(o, g, r.uniforms, greedy=False, label="qwen3-8b")
+    compare(o, g, r.uniforms, greedy=False, label="qwen3-8b", zt=r.z_target, zd=r.z_draft, T=1.0)
     check_ratios(o, g)
     say(f"tau mean {g['tau'].mean():.3f}")
 
@@ -252,9 +262,10 @@ def test_full_size_sweep_topk_subset():
     r = wl.make_round(wl.CONFIGS["sweep-b128"], parts=("verify",))
     g = run_gpu(r.z_target, r.z_draft, r.draft_tokens, r.uniforms, 1.0, 20, 0.95)
     sel = np.arange(0, 128, 8)
-    o = ov.verify(r.z_target[sel], r.z_draft[sel], r.draft_tokens[sel], r.uniforms[sel], 1.0, 20, 0.95)
+    o = oracle_verify(r.z_target[sel], r.z_draft[sel], r.draft_tokens[sel], r.uniforms[sel], 1.0, 20, 0.95)
     gs = {k: v[sel] for k, v in g.items() if v is not None}
-    compare(o, gs, r.uniforms[sel], greedy=False, label="sweep-b128")
+    compare(o, gs, r.uniforms[sel], greedy=False, label="sweep-b128", zt=r.z_target[sel], zd=r.z_draft[sel],
+            T=1.0, k=20, p=0.95)
     check_ratios(o, gs)
 
 

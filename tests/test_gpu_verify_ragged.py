@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from oracle import verify as ov
-from tests.helpers import say
+from tests.helpers import check_request, f32, say
 from tests.test_gpu_verify import NEAR, synth
 
 pytestmark = pytest.mark.gpu
@@ -44,22 +44,28 @@ def run_ragged(zt, zd, dt, u, row_cu, G_max, T, k=0, p=1.0, want_beta=True, row_
                 sample_margin=margin.cpu().numpy(), beta=beta.cpu().numpy()[:N - B] if want_beta else None)
 
 
-def compare(o, g, u, row_cu, greedy, label):
+def compare(o, g, u, row_cu, greedy, label, zt=None, zd=None, T=1.0, k=0, p=1.0):
+    """Decision-exact agreement per request (tests.helpers.check_request)."""
     B = len(row_cu) - 1
-    near = 0
+    kinds = []
     for b in range(B):
-        t0, t1 = row_cu[b], row_cu[b + 1]
+        t0, t1 = int(row_cu[b]), int(row_cu[b + 1])
         d0 = t0 - b
-        if o["tau"][b] == g["tau"][b] and (o["out_tokens"][t0:t1] == g["out_tokens"][t0:t1]).all():
-            continue
-        assert not greedy, f"{label}: greedy request {b} differs"
-        t = min(o["tau"][b], g["tau"][b])
-        tie = any(abs(float(u[t0 + i, 0]) - float(x["accept_ratio"][d0 + i])) < NEAR
-                  for i in range(min(t + 1, t1 - t0 - 1)) for x in (o, g))
-        tie = tie or o["sample_margin"][b] < NEAR or g["sample_margin"][b] < NEAR
-        assert tie, f"{label}: request {b} differs outside a near-tie"
-        near += 1
-    say(f"{label}: {B} requests, {near} near-tie differences")
+        G = t1 - t0 - 1
+
+        def weights(t, t0=t0, d0=d0, G=G):
+            P = ov.filtered_probs(zt[t0 + t], f32(T), k, f32(p))
+            Q = ov.filtered_probs(zd[d0 + t], f32(T), k, f32(p)) if t < G else None
+            return ov.draw_weights(P, Q)
+        kind = check_request(label, b, greedy, int(o["tau"][b]), int(g["tau"][b]), o["out_tokens"][t0:t1],
+                             g["out_tokens"][t0:t1], o["accept_ratio"][d0:d0 + G], g["accept_ratio"][d0:d0 + G],
+                             u[t0:t0 + G, 0], u[t0:t1, 1], weights, NEAR)
+        if kind is not None:
+            kinds.append((b, kind))
+            if kind == "draw":
+                assert o["near_ties"][b] > 0, f"{label}: excused draw of request {b} not an oracle near tie"
+    say(f"{label}: {B} requests, {len(kinds)} excused near-tie differences {kinds}, "
+        f"oracle near-tie requests {int((o['near_ties'] > 0).sum())}")
 
 
 CASES = [
@@ -77,9 +83,9 @@ def test_ragged_parity_and_labels(B, G_list, V, sigma, T, k, p, seed):
     G_max = max(G_list)
     zt, zd, dt, u = synth(B, G_max, V, sigma, seed, T=max(T, 1.0), top_k=k)
     zt_p, zd_p, dt_p, u_p, row_cu = pack(zt, zd, dt, u, G_list)
-    o = ov.verify_ragged(zt_p, zd_p, dt_p, u_p, row_cu, T, k, p, want_beta=True)
+    o = ov.verify_ragged(zt_p, zd_p, dt_p, u_p, row_cu, f32(T), k, f32(p), want_beta=True)
     g = run_ragged(zt_p, zd_p, dt_p, u_p, row_cu, G_max, T, k, p)
-    compare(o, g, u_p, row_cu, greedy=(T == 0.0), label="ragged")
+    compare(o, g, u_p, row_cu, greedy=(T == 0.0), label="ragged", zt=zt_p, zd=zd_p, T=T, k=k, p=p)
     tol = 0.0 if T == 0.0 else (1e-6 if k else 2e-5)
     err = np.abs(g["beta"] - o["beta"]).max() if len(o["beta"]) else 0.0
     say(f"  label max abs err {err:.2e}")
@@ -109,7 +115,7 @@ def test_benchmark_shape_ragged_mix():
     zt_p, zd_p, dt_p, u_p, row_cu = pack(zt, zd, dt, u, G_list)
     o = ov.verify_ragged(zt_p, zd_p, dt_p, u_p, row_cu, 1.0, want_beta=True)
     g = run_ragged(zt_p, zd_p, dt_p, u_p, row_cu, 15, 1.0)
-    compare(o, g, u_p, row_cu, greedy=False, label="bench mix")
+    compare(o, g, u_p, row_cu, greedy=False, label="bench mix", zt=zt_p, zd=zd_p, T=1.0)
     assert np.abs(g["beta"] - o["beta"]).max() <= 2e-5
 
 
