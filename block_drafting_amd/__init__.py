@@ -27,7 +27,7 @@ EXPORTS = (
     "blockdraft_last_error",
     "inject_kv_workspace_size", "inject_kv",
     "draft_block_attn_workspace_size", "draft_block_attn",
-    "verify_block_workspace_size", "verify_block",
+    "verify_block_workspace_size", "verify_block", "verify_block_noalloc",
     "verify_block_ragged_workspace_size", "verify_block_ragged",
     "prefix_schedule", "commit_round",
     "draft_forward_workspace_size", "draft_forward",
@@ -73,6 +73,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     L.verify_block_workspace_size.argtypes = [c_i32] * 4
     L.verify_block.restype = ctypes.c_int
     L.verify_block.argtypes = [c_p] * 4 + [c_i32] * 3 + [c_f, c_i32, c_f] + [c_p] * 6 + [c_p, c_sz, c_p]
+    L.verify_block_noalloc.restype = ctypes.c_int
+    L.verify_block_noalloc.argtypes = [c_p] * 4 + [c_i32] * 3 + [c_f, c_i32, c_f] + [c_p] * 6 + [c_p]
     L.verify_block_ragged_workspace_size.restype = c_sz
     L.verify_block_ragged_workspace_size.argtypes = [c_i32] * 6
     L.verify_block_ragged.restype = ctypes.c_int
@@ -220,6 +222,35 @@ def verify_block(target_logits, draft_logits, draft_tokens, uniforms, temperatur
                              B, G, V, float(temperature), int(top_k), float(top_p), _ptr(tau), _ptr(out_tokens),
                              _ptr(target_probs), _ptr(draft_probs), _ptr(accept_ratio), _ptr(sample_margin),
                              _ptr(ws), nb, _stream(stream))
+    _check(st)
+    return tau, out_tokens
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def verify_block_noalloc(target_logits, draft_logits, draft_tokens, uniforms, temperature: float = 0.0,
+                         top_k: int = 0, top_p: float = 1.0, tau=None, out_tokens=None, target_probs=None,
+                         draft_probs=None, accept_ratio=None, sample_margin=None, stream=None):
+    """verify_block without a workspace: the library's static per-GPU scratch
+    array holds the intermediate records (calls that overlap on one GPU race).
+    The outputs must be passed in when the caller cannot allocate. Returns
+    (tau, out_tokens)."""
+    B, G1, V = target_logits.shape
+    G = G1 - 1
+    dev = target_logits.device
+    _typed(target_logits, torch.float32, "target_logits")
+    _typed(draft_logits, torch.float32, "draft_logits")
+    _typed(draft_tokens, torch.int32, "draft_tokens")
+    _typed(uniforms, torch.float32, "uniforms")
+    if tau is None:
+        tau = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+    st = load().verify_block_noalloc(_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(uniforms),
+                                     B, G, V, float(temperature), int(top_k), float(top_p), _ptr(tau),
+                                     _ptr(out_tokens), _ptr(target_probs), _ptr(draft_probs), _ptr(accept_ratio),
+                                     _ptr(sample_margin), _stream(stream))
     _check(st)
     return tau, out_tokens
 

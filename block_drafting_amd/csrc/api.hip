@@ -9,6 +9,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -127,6 +129,44 @@ size_t verify_block_workspace_size(int32_t B, int32_t G, int32_t V, int32_t top_
   return bd::verify_ws_bytes(B, B * (G + 1), V, top_k, false);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Host checks shared by verify_block and verify_block_noalloc (everything but
+// the workspace).
+int verify_checks(const char* who, const float* target_logits, const float* draft_logits,
+                  const int32_t* draft_tokens, const float* uniforms, int32_t B, int32_t G, int32_t V,
+                  float temperature, int32_t top_k, float top_p, int32_t* tau, int32_t* out_tokens,
+                  float* draft_probs) {
+  if (B < 0 || G < 0 || V < 1 || top_k < 0)
+    return fail(BD_E_SHAPE, "%s: need B >= 0, G >= 0, V >= 1, top_k >= 0 (got B=%d G=%d V=%d top_k=%d)", who,
+                B, G, V, top_k);
+  if (!(temperature >= 0.f) || temperature == INFINITY || top_p != top_p)
+    return fail(BD_E_SHAPE, "%s: temperature must be finite and >= 0, top_p not NaN", who);
+  if (top_k > 64) return fail(BD_E_UNSUPPORTED, "%s: top_k must be <= 64 (got %d)", who, top_k);
+  if (temperature > 0.f && top_p < 1.f && (top_k == 0 || top_k >= V))
+    return fail(BD_E_UNSUPPORTED, "%s: a top-p filter needs a top-k filter with 0 < top_k < V "
+                "(got top_k=%d, V=%d, top_p=%g)", who, top_k, V, double(top_p));
+  if (G > 64) return fail(BD_E_UNSUPPORTED, "%s: G must be <= 64 (got %d)", who, G);
+  if ((long long)B * (2 * G + 1) * ((V + 8191) / 8192) > 0x7fffffffLL)
+    return fail(BD_E_UNSUPPORTED, "%s: too many (row, chunk) pairs", who);
+  const bool greedy = temperature == 0.f;
+  if (!target_logits || !tau || !out_tokens || (G > 0 && !draft_tokens))
+    return fail(BD_E_NULL, "%s: target_logits, draft_tokens, tau and out_tokens are required", who);
+  if (!greedy && (!uniforms || (G > 0 && !draft_logits)))
+    return fail(BD_E_NULL, "%s: sampling needs draft_logits and uniforms", who);
+  if (draft_probs && G > 0 && !draft_logits)
+    return fail(BD_E_NULL, "%s: draft_probs needs draft_logits", who);
+  if (!aligned16(target_logits) || (draft_logits && !aligned16(draft_logits)))
+    return fail(BD_E_UNSUPPORTED, "%s: logits must be 16-byte aligned", who);
+  return BD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int verify_block(const float* target_logits, const float* draft_logits,
                  const int32_t* draft_tokens, const float* uniforms,
                  int32_t B, int32_t G, int32_t V,
@@ -135,27 +175,9 @@ int verify_block(const float* target_logits, const float* draft_logits,
                  float* target_probs, float* draft_probs,
                  float* accept_ratio, float* sample_margin,
                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (B < 0 || G < 0 || V < 1 || top_k < 0)
-    return fail(BD_E_SHAPE, "verify_block: need B >= 0, G >= 0, V >= 1, top_k >= 0 (got B=%d G=%d V=%d top_k=%d)",
-                B, G, V, top_k);
-  if (!(temperature >= 0.f) || temperature == INFINITY || top_p != top_p)
-    return fail(BD_E_SHAPE, "verify_block: temperature must be finite and >= 0, top_p not NaN");
-  if (top_k > 64) return fail(BD_E_UNSUPPORTED, "verify_block: top_k must be <= 64 (got %d)", top_k);
-  if (temperature > 0.f && top_p < 1.f && (top_k == 0 || top_k >= V))
-    return fail(BD_E_UNSUPPORTED, "verify_block: a top-p filter needs a top-k filter with 0 < top_k < V "
-                "(got top_k=%d, V=%d, top_p=%g)", top_k, V, double(top_p));
-  if (G > 64) return fail(BD_E_UNSUPPORTED, "verify_block: G must be <= 64 (got %d)", G);
-  if ((long long)B * (2 * G + 1) * ((V + 8191) / 8192) > 0x7fffffffLL)
-    return fail(BD_E_UNSUPPORTED, "verify_block: too many (row, chunk) pairs");
-  const bool greedy = temperature == 0.f;
-  if (!target_logits || !tau || !out_tokens || (G > 0 && !draft_tokens))
-    return fail(BD_E_NULL, "verify_block: target_logits, draft_tokens, tau and out_tokens are required");
-  if (!greedy && (!uniforms || (G > 0 && !draft_logits)))
-    return fail(BD_E_NULL, "verify_block: sampling needs draft_logits and uniforms");
-  if (draft_probs && G > 0 && !draft_logits)
-    return fail(BD_E_NULL, "verify_block: draft_probs needs draft_logits");
-  if (!aligned16(target_logits) || (draft_logits && !aligned16(draft_logits)))
-    return fail(BD_E_UNSUPPORTED, "verify_block: logits must be 16-byte aligned");
+  const int st = verify_checks("verify_block", target_logits, draft_logits, draft_tokens, uniforms, B, G, V,
+                               temperature, top_k, top_p, tau, out_tokens, draft_probs);
+  if (st != BD_OK) return st;
   const size_t need = verify_block_workspace_size(B, G, V, top_k);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(BD_E_WORKSPACE, "verify_block: workspace of %zu bytes needed, %zu given", need,
@@ -314,6 +336,71 @@ int prefix_schedule(const float* survival, const int32_t* survival_cu, int32_t R
     return fail(BD_E_NULL, "prefix_schedule: sps_b, sps_v, survival_cu and ell are required");
   bd::prefix_schedule(survival, survival_cu, R, sps_b, sps_v, n_sps, ell, theta);
   return ok();
+}
+
+}  // extern "C"
+
+// ----------------------------------------------------- verify_block_noalloc
+// verify_block for callers that cannot allocate device memory: the records,
+// kept lists and draw jobs live in a file-scope device array instead of a
+// caller workspace.  Each device holds its own copy of the array from the
+// first call on it until the process ends.  The host-side name `scratch` is
+// only a stand-in for that array: its device address is looked up once per
+// device (with the device current) and only that address reaches the kernels.
+namespace bd {
+__device__ __align__(256) uint8_t scratch[BD_NOALLOC_SCRATCH_BYTES];
+}  // namespace bd
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+int scratch_address(const char* who, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BD_E_LAUNCH, "%s: hipGetDevice failed: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(BD_E_UNSUPPORTED, "%s: device %d beyond %d", who, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(bd::scratch));
+    if (e != hipSuccess || !p)
+      return fail(BD_E_LAUNCH, "%s: hipGetSymbolAddress of the scratch array failed: %s", who, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int verify_block_noalloc(const float* target_logits, const float* draft_logits,
+                         const int32_t* draft_tokens, const float* uniforms,
+                         int32_t B, int32_t G, int32_t V,
+                         float temperature, int32_t top_k, float top_p,
+                         int32_t* tau, int32_t* out_tokens,
+                         float* target_probs, float* draft_probs,
+                         float* accept_ratio, float* sample_margin, hipStream_t stream) {
+  const int st = verify_checks("verify_block_noalloc", target_logits, draft_logits, draft_tokens, uniforms, B, G, V,
+                               temperature, top_k, top_p, tau, out_tokens, draft_probs);
+  if (st != BD_OK) return st;
+  const size_t need = verify_block_workspace_size(B, G, V, top_k);
+  if (need > BD_NOALLOC_SCRATCH_BYTES)
+    return fail(BD_E_WORKSPACE, "verify_block_noalloc: this call needs %zu bytes of scratch, more than the "
+                "%zu of the static array", need, (size_t)BD_NOALLOC_SCRATCH_BYTES);
+  if (B == 0) return ok();
+  void* ws = nullptr;
+  const int sa = scratch_address("verify_block_noalloc", &ws);
+  if (sa != BD_OK) return sa;
+  return launched(bd::launch_verify(target_logits, draft_logits, draft_tokens, uniforms, nullptr, B, B * (G + 1), G,
+                                    V, temperature, top_k, top_p, tau, out_tokens, target_probs, draft_probs,
+                                    accept_ratio, sample_margin, nullptr, ws, stream),
+                  "verify_block_noalloc");
 }
 
 }  // extern "C"

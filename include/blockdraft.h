@@ -196,6 +196,29 @@ int verify_block(const float* target_logits, const float* draft_logits,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * verify_block_noalloc -- verify_block for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation, arguments and
+ * outputs as verify_block, without the workspace.  Its scratch space is a
+ * static device array of BD_NOALLOC_SCRATCH_BYTES bytes per GPU, held from
+ * the first call on a GPU until the process ends; the call itself allocates
+ * nothing.  A call whose verify_block_workspace_size(B, G, V, top_k) exceeds
+ * that size returns BD_E_WORKSPACE without launching.  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (several streams or
+ * host threads at once) race and give undefined results; calls ordered on
+ * one stream are safe.  Nothing in the array needs to start at zero.
+ * ------------------------------------------------------------------------ */
+#define BD_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+int verify_block_noalloc(const float* target_logits, const float* draft_logits,
+                         const int32_t* draft_tokens, const float* uniforms,
+                         int32_t B, int32_t G, int32_t V,
+                         float temperature, int32_t top_k, float top_p,
+                         int32_t* tau, int32_t* out_tokens,
+                         float* target_probs, float* draft_probs,
+                         float* accept_ratio, float* sample_margin, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * verify_block_ragged -- verify_block with a drafted length per request and
  * the confidence label of every drafted position (DSpark tutorial,
  * confidence-scheduled verification: the prefix scheduler picks a verify

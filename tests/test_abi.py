@@ -213,3 +213,22 @@ def test_select_block_validation_codes(lib):
     assert sel(B=0, z=None, tok=None) == bd.BD_OK  # nothing to do
     assert lib.select_block_workspace_size(2, 3, 1000) > 0
     assert lib.select_block_workspace_size(0, 3, 1000) == 0
+
+
+def test_noalloc_verify_size_limit_on_the_host(lib):
+    # the size check comes before any device call, so it runs without a GPU
+    F = ctypes.c_float
+    need = lib.verify_block_workspace_size(256, 15, 151936, 64)
+    assert need > bd.NOALLOC_SCRATCH_BYTES
+    st = lib.verify_block_noalloc(1 << 20, 1 << 20, 1 << 20, 1 << 20, 256, 15, 151936, F(1.0), 64, F(1.0),
+                                  1 << 20, 1 << 20, None, None, None, None, None)
+    assert st == bd.BD_E_WORKSPACE
+    assert "static array" in bd.last_error()
+    # the same argument checks as verify_block
+    assert lib.verify_block_noalloc(None, 1 << 20, 1 << 20, 1 << 20, 2, 3, 100, F(1.0), 0, F(1.0), 1 << 20, 1 << 20,
+                                    None, None, None, None, None) == bd.BD_E_NULL
+    assert lib.verify_block_noalloc(1 << 20, 1 << 20, 1 << 20, 1 << 20, 2, 3, 100, F(1.0), 0, F(0.9), 1 << 20,
+                                    1 << 20, None, None, None, None, None) == bd.BD_E_UNSUPPORTED
+    # B = 0 needs no scratch and launches nothing
+    assert lib.verify_block_noalloc(1 << 20, 1 << 20, 1 << 20, 1 << 20, 0, 3, 100, F(1.0), 0, F(1.0), 1 << 20,
+                                    1 << 20, None, None, None, None, None) == bd.BD_OK
