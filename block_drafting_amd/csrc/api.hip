@@ -44,7 +44,7 @@ const char* blockdraft_last_error(void) { return g_err; }
 // ------------------------------------------------------------------ inject_kv
 size_t inject_kv_workspace_size(int32_t M, int32_t d_in, int32_t L, int32_t n_kv, int32_t hd) {
   if (M <= 0 || d_in <= 0 || L <= 0 || n_kv <= 0 || hd <= 0) return 0;
-  return bd::inject_ws_bytes(M, d_in, L * 2 * n_kv * hd);
+  return bd::inject_ws_bytes(M, d_in, L, n_kv, hd);
 }
 
 int inject_kv(const uint16_t* h_target, const uint16_t* w_kv, const uint16_t* k_norm_w,

@@ -74,6 +74,32 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// sin and cos of a rotary angle given in fp64 (any size, e.g. position x
+// frequency): Cody-Waite reduction by pi/2 in fp64 with a two-term pi/2, so the
+// reduced |y| <= pi/4 keeps the angle's accuracy at positions in the tens of
+// thousands; then the Taylor polynomials of sin (to y^9) and cos (to y^10) in
+// fp32, whose truncation is below 2e-9 on |y| <= pi/4; then the quadrant's
+// swap and signs.  Absolute error below 1e-7 (checked against libm in fp64).
+__device__ __forceinline__ void sincos_angle(double ang, float* s_out, float* c_out) {
+  const double q = rint(ang * 0.63661977236758134);  // 2 / pi
+  double y = fma(-q, 1.5707963267948966, ang);
+  y = fma(-q, 6.123233995736766e-17, y);
+  const float x = float(y), x2 = x * x;
+  float s = fmaf(x2, 1.f / 362880.f, -1.f / 5040.f);
+  s = fmaf(x2, s, 1.f / 120.f);
+  s = fmaf(x2, s, -1.f / 6.f);
+  s = fmaf(x2 * x, s, x);
+  float c = fmaf(x2, -1.f / 3628800.f, 1.f / 40320.f);
+  c = fmaf(x2, c, -1.f / 720.f);
+  c = fmaf(x2, c, 1.f / 24.f);
+  c = fmaf(x2, c, -0.5f);
+  c = fmaf(x2, c, 1.f);
+  const int quad = int(q - 4.0 * floor(q * 0.25));  // q mod 4
+  const float ss = (quad & 1) ? c : s, cc = (quad & 1) ? s : c;
+  *s_out = (quad & 2) ? -ss : ss;
+  *c_out = ((quad + 1) & 2) ? -cc : cc;
+}
+
 // 2^x with the hardware instruction (no denormal-result handling): used for
 // softmax terms exp((z - max) / T), where a result below 2^-126 is negligible
 // next to the term 1 of the maximum itself.

@@ -7,7 +7,7 @@
 
 namespace bd {
 
-size_t inject_ws_bytes(int M, int d_in, int N);
+size_t inject_ws_bytes(int M, int d_in, int L, int n_kv, int hd);
 hipError_t launch_inject(const uint16_t* h, const uint16_t* w, const uint16_t* gain, const int32_t* row_cu,
                          const int32_t* row_pos0, const int64_t* cache_base, uint16_t* kc, uint16_t* vc,
                          int64_t T_cap, int B, int M, int d_in, int L, int n_kv, int hd, float theta,

@@ -82,13 +82,9 @@ __global__ __launch_bounds__(256) void fw_qk_norm_rope(QkArgs a) {
     const float inv = 1.0f / sqrtf(ss / float(hd) + a.eps);
     const uint16_t* g = head < a.n_q ? a.gq : a.gk;
     const float va = xa * inv * bf16_to_f32(g[d]), vb = xb * inv * bf16_to_f32(g[half + d]);
-    // angle pos * theta^(-2d/hd) in fp64, reduced to [-pi, pi], fp32 sin / cos
-    const double ang = double(pos) * a.inv_freq[d];
-    const double k = rint(ang * 0.15915494309189535);
-    double r = fma(-k, 6.283185307179586, ang);
-    r = fma(-k, 2.4492935982947064e-16, r);
+    // angle pos * theta^(-2d/hd) in fp64, reduced in fp64, fp32 sin / cos
     float sn, cs;
-    sincosf(float(r), &sn, &cs);
+    sincos_angle(double(pos) * a.inv_freq[d], &sn, &cs);
     uint16_t* dst = head < a.n_q ? a.q + (size_t(m) * a.n_q + head) * hd
                                  : a.kb + (size_t(m) * a.n_kv + (head - a.n_q)) * hd;
     dst[d] = f32_to_bf16(va * cs - vb * sn);

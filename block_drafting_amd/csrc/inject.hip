@@ -132,27 +132,34 @@ __global__ __launch_bounds__(GT) void ik_gemm(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------- wide-M projection
-// For M > 256: one workgroup computes a 512 x 128 tile over its d_in range, so
-// every weight row is read from HBM once (the rows of H are re-read from L2).
-// Eight waves as 4 (M) x 2 (N), each a 128 x 64 tile of 32x32x16 MFMAs (16
-// waves of 64 x 64 or 4 of 128 x 128 measured slower).  Both
-// operands reach LDS straight from global memory (global_load_lds, 16 bytes per
-// lane) through rings of SA (H) and SW (W) stages of BK-wide d_in steps; in
-// iteration k a loading wave issues its W loads of step k + SW - 1, then its H loads of
-// step k + SA - 1 (SW >= SA, so the W loads of a step are always older than its
-// H loads).  A row is BK / 8 pieces of 16 bytes; the pieces of each 256-byte
-// line are XOR-permuted so the operand reads (16 lanes: 16 rows, one piece
-// each) are conflict-free.
-constexpr int WBM = 512, WBN = 128;
-#ifndef BD_GEMM_WIDE_WAVES
-#define BD_GEMM_WIDE_WAVES 8
-#endif
-constexpr int WNW = BD_GEMM_WIDE_WAVES;  // 16: 8 (M) x 2 (N) of 64 x 64; 8: 4 x 2 of 128 x 64; 4: 4 x 1 of 128 x 128
-constexpr int WNT = 64 * WNW;
-constexpr int WMW = WNW == 16 ? 8 : 4;   // waves along M
-constexpr int WNWN = WNW / WMW;          // waves along N
-constexpr int WFM = WBM / WMW / 32;      // 32-row blocks per wave
-constexpr int WFN = WBN / WNWN / 32;     // 32-column blocks per wave
+// For M > 256: one workgroup computes a 256 x 256 output tile (two heads of one
+// layer's K or V block at hd 128) over its d_in range; the two row tiles of a
+// column block and the d_in splits of a tile sit at launch indices congruent
+// modulo 8, so they share an XCD and its L2.  Eight waves as 4 (M) x 2 (N), each
+// a 64 x 128 tile of 32x32x16 MFMAs: a wave holds whole heads, so the RMSNorm
+// sum of a row is a reduction over 32 lanes and the rotary pairs (d, d + hd/2)
+// sit in the same lane.  Both operands reach LDS straight from global memory
+// (global_load_lds, 16 bytes per lane) through rings of SA (H) and SW (W)
+// stages of BK-wide d_in steps; in iteration k a loading wave issues its W loads
+// of step k + SW - 1, then its H loads of step k + SA - 1 (SW >= SA, so the W
+// loads of a step are always older than its H loads).  A row is BK / 8 pieces of
+// 16 bytes; the pieces of each 256-byte line are XOR-permuted so the operand
+// reads (16 lanes: 16 rows, one piece each) are conflict-free.
+//
+// The split over d_in is reduced inside the kernel: the splits of a tile count
+// their arrival on a per-tile counter; every split but the last stores its fp32
+// partial (agent-coherent stores, so the store is visible at the device's
+// coherence point once it completes) and then counts itself ready; the last
+// one waits for those S - 1, adds the partials in split order (so the sum is
+// the same whichever split arrives last) and runs the epilogue: per-head
+// RMSNorm and gain, rotary embedding at the row's position, bf16, and the
+// scatter into the cache slots.  With no split the epilogue runs directly.
+constexpr int WBM = 256, WBN = 256;
+constexpr int WNW = 8, WNT = 64 * WNW;
+constexpr int WMW = 4, WNWN = 2;          // waves along M and along N
+constexpr int WFM = WBM / WMW / 32;       // 32-row blocks per wave (2)
+constexpr int WFN = WBN / WNWN / 32;      // 32-column blocks per wave (4)
+static_assert(WFN == 4, "a wave spans 128 columns");
 #ifndef BD_GEMM_WIDE_BK
 #define BD_GEMM_WIDE_BK 64
 #endif
@@ -208,7 +215,106 @@ __device__ __forceinline__ int wide_younger(int k, int ns) {
   return n;
 }
 
-__global__ __launch_bounds__(WNT) void ik_gemm_wide(GemmArgs g) {
+struct ProjArgs {
+  const uint16_t* A;        // [M, Kd]
+  const uint16_t* Bw;       // [N, Kd]
+  float* part;              // [S][M][N] partial sums (S > 1)
+  const int64_t* rslot;     // [M] cache slot of each row, -1 if the row is not written
+  const int32_t* rpos;      // [M] absolute position of each row
+  const uint16_t* gain;     // [L][hd] or NULL
+  const int32_t* row_cu;
+  const int32_t* row_pos0;
+  const int64_t* cache_base;
+  uint16_t* kc;
+  uint16_t* vc;
+  int64_t T_cap;
+  int M, N, Kd, S, steps_per_split, tiles_n;
+  int B, n_kv;
+  float eps;
+  double inv_freq[64];
+};
+
+// Epilogue of one tile from the summed accumulators.  The tile is computed
+// transposed (D = W . H^T), so in block (i, j) lane (lr, h) holds row
+// 64 wm + 32 i + lr of the tile at the 16 columns 128 wn + 32 j + 8 q + 4 h + e
+// (r = 4 q + e).  K heads get RMSNorm x gain and the rotary embedding, V heads
+// are copied; both are rounded to bf16 and written to the row's cache slot,
+// four consecutive dims per 8-byte store.  lds_g / lds_f: this tile's gains
+// (fp32) and inverse frequencies (fp64) staged in LDS.
+template <int HD>
+__device__ __forceinline__ void proj_epilogue(const ProjArgs& a, floatx16 (&acc)[WFM][WFN], int n0, int wn,
+                                              int lane, const int64_t (&slot)[WFM], const int (&pos)[WFM],
+                                              const float* lds_g, const double* lds_f) {
+  constexpr int BPH = HD / 32;                // 32-column blocks per head
+  const int h = lane >> 5;
+  const int c0 = n0 + 128 * wn;               // first column of this wave
+  const int kvw = a.n_kv * HD;                // columns of one layer's K (or V) block
+  const int blk = c0 / kvw;
+  const int l = blk >> 1;
+  const bool is_k = (blk & 1) == 0;
+  const int g0 = (c0 - blk * kvw) / HD;       // first head of this wave
+  uint16_t* cache = is_k ? a.kc : a.vc;
+#pragma clang loop unroll(full)
+  for (int i = 0; i < WFM; ++i) {
+    if (is_k) {
+      // RMS over each head: this lane's 16 values per block, then the other half
+      float s0 = 0.f, s1 = 0.f;
+#pragma clang loop unroll(full)
+      for (int j = 0; j < 4; ++j)
+#pragma clang loop unroll(full)
+        for (int r = 0; r < 16; ++r) {
+          const float v = acc[i][j][r];
+          if (HD == 128 || j < 2) s0 += v * v; else s1 += v * v;
+        }
+      s0 += xor_lane<32>(s0);
+      if constexpr (HD == 64) s1 += xor_lane<32>(s1);
+      const float inv0 = 1.0f / sqrtf(s0 / float(HD) + a.eps);
+      const float inv1 = HD == 128 ? inv0 : 1.0f / sqrtf(s1 / float(HD) + a.eps);
+      // fully unrolled: the accumulators are indexed by r (a loop left rolled
+      // would put them in private memory)
+#pragma clang loop unroll(full)
+      for (int r = 0; r < 16; ++r) {
+        const int dd = 8 * (r >> 2) + 4 * h + (r & 3);  // dim within a 32-column block
+        // angle pos * theta^(-2d/hd) in fp64, reduced in fp64; HD 128: dims dd
+        // and 32 + dd; HD 64: dim dd (both heads)
+        float sn[2], cs[2];
+#pragma clang loop unroll(full)
+        for (int pp = 0; pp < (HD == 128 ? 2 : 1); ++pp)
+          sincos_angle(double(pos[i]) * lds_f[32 * pp + dd], &sn[pp], &cs[pp]);
+        if constexpr (HD == 64) {
+          sn[1] = sn[0];
+          cs[1] = cs[0];
+        }
+        // pairs (d, d + hd/2): HD 128 blocks (0, 2) and (1, 3); HD 64 (0, 1) and (2, 3)
+#pragma clang loop unroll(full)
+        for (int pp = 0; pp < 2; ++pp) {
+          const int ja = HD == 128 ? pp : 2 * pp, jb = HD == 128 ? pp + 2 : 2 * pp + 1;
+          const int d = (HD == 128 ? 32 * pp : 0) + dd;
+          const float inv = (HD == 128 || pp == 0) ? inv0 : inv1;
+          const float xa = acc[i][ja][r] * inv * lds_g[d];
+          const float xb = acc[i][jb][r] * inv * lds_g[d + HD / 2];
+          acc[i][ja][r] = xa * cs[pp] - xb * sn[pp];
+          acc[i][jb][r] = xb * cs[pp] + xa * sn[pp];
+        }
+      }
+    }
+    if (slot[i] >= 0) {
+      uint16_t* dst = cache + ((size_t(l) * a.T_cap + slot[i]) * a.n_kv + g0) * HD;
+#pragma clang loop unroll(full)
+      for (int j = 0; j < 4; ++j)
+#pragma clang loop unroll(full)
+        for (int q = 0; q < 4; ++q) {
+          const int col = (j / BPH) * HD + 32 * (j % BPH) + 8 * q + 4 * h;
+          const uint2 v = make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                     pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+          *reinterpret_cast<uint2*>(dst + col) = v;
+        }
+    }
+  }
+}
+
+template <int HD>
+__global__ __launch_bounds__(WNT) void ik_proj(ProjArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t ringA[WSA * WA_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t ringW[WSW * WW_BYTES];
   constexpr int P = WBK / 8;
@@ -224,8 +330,9 @@ __global__ __launch_bounds__(WNT) void ik_gemm_wide(GemmArgs g) {
   const uint32_t lA = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ringA)));
   const uint32_t lW = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ringW)));
 
-  // per-lane byte offsets of this wave's loads from the step's first column:
-  // load q of a loading wave fills piece slots 64 (w + WLW q) + lane of a stage
+  // per-lane byte offsets of this wave's loads from the tile's first row at the
+  // step's first column: load q of a loading wave fills piece slots
+  // 64 (w + WLW q) + lane of a stage
   uint32_t offA[WA_PW], offW[WW_PW];
 #pragma unroll
   for (int q = 0; q < WA_PW; ++q) {
@@ -234,7 +341,7 @@ __global__ __launch_bounds__(WNT) void ik_gemm_wide(GemmArgs g) {
     constexpr int RPL = 16 / P;
     const int line = ps >> 4, lc = (ps & 15) ^ (line & (P - 1));
     const int row = line * RPL + lc / P, c = lc % P;
-    const int m = min(m0 + row, g.M - 1);  // rows past M re-read row M - 1; never stored
+    const int m = min(m0 + row, g.M - 1) - m0;  // rows past M re-read row M - 1; never stored
     offA[q] = uint32_t(m * g.Kd * 2 + c * 16);
   }
 #pragma unroll
@@ -245,7 +352,7 @@ __global__ __launch_bounds__(WNT) void ik_gemm_wide(GemmArgs g) {
     const int row = line * RPL + lc / P, c = lc % P;
     offW[q] = uint32_t(row * g.Kd * 2 + c * 16);
   }
-  const uint16_t* Abase = g.A + size_t(step0) * WBK;
+  const uint16_t* Abase = g.A + size_t(m0) * g.Kd + size_t(step0) * WBK;
   const uint16_t* Wbase = g.Bw + size_t(n0) * g.Kd + size_t(step0) * WBK;
 
   floatx16 acc[WFM][WFN];
@@ -309,7 +416,7 @@ __global__ __launch_bounds__(WNT) void ik_gemm_wide(GemmArgs g) {
       for (int i = 0; i < WFM; ++i)
 #pragma unroll
         for (int j = 0; j < WFN; ++j) {
-          acc[i][j] = mfma32x32x16(af[i], bfr[j], acc[i][j]);
+          acc[i][j] = mfma32x32x16(bfr[j], af[i], acc[i][j]);  // D = W . H^T
           const int m = (kk * WFM + i) * WFN + j;
           if (m % EVERY == 0 && m / EVERY < NDMA) refill(m / EVERY);
         }
@@ -319,21 +426,76 @@ __global__ __launch_bounds__(WNT) void ik_gemm_wide(GemmArgs g) {
     for (int d = (NMF + EVERY - 1) / EVERY; d < NDMA; ++d) refill(d);
   }
 
-  // C block layout: lane holds column (lane & 31), rows 8 (r / 4) + 4 h + r % 4
-  float* P_ = g.P + size_t(split) * g.M * g.N;
+  // ------------------------------------------------ split over d_in: partials
+  // With a split, the fp32 partial goes to P[split][m][n] for the finish pass
+  // (four consecutive columns per 16-byte store).  A reduction inside this
+  // kernel (the last split of a tile adding the others' partials) was measured
+  // slower: the one reducing CU per tile must read the other splits' 512 KB at
+  // its own load rate, which costs as much as the finish pass over all CUs.
+  if (g.S > 1) {
+    float* P = g.part + size_t(split) * g.M * g.N;
 #pragma unroll
-  for (int i = 0; i < WFM; ++i)
+    for (int i = 0; i < WFM; ++i) {
+      const int m = m0 + 64 * wm + 32 * i + lr;
+      if (m >= g.M) continue;
 #pragma unroll
-    for (int j = 0; j < WFN; ++j) {
-      const int n = n0 + 32 * (WFN * wn + j) + lr;
+      for (int j = 0; j < WFN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + 32 * (WFM * wm + i) + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < g.M) P_[size_t(m) * g.N + n] = acc[i][j][r];
-      }
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + 128 * wn + 32 * j + 8 * q + 4 * h;
+          *reinterpret_cast<floatx4*>(P + size_t(m) * g.N + n) =
+              floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        }
     }
+    return;
+  }
+
+  // ------------------------------------------------ epilogue
+  // this lane's two output rows (64 wm + 32 i + lr): cache slot and position
+  int64_t rslot[WFM];
+  int rpos[WFM];
+#pragma unroll
+  for (int i = 0; i < WFM; ++i) {
+    const int m = m0 + 64 * wm + 32 * i + lr;
+    rslot[i] = m < g.M ? g.rslot[m] : -1;
+    rpos[i] = m < g.M ? g.rpos[m] : 0;
+  }
+  __syncthreads();  // the rings are free: this tile's gains and frequencies go there
+  const int kvw = g.n_kv * HD;
+  const int l = n0 / (2 * kvw);
+  float* lds_g = reinterpret_cast<float*>(ringW);
+  double* lds_f = reinterpret_cast<double*>(ringW + HD * 4);
+  for (int d = t; d < HD; d += WNT) lds_g[d] = g.gain ? bf16_to_f32(g.gain[l * HD + d]) : 1.f;
+  // static indices into the argument array (an indexed argument array would be
+  // copied to private memory)
+#pragma unroll
+  for (int d = 0; d < HD / 2; ++d)
+    if (t == d) lds_f[d] = g.inv_freq[d];
+  __syncthreads();
+  proj_epilogue<HD>(g, acc, n0, wn, lane, rslot, rpos, lds_g, lds_f);
 }
 
+// Before an unsplit projection: the cache slot (-1: not written) and absolute
+// position of every row.
+__global__ void ik_prep(ProjArgs a) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.M) return;
+  int64_t slot = -1;
+  int pos = 0;
+  if (a.B > 0 && i < a.row_cu[a.B]) {
+    int lo = 0, hi = a.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.row_cu[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    const int jrow = i - a.row_cu[lo];
+    pos = a.row_pos0[lo] + jrow;
+    const int64_t s = a.cache_base[lo] + pos;
+    if (jrow >= 0 && s >= 0 && s < a.T_cap) slot = s;
+  }
+  const_cast<int64_t*>(a.rslot)[i] = slot;
+  const_cast<int32_t*>(a.rpos)[i] = pos;
+}
 struct FinishArgs {
   const float* P;  // [S][M][N]
   const uint16_t* gain;  // [L][hd] or NULL
@@ -398,14 +560,9 @@ __global__ __launch_bounds__(256) void ik_finish(FinishArgs f) {
         gb = bf16_to_f32(f.gain[l * hd + half + i]);
       }
       const float a = xa[c] * inv * ga, bb = xb[c] * inv * gb;
-      // angle pos * theta^(-2i/hd) in fp64, reduced to [-pi, pi] before the
-      // fp32 sine / cosine
-      const double ang = double(pos) * f.inv_freq[i];
-      const double k = rint(ang * 0.15915494309189535);
-      double r = fma(-k, 6.283185307179586, ang);
-      r = fma(-k, 2.4492935982947064e-16, r);
+      // angle pos * theta^(-2i/hd) in fp64, reduced in fp64
       float sn, cs;
-      sincosf(float(r), &sn, &cs);
+      sincos_angle(double(pos) * f.inv_freq[i], &sn, &cs);
       oa[c] = f32_to_bf16(a * cs - bb * sn);
       ob[c] = f32_to_bf16(bb * cs + a * sn);
     }
@@ -451,12 +608,18 @@ struct GemmPlan {
   bool wide;
 };
 
-// M > 256: 512 x 128 tiles of the wide kernel, d_in split until about one
-// workgroup per CU runs.  Otherwise 256 x BD_GEMM_BN tiles (M > 128) or
-// 64 x 128 tiles (small M, weight-bound), split until about BD_GEMM_WGS run.
-static GemmPlan gemm_plan(int M, int N, int Kd) {
+// The fused 256 x 256 projection covers M > 256 when every 256-column tile
+// lies inside one layer's K or V block (n_kv * hd a multiple of 256); its d_in
+// is split until about one workgroup per CU runs.  Otherwise 256 x BD_GEMM_BN
+// tiles (M > 128) or 64 x 128 tiles (small M, weight-bound), split until about
+// BD_GEMM_WGS run, followed by the finish pass.
+static bool wide_fits(int M, int n_kv, int hd) {
+  return M > 256 && (hd == 64 || hd == 128) && (size_t(n_kv) * hd) % WBN == 0;
+}
+
+static GemmPlan gemm_plan(int M, int N, int Kd, bool wide) {
   GemmPlan p;
-  p.wide = M > 256 && N % WBN == 0;
+  p.wide = wide;
   if (p.wide) {
     p.bm = WBM; p.bn = WBN; p.bk = WBK;
     p.tiles = ((M + WBM - 1) / WBM) * (N / WBN);
@@ -484,9 +647,27 @@ static GemmPlan gemm_plan(int M, int N, int Kd) {
   return p;
 }
 
-size_t inject_ws_bytes(int M, int d_in, int N) {
+// workspace: projection without a split: row slots [M] (int64) and positions
+// [M] (int32); with a split (either kernel): the partials [S][M][N] fp32 of the
+// finish pass
+struct WideLayout {
+  size_t rslot, rpos, total;
+};
+static WideLayout wide_layout(int M) {
+  WideLayout w{};
+  size_t o = 0;
+  w.rslot = o; o += al(size_t(M) * 8);
+  w.rpos = o; o += al(size_t(M) * 4);
+  w.total = o;
+  return w;
+}
+
+size_t inject_ws_bytes(int M, int d_in, int L, int n_kv, int hd) {
   if (M <= 0) return 0;
-  GemmPlan p = gemm_plan(M, N, d_in);
+  const int N = L * 2 * n_kv * hd;
+  const bool wide = wide_fits(M, n_kv, hd);
+  GemmPlan p = gemm_plan(M, N, d_in, wide);
+  if (wide && p.S == 1) return wide_layout(M).total;
   return al(size_t(p.S) * M * N * 4);
 }
 
@@ -496,18 +677,40 @@ hipError_t launch_inject(const uint16_t* h, const uint16_t* w, const uint16_t* g
                          float eps, void* ws, hipStream_t stream) {
   if (M == 0 || B == 0) return hipSuccess;
   const int N = L * 2 * n_kv * hd;
-  GemmPlan p = gemm_plan(M, N, d_in);
-  GemmArgs g;
-  g.A = h; g.Bw = w; g.P = static_cast<float*>(ws);
-  g.M = M; g.N = N; g.Kd = d_in; g.S = p.S; g.steps_per_split = p.steps_per_split;
-  g.tiles_n = N / p.bn;
+  const bool wide = wide_fits(M, n_kv, hd);
+  GemmPlan p = gemm_plan(M, N, d_in, wide);
   dim3 grid(p.tiles, p.S);
-  if (p.wide) hipLaunchKernelGGL(ik_gemm_wide, grid, dim3(WNT), 0, stream, g);
-  else if (p.bm == 256) hipLaunchKernelGGL((ik_gemm<256, BD_GEMM_BN, BD_GEMM_BK>), grid, dim3(GT), 0, stream, g);
-  else hipLaunchKernelGGL((ik_gemm<64, 128, 64>), grid, dim3(GT), 0, stream, g);
+  if (wide) {
+    ProjArgs a{};
+    a.A = h; a.Bw = w; a.gain = gain; a.row_cu = row_cu; a.row_pos0 = row_pos0; a.cache_base = cache_base;
+    a.kc = kc; a.vc = vc; a.T_cap = T_cap;
+    a.M = M; a.N = N; a.Kd = d_in; a.S = p.S; a.steps_per_split = p.steps_per_split; a.tiles_n = N / WBN;
+    a.B = B; a.n_kv = n_kv; a.eps = eps;
+    for (int i = 0; i < hd / 2; ++i) a.inv_freq[i] = pow(double(theta), -2.0 * i / double(hd));
+    if (p.S == 1) {
+      // fused epilogue: the row map first
+      const WideLayout wl = wide_layout(M);
+      a.rslot = reinterpret_cast<const int64_t*>(static_cast<char*>(ws) + wl.rslot);
+      a.rpos = reinterpret_cast<const int32_t*>(static_cast<char*>(ws) + wl.rpos);
+      hipLaunchKernelGGL(ik_prep, dim3((M + 255) / 256), dim3(256), 0, stream, a);
+    } else {
+      a.part = static_cast<float*>(ws);
+    }
+    if (hd == 128) hipLaunchKernelGGL(ik_proj<128>, grid, dim3(WNT), 0, stream, a);
+    else hipLaunchKernelGGL(ik_proj<64>, grid, dim3(WNT), 0, stream, a);
+    if (p.S == 1) return hipGetLastError();
+  }
+  if (!wide) {
+    GemmArgs g;
+    g.A = h; g.Bw = w; g.P = static_cast<float*>(ws);
+    g.M = M; g.N = N; g.Kd = d_in; g.S = p.S; g.steps_per_split = p.steps_per_split;
+    g.tiles_n = N / p.bn;
+    if (p.bm == 256) hipLaunchKernelGGL((ik_gemm<256, BD_GEMM_BN, BD_GEMM_BK>), grid, dim3(GT), 0, stream, g);
+    else hipLaunchKernelGGL((ik_gemm<64, 128, 64>), grid, dim3(GT), 0, stream, g);
+  }
 
   FinishArgs f{};
-  f.P = g.P; f.gain = gain; f.row_cu = row_cu; f.row_pos0 = row_pos0; f.cache_base = cache_base;
+  f.P = static_cast<float*>(ws); f.gain = gain; f.row_cu = row_cu; f.row_pos0 = row_pos0; f.cache_base = cache_base;
   f.kc = kc; f.vc = vc; f.T_cap = T_cap;
   f.B = B; f.M = M; f.N = N; f.S = p.S; f.L = L; f.n_kv = n_kv; f.hd = hd; f.eps = eps;
   for (int i = 0; i < hd / 2; ++i) f.inv_freq[i] = pow(double(theta), -2.0 * i / double(hd));

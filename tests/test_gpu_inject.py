@@ -76,35 +76,54 @@ def test_m_above_128_uses_big_tiles():
 
 
 def test_wide_tiles_two_m_tiles_one_step_splits():
-    """M = 700 > 512: two 512-row tiles of the wide kernel, the second ragged;
-    d_in = 128 gives four 32-wide steps, split one per workgroup (ring tails)."""
+    """M = 700: three 256-row tiles of the wide kernel, the last ragged; d_in =
+    128 gives two 64-wide steps, split one per workgroup, then the finish pass."""
     run_case(1, 2, 128, 128, [400, 300], [5, 20000], 7)
 
 
 def test_wide_tiles_hd64_long_k():
-    """M = 513 (one row into the second tile), hd = 64, d_in = 2048 (64 steps)."""
+    """M = 513 (one row into the third tile), hd = 64, d_in = 2048 (32 steps in
+    16 splits)."""
     run_case(2, 4, 64, 2048, [500, 13], [0, 77], 8)
+
+
+def test_wide_unsplit_fused_epilogue_hd128():
+    """M = 516 > 256 with d_in = 64 (one step, so no split): the 256 x 256 tiles
+    run RMSNorm, RoPE and the scatter in the projection's own epilogue; ragged
+    requests, positions up to 32 700, a last tile four rows deep."""
+    run_case(2, 2, 128, 64, [300, 5, 211], [0, 32700, 1000], 9)
+
+
+def test_wide_unsplit_fused_epilogue_hd64():
+    """The unsplit fused epilogue at hd = 64 (two heads per wave), with and
+    without gains."""
+    run_case(1, 4, 64, 64, [257, 3], [11, 20000], 10)
+    run_case(2, 4, 64, 64, [40, 400], [3, 0], 11, gains=False)
 
 
 def test_no_gains_hd64():
     run_case(2, 3, 64, 640, [40, 9], [7, 1000], 4, gains=False)
 
 
-def test_rows_past_row_cu_end_are_not_written():
-    """row_cu[B] < M: trailing rows of H are ignored."""
+@pytest.mark.parametrize("n_kv,M,d_in,used", [(2, 20, 256, 12), (4, 300, 64, 261), (4, 600, 128, 333)])
+def test_rows_past_row_cu_end_are_not_written(n_kv, M, d_in, used):
+    """row_cu[B] < M: trailing rows of H are ignored (small tiles; the wide
+    tiles unsplit with the fused epilogue; the wide tiles split)."""
     import block_drafting_amd as bd
+    say(f"rows past row_cu: n_kv={n_kv} M={M} d_in={d_in} used={used}")
     rng = np.random.default_rng(5)
-    L, n_kv, hd, d_in, M = 1, 2, 64, 256, 20
+    L, hd = 1, 64
+    T = M + 20
     h, _ = wl.bf16_normal(rng, (M, d_in))
     w, _ = wl.bf16_normal(rng, (L * 2 * n_kv * hd, d_in), std=0.02)
-    kc = torch.full((L, 40, n_kv, hd), SENTINEL, dtype=torch.int16, device="cuda")
-    vc = torch.full((L, 40, n_kv, hd), SENTINEL, dtype=torch.int16, device="cuda")
-    bd.inject_kv(cuda_bits(h), cuda_bits(w), None, torch.tensor([0, 12], dtype=torch.int32, device="cuda"),
+    kc = torch.full((L, T, n_kv, hd), SENTINEL, dtype=torch.int16, device="cuda")
+    vc = torch.full((L, T, n_kv, hd), SENTINEL, dtype=torch.int16, device="cuda")
+    bd.inject_kv(cuda_bits(h), cuda_bits(w), None, torch.tensor([0, used], dtype=torch.int32, device="cuda"),
                  torch.tensor([0], dtype=torch.int32, device="cuda"),
                  torch.tensor([0], dtype=torch.int64, device="cuda"), kc, vc)
     torch.cuda.synchronize()
-    gk = host_bits(kc)
-    assert (gk[:, 12:] == SENTINEL).all() and (gk[:, :12] != SENTINEL).any()
+    for c in (host_bits(kc), host_bits(vc)):
+        assert (c[:, used:] == SENTINEL).all() and (c[:, :used] != SENTINEL).any()
 
 
 def test_deterministic_run_to_run():
@@ -150,7 +169,7 @@ def _full_size_sampled_rows(name, rows):
 
 def test_full_size_8b_round_sampled_rows():
     """M = 512 rows (B = 32, K = 16), d_in = 20480, 5 layers x 8 heads x 128:
-    the wide 512-row tiles split over d_in; the oracle checks 8 rows."""
+    the wide 256 x 256 tiles split over d_in; the oracle checks 8 rows."""
     _full_size_sampled_rows("qwen3-8b", [0, 15, 16, 100, 257, 300, 498, 511])
 
 
@@ -166,7 +185,7 @@ def test_full_size_27b_round_sampled_rows():
 
 
 def test_full_size_sweep_round_sampled_rows():
-    """Batch 128 (M = 2048: four 512-row tiles of the wide kernel)."""
+    """Batch 128 (M = 2048: eight 256-row tiles of the wide kernel)."""
     _full_size_sampled_rows("sweep-b128", [0, 511, 512, 1000, 1535, 1536, 2047])
 
 
