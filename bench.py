@@ -65,6 +65,10 @@ def parse():
                          "chained rounds, prefill, whole draft pass), e.g. under a profiler")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for HBM counter scaling)")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="time only --config's round, not every other workload's round as well")
+    ap.add_argument("--other-steps", type=int, default=30, help="timed rounds of each other workload")
+    ap.add_argument("--no-graph", action="store_true", help="skip the rounds replayed from a HIP graph")
     return ap.parse_args()
 
 
@@ -73,10 +77,11 @@ def source_sha(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_traffic(call: str):
-    """HBM bytes per launch of ``call`` measured with rocprofv3 counters, if the
-    committed measurement was taken on the current kernel source."""
-    p = os.path.join(ROOT, "profiles", "traffic_qwen3-8b.txt")
+def read_traffic(config: str, call: str):
+    """HBM bytes per launch of ``call`` at workload ``config``, measured with
+    rocprofv3 counters, if the committed measurement was taken on the current
+    kernel source."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{config}.txt")
     if not os.path.exists(p):
         return None
     rec = {}
@@ -88,6 +93,216 @@ def read_traffic(call: str):
     if not rec or rec.get("source_sha") != source_sha(KERNEL_SOURCES[call]):
         return None
     return float(rec["bytes_per_call"])
+
+
+def read_mfma_busy(config: str, call: str):
+    """MFMA busy fraction of ``call``'s matrix kernels at ``config`` (busy cycles
+    of the SIMDs' matrix pipes over 4 x the CU-busy cycles, rocprofv3 counters),
+    if measured on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"mfma_{config}.txt")
+    if not os.path.exists(p):
+        return None
+    for line in open(p):
+        if line.startswith(call + " "):
+            rec = dict(kv.partition("=")[::2] for kv in line.split()[1:])
+            if rec.get("source_sha") == source_sha(KERNEL_SOURCES[call]):
+                return float(rec["busy"])
+    return None
+
+
+class RoundSetup:
+    """One workload's inputs resident in HBM, its context caches filled
+    (untimed: inject_kv over synthetic context hidden states drawn on the
+    device), workspaces and outputs allocated once, and the round itself."""
+
+    def __init__(self, cfg, torch, bd, wl, dev):
+        self.cfg, self.torch, self.bd, self.dev = cfg, torch, bd, dev
+        B, K, G, L, n_q, n_kv, hd, V = cfg.B, cfg.K, cfg.G, cfg.L, cfg.n_q, cfg.n_kv, cfg.hd, cfg.V
+        self.sampling = cfg.temperature > 0
+        r = wl.make_round(cfg, seed=0)
+        self.r = r
+        i16 = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev)
+        self.h, self.w, self.gains = i16(r.h_round_bits), i16(r.w_bits), i16(r.k_norm_bits)
+        self.q, self.kb, self.vb = i16(r.q_bits), i16(r.k_blk_bits), i16(r.v_blk_bits)
+        self.zt = torch.from_numpy(r.z_target).to(dev)
+        self.zd = torch.from_numpy(r.z_draft).to(dev) if self.sampling else None
+        self.dtok = torch.from_numpy(r.draft_tokens).to(dev)
+        self.uni = torch.from_numpy(r.uniforms).to(dev)
+        self.row_cu = torch.from_numpy(r.row_cu).to(dev)
+        self.row_pos0 = torch.from_numpy(r.row_pos0).to(dev)
+        self.cache_base = torch.from_numpy(r.cache_base).to(dev)
+        self.ctx_len = torch.from_numpy(r.ctx_len).to(dev)
+        self.kc = torch.zeros((L, r.T_cap, n_kv, hd), dtype=torch.int16, device=dev)
+        self.vc = torch.zeros((L, r.T_cap, n_kv, hd), dtype=torch.int16, device=dev)
+        self.max_ctx = int(r.ctx_len.max())
+        self._fill()
+        self.ws_inj = torch.empty(max(1, bd.inject_kv_workspace_size(B * K, cfg.d_in, L, n_kv, hd)),
+                                  dtype=torch.uint8, device=dev)
+        self.ws_att = torch.empty(max(1, bd.draft_block_attn_workspace_size(B, K, n_q, n_kv, hd, self.max_ctx,
+                                                                            cfg.window)), dtype=torch.uint8, device=dev)
+        self.ws_ver = torch.empty(max(1, bd.verify_block_workspace_size(B, G, V, cfg.top_k)), dtype=torch.uint8,
+                                  device=dev)
+        self.attn_out = torch.empty((L, B, K, n_q, hd), dtype=torch.int16, device=dev)
+        self.tau = torch.empty(B, dtype=torch.int32, device=dev)
+        self.out_tok = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+
+    def _fill(self):
+        cfg, torch, bd, dev, r = self.cfg, self.torch, self.bd, self.dev, self.r
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1)
+        lo = np.maximum(0, r.ctx_len - cfg.window) if cfg.window > 0 else np.zeros(cfg.B, np.int64)
+        rows_b = (r.ctx_len - lo).astype(np.int64)
+        slice_rows = 8192
+        fill_ws = torch.empty(bd.inject_kv_workspace_size(slice_rows, cfg.d_in, cfg.L, cfg.n_kv, cfg.hd),
+                              dtype=torch.uint8, device=dev)
+        for b in range(cfg.B):
+            done = 0
+            while done < rows_b[b]:
+                n = int(min(slice_rows, rows_b[b] - done))
+                hc = torch.randn((n, cfg.d_in), generator=gen, device=dev).to(torch.bfloat16)
+                bd.inject_kv(hc, self.w, self.gains, torch.tensor([0, n], dtype=torch.int32, device=dev),
+                             torch.tensor([int(lo[b]) + done], dtype=torch.int32, device=dev),
+                             self.cache_base[b:b + 1].contiguous(), self.kc, self.vc, cfg.rope_theta, cfg.rms_eps,
+                             workspace=fill_ws)
+                done += n
+        torch.cuda.synchronize()
+
+    def round(self, ev=None):
+        """One round: inject_kv for the B*K rows, every layer's block attention,
+        verify_block; ev (optional) gets an event before each call and after the last."""
+        cfg, bd, stream = self.cfg, self.bd, self.torch.cuda.current_stream()
+        if ev is not None:
+            ev[0].record(stream)
+        bd.inject_kv(self.h, self.w, self.gains, self.row_cu, self.row_pos0, self.cache_base, self.kc, self.vc,
+                     cfg.rope_theta, cfg.rms_eps, workspace=self.ws_inj)
+        if ev is not None:
+            ev[1].record(stream)
+        for l in range(cfg.L):
+            bd.draft_block_attn(self.q[l], self.kb[l], self.vb[l], self.kc[l], self.vc[l], self.cache_base,
+                                self.ctx_len, self.max_ctx, cfg.window, out=self.attn_out[l], workspace=self.ws_att)
+        if ev is not None:
+            ev[2].record(stream)
+        bd.verify_block(self.zt, self.zd, self.dtok, self.uni, cfg.temperature, cfg.top_k, cfg.top_p, tau=self.tau,
+                        out_tokens=self.out_tok, workspace=self.ws_ver)
+        if ev is not None:
+            ev[3].record(stream)
+
+    def timed(self, steps, warmup):
+        """Whole rounds bracketed by device synchronisation, per-call HIP events
+        on the launch stream. Returns (rounds/s, ms per round, per-stage ms)."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.round()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            self.round(evs[s])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        stage_ms = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in evs]).mean(axis=0)
+        return steps / elapsed, 1e3 * elapsed / steps, stage_ms
+
+    def graph_rate(self, steps):
+        """The same round captured once in a HIP graph and replayed (the launch
+        latency of the round's kernels leaves the host); rounds/s."""
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.round()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.round()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        rate = steps / (time.perf_counter() - t0)
+        del g
+        return rate
+
+    def stages(self, stage_ms):
+        """Per-call achieved rates against the roofline of each call, from the
+        algorithmic work per call (kernels and rooflines)."""
+        cfg, r = self.cfg, self.r
+        B, K, G, L, n_q, n_kv, hd, V = cfg.B, cfg.K, cfg.G, cfg.L, cfg.n_q, cfg.n_kv, cfg.hd, cfg.V
+        M = B * K
+        inj_flops = 2.0 * M * cfg.d_in * cfg.n_out
+        inj_bytes = 2.0 * cfg.d_in * cfg.n_out + 2.0 * M * (cfg.d_in + cfg.n_out)
+        vis = np.minimum(r.ctx_len, cfg.window) if cfg.window > 0 else r.ctx_len
+        att_bytes = float(vis.sum()) * n_kv * hd * 2 * 2 + 2.0 * B * K * n_q * hd * 2 + 2.0 * B * K * n_kv * hd * 2
+        ver_bytes = 4.0 * V * (B * (G + 1) + (B * G if self.sampling else 0))
+        t_inj, t_att, t_ver = stage_ms[0] / 1e3, stage_ms[1] / L / 1e3, stage_ms[2] / 1e3
+        # the projection is bound by the matrix cores when its arithmetic
+        # intensity passes the ridge (2.5 PFLOP/s / 8 TB/s = 312 flop/B), by
+        # streaming its weights otherwise
+        inj_mfma = inj_flops / inj_bytes > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        st = []
+        if inj_mfma:
+            st.append(dict(call="inject_kv", bound="mfma", per_call_us=t_inj * 1e6, calls_per_round=1,
+                           achieved=inj_flops / t_inj / 1e12, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                           frac=inj_flops / t_inj / 1e12 / BF16_PEAK_TFLOPS, algorithmic_flops=inj_flops,
+                           algorithmic_bytes=inj_bytes))
+        else:
+            st.append(dict(call="inject_kv", bound="hbm", per_call_us=t_inj * 1e6, calls_per_round=1,
+                           achieved=inj_bytes / t_inj / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
+                           frac=inj_bytes / t_inj / 1e9 / HBM_PEAK_GBS, algorithmic_flops=inj_flops,
+                           algorithmic_bytes=inj_bytes))
+        st.append(dict(call="draft_block_attn", bound="hbm", per_call_us=t_att * 1e6, calls_per_round=L,
+                       achieved=att_bytes / t_att / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
+                       frac=att_bytes / t_att / 1e9 / HBM_PEAK_GBS, algorithmic_bytes=att_bytes))
+        st.append(dict(call="verify_block", bound="hbm", per_call_us=t_ver * 1e6, calls_per_round=1,
+                       achieved=ver_bytes / t_ver / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
+                       frac=ver_bytes / t_ver / 1e9 / HBM_PEAK_GBS, algorithmic_bytes=ver_bytes))
+        for s in st:
+            s["algorithmic_gbs"] = s["algorithmic_bytes"] / (s["per_call_us"] * 1e-6) / 1e9
+            s["traffic"] = read_traffic(cfg.name, s["call"])
+            # the HBM bytes the counters measured per call, over this run's call time
+            s["counter_gbs"] = None if s["traffic"] is None else s["traffic"] / (s["per_call_us"] * 1e-6) / 1e9
+            s["counter_mfma_busy"] = read_mfma_busy(cfg.name, s["call"])
+        return st
+
+    def free(self):
+        for k in list(vars(self)):
+            if k not in ("cfg", "torch", "bd", "dev", "r", "sampling"):
+                delattr(self, k)
+        self.torch.cuda.empty_cache()
+
+
+def _rounded(d):
+    return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
+
+
+def config_summary(rs, steps, warmup, graph):
+    """Rounds/s and per-stage rates of one workload (eager; and replayed from a
+    HIP graph when ``graph``)."""
+    cfg = rs.cfg
+    rate, ms, stage_ms = rs.timed(steps, warmup)
+    tau_h = rs.tau.cpu().numpy()
+    committed = int((tau_h + 1).sum())
+    out = {"workload": workload_name(cfg), "rounds_s": round(rate, 2), "ms_per_round": round(ms, 4),
+           "accepted_tok_s": round(rate * committed, 1), "drafted_accepted_tok_s": round(rate * int(tau_h.sum()), 1),
+           "tokens_per_round": committed, "mean_tau": round(float(tau_h.mean()), 3),
+           "stages": [_rounded(s) for s in rs.stages(stage_ms)]}
+    if graph:
+        g = rs.graph_rate(steps)
+        out["graph_rounds_s"] = round(g, 2)
+        out["graph_accepted_tok_s"] = round(g * committed, 1)
+    return out
+
+
+def workload_name(cfg):
+    return (f"{cfg.name}: B={cfg.B} K={cfg.K} contexts {cfg.ctx_kind}[{cfg.ctx_a},{cfg.ctx_b}]"
+            + (f" window {cfg.window}" if cfg.window else "")
+            + f" L={cfg.L} n_q={cfg.n_q} n_kv={cfg.n_kv} hd={cfg.hd} d_in={cfg.d_in} V={cfg.V} "
+              f"T={cfg.temperature} top_k={cfg.top_k} top_p={cfg.top_p}")
 
 
 def main():
@@ -104,136 +319,44 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfg = wl.CONFIGS[a.config]
-    B, K, G, L, n_q, n_kv, hd, V = cfg.B, cfg.K, cfg.G, cfg.L, cfg.n_q, cfg.n_kv, cfg.hd, cfg.V
-    sampling = cfg.temperature > 0
+    B, K, G, L = cfg.B, cfg.K, cfg.G, cfg.L
 
-    # ---------------------------------------------------------------- inputs
-    r = wl.make_round(cfg, seed=0)
-    i16 = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev)
-    h = i16(r.h_round_bits)
-    w = i16(r.w_bits)
-    gains = i16(r.k_norm_bits)
-    q = i16(r.q_bits)
-    kb = i16(r.k_blk_bits)
-    vb = i16(r.v_blk_bits)
-    zt = torch.from_numpy(r.z_target).to(dev)
-    zd = torch.from_numpy(r.z_draft).to(dev) if sampling else None
-    dtok = torch.from_numpy(r.draft_tokens).to(dev)
-    uni = torch.from_numpy(r.uniforms).to(dev)
-    row_cu = torch.from_numpy(r.row_cu).to(dev)
-    row_pos0 = torch.from_numpy(r.row_pos0).to(dev)
-    cache_base = torch.from_numpy(r.cache_base).to(dev)
-    ctx_len = torch.from_numpy(r.ctx_len).to(dev)
-    T_cap = r.T_cap
-    kc = torch.zeros((L, T_cap, n_kv, hd), dtype=torch.int16, device=dev)
-    vc = torch.zeros((L, T_cap, n_kv, hd), dtype=torch.int16, device=dev)
-    max_ctx = int(r.ctx_len.max())
-
-    # context fill (untimed): inject_kv over synthetic context hidden states,
-    # drawn on the device in slices
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(1)
-    lo = np.maximum(0, r.ctx_len - cfg.window) if cfg.window > 0 else np.zeros(B, np.int64)
-    rows_b = (r.ctx_len - lo).astype(np.int64)
-    slice_rows = 8192
-    fill_ws = torch.empty(bd.inject_kv_workspace_size(slice_rows, cfg.d_in, L, n_kv, hd), dtype=torch.uint8,
-                          device=dev)
-    for b in range(B):
-        done = 0
-        while done < rows_b[b]:
-            n = int(min(slice_rows, rows_b[b] - done))
-            hc = torch.randn((n, cfg.d_in), generator=gen, device=dev).to(torch.bfloat16)
-            bd.inject_kv(hc, w, gains, torch.tensor([0, n], dtype=torch.int32, device=dev),
-                         torch.tensor([int(lo[b]) + done], dtype=torch.int32, device=dev),
-                         cache_base[b:b + 1].contiguous(), kc, vc, cfg.rope_theta, cfg.rms_eps, workspace=fill_ws)
-            done += n
-    torch.cuda.synchronize()
-    del fill_ws
-
-    # workspaces and outputs, allocated once
-    ws_inj = torch.empty(max(1, bd.inject_kv_workspace_size(B * K, cfg.d_in, L, n_kv, hd)), dtype=torch.uint8,
-                         device=dev)
-    ws_att = torch.empty(max(1, bd.draft_block_attn_workspace_size(B, K, n_q, n_kv, hd, max_ctx, cfg.window)),
-                         dtype=torch.uint8, device=dev)
-    ws_ver = torch.empty(max(1, bd.verify_block_workspace_size(B, G, V, cfg.top_k)), dtype=torch.uint8,
-                         device=dev)
-    attn_out = torch.empty((L, B, K, n_q, hd), dtype=torch.int16, device=dev)
-    tau = torch.empty(B, dtype=torch.int32, device=dev)
-    out_tok = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def round_(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        bd.inject_kv(h, w, gains, row_cu, row_pos0, cache_base, kc, vc, cfg.rope_theta, cfg.rms_eps,
-                     workspace=ws_inj)
-        if ev is not None:
-            ev[1].record(stream)
-        for l in range(L):
-            bd.draft_block_attn(q[l], kb[l], vb[l], kc[l], vc[l], cache_base, ctx_len, max_ctx, cfg.window,
-                                out=attn_out[l], workspace=ws_att)
-        if ev is not None:
-            ev[2].record(stream)
-        bd.verify_block(zt, zd, dtok, uni, cfg.temperature, cfg.top_k, cfg.top_p, tau=tau, out_tokens=out_tok,
-                        workspace=ws_ver)
-        if ev is not None:
-            ev[3].record(stream)
-
-    for _ in range(a.warmup):
-        round_()
-    torch.cuda.synchronize()
-
-    # timed region: whole rounds, bracketed by device synchronisation
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(a.steps):
-        round_(evs[s])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    stage_ms = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in evs]).mean(axis=0)
-
-    tau_h = tau.cpu().numpy()
+    rs = RoundSetup(cfg, torch, bd, wl, dev)
+    rounds_s, ms_step, stage_ms = rs.timed(a.steps, a.warmup)
+    tau_h = rs.tau.cpu().numpy()
     committed = int((tau_h + 1).sum())
-    decisions = verify_diagnostics(cfg, bd, torch, dev, zt, zd, dtok, uni, ws_ver, tau_h)
-    rounds_s = a.steps / elapsed
-    ms_step = 1e3 * elapsed / a.steps
-
-    # ---------------------------------------------------------------- rooflines
-    M = B * K
-    N_out = cfg.n_out
-    inj_flops = 2.0 * M * cfg.d_in * N_out
-    inj_bytes = 2.0 * cfg.d_in * N_out + 2.0 * M * (cfg.d_in + N_out)
-    vis = np.minimum(r.ctx_len, cfg.window) if cfg.window > 0 else r.ctx_len
-    att_bytes = float(vis.sum()) * n_kv * hd * 2 * 2 + 2.0 * B * K * n_q * hd * 2 + 2.0 * B * K * n_kv * hd * 2
-    ver_rows = B * (G + 1) + (B * G if sampling else 0)
-    ver_bytes = 4.0 * V * ver_rows
-    stages = []
-    t_inj, t_att, t_ver = stage_ms[0] / 1e3, stage_ms[1] / L / 1e3, stage_ms[2] / 1e3
-    stages.append(dict(call="inject_kv", bound="mfma", per_call_us=t_inj * 1e6, calls_per_round=1,
-                       achieved=inj_flops / t_inj / 1e12, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                       frac=inj_flops / t_inj / 1e12 / BF16_PEAK_TFLOPS, algorithmic_flops=inj_flops,
-                       algorithmic_bytes=inj_bytes, hbm_gbs=inj_bytes / t_inj / 1e9))
-    stages.append(dict(call="draft_block_attn", bound="hbm", per_call_us=t_att * 1e6, calls_per_round=L,
-                       achieved=att_bytes / t_att / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
-                       frac=att_bytes / t_att / 1e9 / HBM_PEAK_GBS, algorithmic_bytes=att_bytes))
-    stages.append(dict(call="verify_block", bound="hbm", per_call_us=t_ver * 1e6, calls_per_round=1,
-                       achieved=ver_bytes / t_ver / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
-                       frac=ver_bytes / t_ver / 1e9 / HBM_PEAK_GBS, algorithmic_bytes=ver_bytes))
-    for s in stages:
-        s["traffic"] = read_traffic(s["call"])
+    decisions = verify_diagnostics(cfg, bd, torch, dev, rs.zt, rs.zd, rs.dtok, rs.uni, rs.ws_ver, tau_h)
+    stages = rs.stages(stage_ms)
     dom = max(stages, key=lambda s: s["per_call_us"] * s["calls_per_round"])
     roofline = dict(kernel=dom["call"], bound=dom["bound"], achieved=round(dom["achieved"], 2),
-                    peak=dom["peak"], unit=dom["unit"], frac=round(dom["frac"], 4),
-                    traffic=dom["traffic"])
+                    peak=dom["peak"], unit=dom["unit"], frac=round(dom["frac"], 4), traffic=dom["traffic"])
+    graph_rate = None if a.no_graph else rs.graph_rate(a.steps)
 
-    extras = None if a.no_extras else next_rows(a, cfg, r, bd, torch, dev, stream, q, kb, vb, kc, vc, cache_base,
-                                                ctx_len, max_ctx, zt, zd, dtok, uni, att_bytes)
+    extras = None
+    if not a.no_extras:
+        vis = np.minimum(rs.r.ctx_len, cfg.window) if cfg.window > 0 else rs.r.ctx_len
+        att_bytes = float(vis.sum()) * cfg.n_kv * cfg.hd * 2 * 2 + 2.0 * B * K * cfg.n_q * cfg.hd * 2 \
+            + 2.0 * B * K * cfg.n_kv * cfg.hd * 2
+        stream = torch.cuda.current_stream()
+        extras = next_rows(a, cfg, rs.r, bd, torch, dev, stream, rs.q, rs.kb, rs.vb, rs.kc, rs.vc, rs.cache_base,
+                           rs.ctx_len, rs.max_ctx, rs.zt, rs.zd, rs.dtok, rs.uni, att_bytes)
 
-    # ---------------------------------------------------------------- CPU baseline
     cpu = None
     if not a.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, r, kc, vc, h, w, tau_h)
+        cpu = cpu_baseline(cfg, rs.r, rs.kc, rs.vc, rs.h, rs.w, tau_h)
+    rs.free()
+
+    # every other workload's round on the same GPU (fewer steps; graph replay too)
+    others = None
+    if not a.no_other_configs:
+        others = {}
+        for name, ocfg in wl.CONFIGS.items():
+            if name == cfg.name:
+                continue
+            ors = RoundSetup(ocfg, torch, bd, wl, dev)
+            others[name] = config_summary(ors, a.other_steps, max(3, a.warmup // 2), graph=not a.no_graph)
+            ors.free()
+            del ors
 
     line = {
         "metric": "rounds/s + accepted tok/s at B=32, K=16 (8B shape); % of HBM/MFMA roofline",
@@ -248,18 +371,16 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16 (MFMA, fp32 accumulate) + fp32 (verify)",
         "data": "synthetic (seeded; random-init projection weights)",
-        "config": {"workload": f"{cfg.name}: B={B} K={K} contexts {cfg.ctx_kind}[{cfg.ctx_a},{cfg.ctx_b}] "
-                               f"L={L} n_q={n_q} n_kv={n_kv} hd={hd} d_in={cfg.d_in} V={V} "
-                               f"T={cfg.temperature} top_k={cfg.top_k}",
-                   "global_batch": B, "block": K, "parallelism": "none (1 GPU)"},
+        "config": {"workload": workload_name(cfg), "global_batch": B, "block": K, "parallelism": "none (1 GPU)"},
         "accepted_tok_s": round(rounds_s * committed, 1),
         "drafted_accepted_tok_s": round(rounds_s * int(tau_h.sum()), 1),
         "tokens_per_round": committed,
+        "graph_rounds_s": None if graph_rate is None else round(graph_rate, 2),
         "verify_decisions": decisions,
         "roofline": roofline,
-        "stages": [{k: (round(v, 4) if isinstance(v, float) and k != "traffic" else v) for k, v in s.items()}
-                   for s in stages],
+        "stages": [_rounded(s) for s in stages],
         "cpu_baseline": cpu,
+        "other_configs": others,
         "extras": extras,
     }
     if a.copy_calibration:

@@ -662,13 +662,31 @@ static WideLayout wide_layout(int M) {
   return w;
 }
 
-size_t inject_ws_bytes(int M, int d_in, int L, int n_kv, int hd) {
-  if (M <= 0) return 0;
-  const int N = L * 2 * n_kv * hd;
+// workspace a call with exactly M rows uses
+static size_t ws_bytes_exact(int M, int d_in, int N, int n_kv, int hd) {
   const bool wide = wide_fits(M, n_kv, hd);
   GemmPlan p = gemm_plan(M, N, d_in, wide);
   if (wide && p.S == 1) return wide_layout(M).total;
   return al(size_t(p.S) * M * N * 4);
+}
+
+// The size reported covers every call with up to M rows (the unsplit wide
+// projection needs less than a smaller, split one): the largest exact need
+// over M' <= M.  Within one tile count the need grows with M', so the row
+// counts that end a tile (and M itself) are the only candidates.
+size_t inject_ws_bytes(int M, int d_in, int L, int n_kv, int hd) {
+  if (M <= 0) return 0;
+  const int N = L * 2 * n_kv * hd;
+  size_t need = ws_bytes_exact(M, d_in, N, n_kv, hd);
+  for (int m = 1; m < M && m <= 256; ++m) {
+    const size_t x = ws_bytes_exact(m, d_in, N, n_kv, hd);
+    if (x > need) need = x;
+  }
+  for (long long m = 256; m < M; m += 256) {
+    const size_t x = ws_bytes_exact(int(m), d_in, N, n_kv, hd);
+    if (x > need) need = x;
+  }
+  return need;
 }
 
 hipError_t launch_inject(const uint16_t* h, const uint16_t* w, const uint16_t* gain, const int32_t* row_cu,

@@ -128,6 +128,11 @@ def test_workspace_sizes_are_monotone(lib):
     assert bd.verify_block_workspace_size(8, 15, 151936, 20) > bd.verify_block_workspace_size(8, 15, 151936, 0)
     assert bd.draft_block_attn_workspace_size(0, 16, 32, 8, 128, 4096, 0) == 0
     assert bd.inject_kv_workspace_size(512, 20480, 5, 8, 128) > 0
+    # a workspace sized for M rows serves every call with fewer rows
+    sizes = [bd.inject_kv_workspace_size(m, 20480, 5, 8, 128) for m in (1, 16, 128, 300, 512, 1024, 3000, 8192)]
+    assert sizes == sorted(sizes)
+    sizes = [bd.inject_kv_workspace_size(m, 768, 2, 2, 64) for m in (1, 8, 300, 512, 5000)]
+    assert sizes == sorted(sizes)
 
 
 def test_product_path_has_no_fallback(tmp_path):
