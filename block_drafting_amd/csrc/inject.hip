@@ -599,9 +599,6 @@ static inline size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 #define BD_GEMM_WGS 512
 #endif
 
-#ifndef BD_GEMM_WIDE_WGS
-#define BD_GEMM_WIDE_WGS 256
-#endif
 
 struct GemmPlan {
   int bm, bn, bk, S, steps_per_split, tiles;
@@ -610,11 +607,23 @@ struct GemmPlan {
 
 // The fused 256 x 256 projection covers M > 256 when every 256-column tile
 // lies inside one layer's K or V block (n_kv * hd a multiple of 256); its d_in
-// is split until about one workgroup per CU runs.  Otherwise 256 x BD_GEMM_BN
+// split comes from a cost model of waves and partial traffic.  Otherwise 256 x BD_GEMM_BN
 // tiles (M > 128) or 64 x 128 tiles (small M, weight-bound), split until about
 // BD_GEMM_WGS run, followed by the finish pass.
 static bool wide_fits(int M, int n_kv, int hd) {
   return M > 256 && (hd == 64 || hd == 128) && (size_t(n_kv) * hd) % WBN == 0;
+}
+
+// Compute units of the current device (queried once; 256 if the query fails).
+static int inject_cus() {
+  static const int n = [] {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+    return cus;
+  }();
+  return n;
 }
 
 static GemmPlan gemm_plan(int M, int N, int Kd, bool wide) {
@@ -624,10 +633,21 @@ static GemmPlan gemm_plan(int M, int N, int Kd, bool wide) {
     p.bm = WBM; p.bn = WBN; p.bk = WBK;
     p.tiles = ((M + WBM - 1) / WBM) * (N / WBN);
     const int steps = Kd / WBK;
-    int S = (BD_GEMM_WIDE_WGS + p.tiles / 2) / p.tiles;
-    if (S > steps) S = steps;
-    if (S < 1) S = 1;
-    p.steps_per_split = (steps + S - 1) / S;
+    // the split over d_in with the least modelled time: one workgroup per CU
+    // (the LDS rings allow no more), so the busiest CU runs ceil(tiles S /
+    // CUs) workgroups of ceil(steps / S) steps (about 1.7 us per step at full
+    // load); a split adds its fp32 partials, written once and read once by
+    // the finish pass at about 6 TB/s
+    const int cus = inject_cus();
+    int best_S = 1;
+    double best = 1e30;
+    for (int S = 1; S <= 8 && S <= steps; ++S) {
+      const double waves = double((long long)p.tiles * S + cus - 1) / cus;
+      const double t = double(int(waves)) * double((steps + S - 1) / S) * 1.7e-6 +
+                       (S > 1 ? 2.0 * S * double(M) * N * 4 / 6e12 : 0.0);
+      if (t < best * 0.999) { best = t; best_S = S; }
+    }
+    p.steps_per_split = (steps + best_S - 1) / best_S;
     p.S = (steps + p.steps_per_split - 1) / p.steps_per_split;
     return p;
   }
