@@ -56,8 +56,7 @@ def build(jobs: int = 4, verbose: bool = True, out: str = LIB, build_dir: str = 
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(lambda s: _compile(s, build_dir, defines), srcs))
     tmp = out + ".tmp"
-    # rocBLAS: the library GEMMs of the draft forward
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, "-lrocblas"]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

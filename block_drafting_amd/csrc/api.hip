@@ -270,10 +270,18 @@ int draft_forward(const uint16_t* x_in, int32_t B, int32_t K, int32_t d_model, i
   if (!x_in || !final_norm || !lm_head || !logits || !cache_base || !ctx_len || (L > 0 && (!layer_weights ||
       !k_cache || !v_cache)))
     return fail(BD_E_NULL, "draft_forward: a required pointer is NULL");
-  for (int i = 0; i < 8 * L; ++i)
+  for (int i = 0; i < 8 * L; ++i) {
     if (!layer_weights[i]) return fail(BD_E_NULL, "draft_forward: layer weight %d of layer %d is NULL", i % 8, i / 8);
-  if (!aligned16(k_cache) || !aligned16(v_cache))
-    return fail(BD_E_UNSUPPORTED, "draft_forward: the caches must be 16-byte aligned");
+    const int k = i % 8;  // the four matrices are streamed in 16-byte pieces
+    if ((k == 1 || k == 4 || k == 6 || k == 7) && !aligned16(layer_weights[i]))
+      return fail(BD_E_UNSUPPORTED, "draft_forward: layer weight %d of layer %d must be 16-byte aligned", k, i / 8);
+  }
+  if (d_model % 64 || ffn % 64)
+    return fail(BD_E_UNSUPPORTED, "draft_forward: d_model (%d) and ffn (%d) must be multiples of 64", d_model, ffn);
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(x_in) || !aligned16(lm_head))
+    return fail(BD_E_UNSUPPORTED, "draft_forward: x_in, lm_head and the caches must be 16-byte aligned");
+  if (V % 4 == 0 && !aligned16(logits))
+    return fail(BD_E_UNSUPPORTED, "draft_forward: logits must be 16-byte aligned");
   const size_t need = draft_forward_workspace_size(B, K, d_model, n_q, n_kv, hd, ffn, max_ctx, window);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(BD_E_WORKSPACE, "draft_forward: workspace of %zu bytes needed, %zu given", need,
@@ -283,7 +291,6 @@ int draft_forward(const uint16_t* x_in, int32_t B, int32_t K, int32_t d_model, i
   const hipError_t e = bd::launch_forward(x_in, B, K, d_model, L, n_q, n_kv, hd, ffn, V, layer_weights, final_norm,
                                           lm_head, k_cache, v_cache, cache_base, ctx_len, T_cap, max_ctx, window,
                                           rope_theta, rms_eps, logits, workspace, stream);
-  if (e == hipErrorUnknown) return fail(BD_E_LAUNCH, "draft_forward: a library GEMM failed");
   return launched(e, "draft_forward");
 }
 

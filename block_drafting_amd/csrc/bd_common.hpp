@@ -74,6 +74,18 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// wait until at most min(n, N) vector memory operations are outstanding (n
+// known only at run time, N its compile-time bound)
+template <int N>
+__device__ __forceinline__ void vm_wait_le(int n) {
+  if constexpr (N == 0) {
+    vm_wait<0>();
+  } else {
+    if (n >= N) vm_wait<N>();
+    else vm_wait_le<N - 1>(n);
+  }
+}
+
 // sin and cos of a rotary angle given in fp64 (any size, e.g. position x
 // frequency): Cody-Waite reduction by pi/2 in fp64 with a two-term pi/2, so the
 // reduced |y| <= pi/4 keeps the angle's accuracy at positions in the tens of

@@ -15,121 +15,12 @@
 // the half-split pairs (i, i + hd/2) by pos * theta^(-2i/hd), rounds K and V
 // to bf16 and writes them to the request's cache slot.
 #include "bd_common.hpp"
+#include "bd_gemm.hpp"
 #include "bd_launch.hpp"
 
 #include <math.h>
 
 namespace bd {
-
-constexpr int GT = 256;  // threads per GEMM workgroup (2 x 2 waves)
-constexpr int KALIGN = 64;  // d_in must be a multiple of this
-
-struct GemmArgs {
-  const uint16_t* A;  // [M, Kd]
-  const uint16_t* Bw; // [N, Kd]
-  float* P;           // [S][M][N]
-  int M, N, Kd, S, steps_per_split, tiles_n;
-};
-
-template <int BM, int BN, int BK>
-__global__ __launch_bounds__(GT) void ik_gemm(GemmArgs g) {
-  constexpr int GLS = BK + 8;               // LDS row stride (elements)
-  constexpr int WM = BM / 2, WN = BN / 2;   // wave tile
-  constexpr int FM = WM / 32, FN = WN / 32; // 32x32 blocks per wave
-  constexpr int APT = BM * BK / 8 / GT;     // 16-byte pieces per thread
-  constexpr int BPT = BN * BK / 8 / GT;
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * GLS];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * GLS];
-
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  const int tile = blockIdx.x, split = blockIdx.y;
-  const int tm = tile / g.tiles_n, tn = tile - tm * g.tiles_n;
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int step0 = split * g.steps_per_split;
-  const int nsteps_all = g.Kd / BK;
-  const int nsteps = min(g.steps_per_split, nsteps_all - step0);
-
-  floatx16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  u32x4 ra[APT], rb[BPT];
-  auto fetch = [&](int step) {
-    const int k0 = (step0 + step) * BK;
-#pragma unroll
-    for (int p = 0; p < APT; ++p) {
-      const int piece = t + p * GT;
-      const int row = piece / (BK / 8), kc = piece - row * (BK / 8);
-      const int m = m0 + row;
-      ra[p] = *reinterpret_cast<const u32x4*>(g.A + size_t(m < g.M ? m : g.M - 1) * g.Kd + k0 + kc * 8);
-    }
-#pragma unroll
-    for (int p = 0; p < BPT; ++p) {
-      const int piece = t + p * GT;
-      const int row = piece / (BK / 8), kc = piece - row * (BK / 8);
-      rb[p] = *reinterpret_cast<const u32x4*>(g.Bw + size_t(n0 + row) * g.Kd + k0 + kc * 8);
-    }
-  };
-
-  if (nsteps > 0) fetch(0);
-  for (int step = 0; step < nsteps; ++step) {
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < APT; ++p) {
-      // rows past M were loaded from row M - 1 (unconditional loads); they
-      // are zeroed here, where the data is consumed
-      const int piece = t + p * GT;
-      const int row = piece / (BK / 8), kc = piece - row * (BK / 8);
-      const u32x4 z4 = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&As[row * GLS + kc * 8]) = m0 + row < g.M ? ra[p] : z4;
-    }
-#pragma unroll
-    for (int p = 0; p < BPT; ++p) {
-      const int piece = t + p * GT;
-      const int row = piece / (BK / 8), kc = piece - row * (BK / 8);
-      *reinterpret_cast<u32x4*>(&Bs[row * GLS + kc * 8]) = rb[p];
-    }
-    __syncthreads();
-    if (step + 1 < nsteps) fetch(step + 1);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(
-            &As[(wm * WM + i * 32 + (lane & 31)) * GLS + kk * 16 + (lane >> 5) * 8]));
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = as_bf16x8(*reinterpret_cast<const uint4*>(
-            &Bs[(wn * WN + j * 32 + (lane & 31)) * GLS + kk * 16 + (lane >> 5) * 8]));
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(af[i], bfr[j], acc[i][j]);
-    }
-  }
-
-  // C block layout: lane holds column (lane & 31), rows 8*jj + 4*(lane >> 5) + r
-  float* P = g.P + size_t(split) * g.M * g.N;
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n0 + wn * WN + j * 32 + (lane & 31);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + wm * WM + i * 32 + jj * 8 + (lane >> 5) * 4 + r;
-          if (m < g.M) P[size_t(m) * g.N + n] = acc[i][j][jj * 4 + r];
-        }
-    }
-}
 
 // ---------------------------------------------------------------- wide-M projection
 // For M > 256: one workgroup computes a 256 x 256 output tile (two heads of one
@@ -146,14 +37,11 @@ __global__ __launch_bounds__(GT) void ik_gemm(GemmArgs g) {
 // 16 bytes; the pieces of each 256-byte line are XOR-permuted so the operand
 // reads (16 lanes: 16 rows, one piece each) are conflict-free.
 //
-// The split over d_in is reduced inside the kernel: the splits of a tile count
-// their arrival on a per-tile counter; every split but the last stores its fp32
-// partial (agent-coherent stores, so the store is visible at the device's
-// coherence point once it completes) and then counts itself ready; the last
-// one waits for those S - 1, adds the partials in split order (so the sum is
-// the same whichever split arrives last) and runs the epilogue: per-head
-// RMSNorm and gain, rotary embedding at the row's position, bf16, and the
-// scatter into the cache slots.  With no split the epilogue runs directly.
+// With a split over d_in, each split stores its fp32 partial tile to the
+// workspace and ik_finish adds the partials in split order and runs the
+// epilogue.  With no split the epilogue runs in this kernel: per-head RMSNorm
+// and gain, rotary embedding at the row's position, bf16, and the scatter into
+// the cache slots (the row map comes from ik_prep).
 constexpr int WBM = 256, WBN = 256;
 constexpr int WNW = 8, WNT = 64 * WNW;
 constexpr int WMW = 4, WNWN = 2;          // waves along M and along N
@@ -191,16 +79,6 @@ __device__ __forceinline__ int wpiece(int row, int c) {
   constexpr int P = WBK / 8, RPL = 16 / P;  // pieces per row, rows per line
   const int line = row / RPL;
   return (line * 16 + (((row % RPL) * P + c) ^ (line & (P - 1)))) * 16;
-}
-
-template <int N>
-__device__ __forceinline__ void vm_wait_le(int n) {
-  if constexpr (N == 0) {
-    vm_wait<0>();
-  } else {
-    if (n >= N) vm_wait<N>();
-    else vm_wait_le<N - 1>(n);
-  }
 }
 
 // ops a wave issues after its H loads of step k (loads complete in order, so

@@ -278,9 +278,10 @@ int verify_block_ragged(const float* target_logits, const float* draft_logits,
  *   position i; a = draft_block_attn(q, k, v, layer l's caches) (no flags);
  *   x += a W_o^T; xn = RMSNorm(x, g_mlp); x += (SiLU(gate) * up) W_down^T.
  * logits = RMSNorm(x, final_norm) lm_head^T, fp32.  Intermediates and the
- * residual stream are bf16 (fp32 arithmetic inside each step).  The GEMMs run
- * in rocBLAS on the given stream (calls from several host threads are
- * serialised); the rest in this library's kernels.
+ * residual stream are bf16 (fp32 arithmetic inside each step).  Every step
+ * runs in this library's kernels; the projections in a weight-streaming GEMM
+ * whose d_in splits are added, in a fixed order, by the kernel that consumes
+ * them, so the result is deterministic.
  *
  * x_in        device bf16 [B K, d]: the block rows' input hidden states.
  * layer_weights host array of 8 L device pointers (may be NULL when L = 0).
@@ -288,7 +289,9 @@ int verify_block_ragged(const float* target_logits, const float* draft_logits,
  * k_cache, v_cache device bf16 [L, T_cap, n_kv, hd] (filled by inject_kv);
  * cache_base, ctx_len, max_ctx, window: as draft_block_attn.
  * logits      device fp32 [B K, V].
- * Supported: hd in {64, 128}; K <= 64; (n_q / n_kv) K <= 128.
+ * Supported: hd in {64, 128}; K <= 64; (n_q / n_kv) K <= 128; d and ffn
+ * multiples of 64; x_in, lm_head, the four weight matrices of each layer and
+ * the caches 16-byte aligned (logits too when V % 4 == 0).
  * ------------------------------------------------------------------------ */
 size_t draft_forward_workspace_size(int32_t B, int32_t K, int32_t d_model, int32_t n_q, int32_t n_kv, int32_t hd,
                                     int32_t ffn, int32_t max_ctx, int32_t window);
