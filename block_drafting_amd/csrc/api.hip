@@ -272,14 +272,13 @@ int draft_forward(const uint16_t* x_in, int32_t B, int32_t K, int32_t d_model, i
     return fail(BD_E_NULL, "draft_forward: a required pointer is NULL");
   for (int i = 0; i < 8 * L; ++i) {
     if (!layer_weights[i]) return fail(BD_E_NULL, "draft_forward: layer weight %d of layer %d is NULL", i % 8, i / 8);
-    const int k = i % 8;  // the four matrices are streamed in 16-byte pieces
-    if ((k == 1 || k == 4 || k == 6 || k == 7) && !aligned16(layer_weights[i]))
-      return fail(BD_E_UNSUPPORTED, "draft_forward: layer weight %d of layer %d must be 16-byte aligned", k, i / 8);
+    if (!aligned16(layer_weights[i]))
+      return fail(BD_E_UNSUPPORTED, "draft_forward: layer weight %d of layer %d must be 16-byte aligned", i % 8, i / 8);
   }
   if (d_model % 64 || ffn % 64)
     return fail(BD_E_UNSUPPORTED, "draft_forward: d_model (%d) and ffn (%d) must be multiples of 64", d_model, ffn);
-  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(x_in) || !aligned16(lm_head))
-    return fail(BD_E_UNSUPPORTED, "draft_forward: x_in, lm_head and the caches must be 16-byte aligned");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(x_in) || !aligned16(lm_head) || !aligned16(final_norm))
+    return fail(BD_E_UNSUPPORTED, "draft_forward: x_in, final_norm, lm_head and the caches must be 16-byte aligned");
   if (V % 4 == 0 && !aligned16(logits))
     return fail(BD_E_UNSUPPORTED, "draft_forward: logits must be 16-byte aligned");
   const size_t need = draft_forward_workspace_size(B, K, d_model, n_q, n_kv, hd, ffn, max_ctx, window);

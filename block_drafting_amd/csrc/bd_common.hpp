@@ -1,6 +1,8 @@
 // Shared device helpers of the block-draft library (gfx950, wave64).
 #pragma once
 
+#include <stddef.h>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -72,6 +74,17 @@ template <int N>
 __device__ __forceinline__ void vm_wait() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Element i of an array member (at byte offset member_offset) of the argument
+// struct of a kernel whose only argument is that struct, read straight from
+// the kernel-argument segment, where the struct sits at offset 0.  For a
+// per-lane index: indexing the by-value argument itself would make the
+// compiler copy the whole struct to private memory.
+template <typename T>
+__device__ __forceinline__ T kernarg_elem(size_t member_offset, int i) {
+  const char* base = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
+  return reinterpret_cast<const T*>(base + member_offset)[i];
 }
 
 // wait until at most min(n, N) vector memory operations are outstanding (n

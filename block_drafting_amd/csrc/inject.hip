@@ -344,11 +344,7 @@ __global__ __launch_bounds__(WNT) void ik_proj(ProjArgs g) {
   float* lds_g = reinterpret_cast<float*>(ringW);
   double* lds_f = reinterpret_cast<double*>(ringW + HD * 4);
   for (int d = t; d < HD; d += WNT) lds_g[d] = g.gain ? bf16_to_f32(g.gain[l * HD + d]) : 1.f;
-  // static indices into the argument array (an indexed argument array would be
-  // copied to private memory)
-#pragma unroll
-  for (int d = 0; d < HD / 2; ++d)
-    if (t == d) lds_f[d] = g.inv_freq[d];
+  if (t < HD / 2) lds_f[t] = kernarg_elem<double>(offsetof(ProjArgs, inv_freq), t);
   __syncthreads();
   proj_epilogue<HD>(g, acc, n0, wn, lane, rslot, rpos, lds_g, lds_f);
 }
@@ -440,7 +436,7 @@ __global__ __launch_bounds__(256) void ik_finish(FinishArgs f) {
       const float a = xa[c] * inv * ga, bb = xb[c] * inv * gb;
       // angle pos * theta^(-2i/hd) in fp64, reduced in fp64
       float sn, cs;
-      sincos_angle(double(pos) * f.inv_freq[i], &sn, &cs);
+      sincos_angle(double(pos) * kernarg_elem<double>(offsetof(FinishArgs, inv_freq), i), &sn, &cs);
       oa[c] = f32_to_bf16(a * cs - bb * sn);
       ob[c] = f32_to_bf16(bb * cs + a * sn);
     }

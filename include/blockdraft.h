@@ -290,8 +290,8 @@ int verify_block_ragged(const float* target_logits, const float* draft_logits,
  * cache_base, ctx_len, max_ctx, window: as draft_block_attn.
  * logits      device fp32 [B K, V].
  * Supported: hd in {64, 128}; K <= 64; (n_q / n_kv) K <= 128; d and ffn
- * multiples of 64; x_in, lm_head, the four weight matrices of each layer and
- * the caches 16-byte aligned (logits too when V % 4 == 0).
+ * multiples of 64; x_in, final_norm, lm_head, every layer weight and the
+ * caches 16-byte aligned (logits too when V % 4 == 0).
  * ------------------------------------------------------------------------ */
 size_t draft_forward_workspace_size(int32_t B, int32_t K, int32_t d_model, int32_t n_q, int32_t n_kv, int32_t hd,
                                     int32_t ffn, int32_t max_ctx, int32_t window);
