@@ -474,6 +474,7 @@ def next_rows(a, cfg, r, bd, torch, dev, stream, q, kb, vb, kc, vc, cache_base, 
     ex["overlap"] = overlap_rounds(cfg, r, bd, torch, dev, q, kb, vb, zt, zd, dtok, uni)
     ex["inject_prefill"] = inject_prefill(cfg, r, bd, torch, dev, stream)
     ex["draft_pass"] = draft_pass(cfg, r, bd, torch, dev, stream, kc, vc, cache_base, ctx_len, max_ctx)
+    ex["library_gemm"] = library_gemm(cfg, r, bd, torch, dev, stream, kc, vc, cache_base, ctx_len)
     surv = [np.full(G, c, np.float32) for c in rng.uniform(0.6, 0.95, B)]
     t0 = time.perf_counter()
     ell, theta = bd.prefix_schedule(surv, table_b, table_v)
@@ -482,6 +483,53 @@ def next_rows(a, cfg, r, bd, torch, dev, stream, q, kb, vb, kc, vc, cache_base, 
                                  survival="per request constant c_r ~ U(0.6, 0.95) (seed 5), G positions",
                                  chosen_tokens=int(sum(ell) + B), theta=round(theta, 1), host_us=round(host_us, 1))
     return ex
+
+
+def library_gemm(cfg, r, bd, torch, dev, stream, kc, vc, cache_base, ctx_len, d_model=4096):
+    """Context for the hand-written GEMMs: torch's bf16 linear (a library GEMM,
+    hipBLASLt on ROCm) at the same shapes, the plain product without any
+    epilogue. The round's projection Y = H W^T (M = B K, d_in, N = 2 L n_kv hd)
+    against inject_kv, which also normalises, rotates and scatters into the
+    caches; the drafter's LM head at M = 4 B (logits = X lm_head^T: this library
+    writes fp32; the library GEMM writes bf16, then a cast to fp32 is timed with
+    it)."""
+    B, K, L, nkv, hd, V = cfg.B, cfg.K, cfg.L, cfg.n_kv, cfg.hd, cfg.V
+    g = torch.Generator(device=dev)
+    g.manual_seed(41)
+    i16 = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev)
+    w_bits, gains = i16(r.w_bits), i16(r.k_norm_bits)
+    w = w_bits.view(torch.bfloat16)
+    h = torch.randn((B * K, cfg.d_in), generator=g, device=dev).to(torch.bfloat16)
+    cu = torch.arange(0, (B + 1) * K, K, dtype=torch.int32, device=dev)
+    wsi = torch.empty(max(1, bd.inject_kv_workspace_size(B * K, cfg.d_in, L, nkv, hd)), dtype=torch.uint8,
+                      device=dev)
+    t_lib = _time_us(torch, stream, lambda: torch.nn.functional.linear(h, w))
+    t_ours = _time_us(torch, stream, lambda: bd.inject_kv(h.view(torch.int16), w_bits, gains, cu, ctx_len, cache_base,
+                                                          kc, vc, cfg.rope_theta, cfg.rms_eps, workspace=wsi))
+    flops = 2.0 * B * K * cfg.d_in * w.shape[0]
+    out = dict(projection=dict(shape=f"M={B * K} d_in={cfg.d_in} N={w.shape[0]} bf16",
+                               library_linear_us=round(t_lib, 1), inject_kv_us=round(t_ours, 1),
+                               library_tflops=round(flops / t_lib / 1e6, 1), inject_kv_tflops=round(flops / t_ours / 1e6, 1)))
+    M = 4 * B
+    x = torch.randn((M, d_model), generator=g, device=dev).to(torch.bfloat16)
+    lm = (torch.randn((V, d_model), generator=g, device=dev) * d_model ** -0.5).to(torch.bfloat16)
+    one = torch.ones(d_model, device=dev).to(torch.bfloat16)
+    t_lib = _time_us(torch, stream, lambda: torch.nn.functional.linear(x, lm).float(), n=10)
+    logits = torch.empty((M, V), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, bd.draft_forward_workspace_size(B, 4, d_model, cfg.n_q, nkv, hd, 4 * d_model, 1, 0)),
+                     dtype=torch.uint8, device=dev)
+    xb = x.view(torch.int16)
+    # zero drafter layers: the call is the final RMSNorm and the LM head
+    t_ours = _time_us(torch, stream, lambda: bd.draft_forward(xb, [], one.view(torch.int16), lm.view(torch.int16), kc,
+                                                              vc, cache_base, ctx_len, 1, 4, cfg.n_q, nkv,
+                                                              4 * d_model, logits=logits, workspace=ws), n=10)
+    wb = 2.0 * V * d_model
+    out["lm_head"] = dict(shape=f"M={M} d={d_model} V={V} bf16, fp32 logits",
+                          library_linear_us=round(t_lib, 1), draft_forward_rmsnorm_lm_head_us=round(t_ours, 1),
+                          library_weight_tbs=round(wb / t_lib / 1e6, 2), ours_weight_tbs=round(wb / t_ours / 1e6, 2))
+    del lm, x
+    torch.cuda.empty_cache()
+    return out
 
 
 def select_block(cfg, bd, torch, dev, stream, zd, rank=256):
