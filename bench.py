@@ -475,6 +475,7 @@ def next_rows(a, cfg, r, bd, torch, dev, stream, q, kb, vb, kc, vc, cache_base, 
     ex["inject_prefill"] = inject_prefill(cfg, r, bd, torch, dev, stream)
     ex["draft_pass"] = draft_pass(cfg, r, bd, torch, dev, stream, kc, vc, cache_base, ctx_len, max_ctx)
     ex["library_gemm"] = library_gemm(cfg, r, bd, torch, dev, stream, kc, vc, cache_base, ctx_len)
+    ex["stream_reference"] = stream_reference(torch, dev, stream)
     surv = [np.full(G, c, np.float32) for c in rng.uniform(0.6, 0.95, B)]
     t0 = time.perf_counter()
     ell, theta = bd.prefix_schedule(surv, table_b, table_v)
@@ -528,6 +529,21 @@ def library_gemm(cfg, r, bd, torch, dev, stream, kc, vc, cache_base, ctx_len, d_
                           library_linear_us=round(t_lib, 1), draft_forward_rmsnorm_lm_head_us=round(t_ours, 1),
                           library_weight_tbs=round(wb / t_lib / 1e6, 2), ours_weight_tbs=round(wb / t_ours / 1e6, 2))
     del lm, x
+    torch.cuda.empty_cache()
+    return out
+
+
+def stream_reference(torch, dev, stream, nbytes=1 << 30):
+    """Plain streaming rates of this GPU for context (library kernels, not this
+    library's): a sum over a 1 GiB fp32 buffer (read only) and a 1 GiB device
+    copy (read + write), each as bytes moved over HIP-event time."""
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    t_sum = _time_us(torch, stream, lambda: x.sum(), n=10)
+    t_copy = _time_us(torch, stream, lambda: y.copy_(x), n=10)
+    out = dict(read_sum_tbs=round(nbytes / t_sum / 1e6, 2), copy_tbs=round(2 * nbytes / t_copy / 1e6, 2),
+               buffer_bytes=nbytes)
+    del x, y
     torch.cuda.empty_cache()
     return out
 
