@@ -95,19 +95,20 @@ def read_traffic(config: str, call: str):
     return float(rec["bytes_per_call"])
 
 
-def read_mfma_busy(config: str, call: str):
-    """MFMA busy fraction of ``call``'s matrix kernels at ``config`` (busy cycles
-    of the SIMDs' matrix pipes over 4 x the CU-busy cycles, rocprofv3 counters),
-    if measured on the current kernel source."""
+def read_mfma(config: str, call: str):
+    """(MFMA utilisation, bf16 matrix flops executed per call) of ``call``'s
+    matrix kernels at ``config`` from rocprofv3 counters (the tool's MfmaUtil
+    and MfmaFlopsBF16), if measured on the current kernel source; else
+    (None, None)."""
     p = os.path.join(ROOT, "profiles", f"mfma_{config}.txt")
     if not os.path.exists(p):
-        return None
+        return None, None
     for line in open(p):
         if line.startswith(call + " "):
             rec = dict(kv.partition("=")[::2] for kv in line.split()[1:])
-            if rec.get("source_sha") == source_sha(KERNEL_SOURCES[call]):
-                return float(rec["busy"])
-    return None
+            if rec.get("source_sha") == source_sha(KERNEL_SOURCES[call]) and "util" in rec and "exec_flops" in rec:
+                return float(rec["util"]), float(rec["exec_flops"])
+    return None, None
 
 
 class RoundSetup:
@@ -266,7 +267,10 @@ class RoundSetup:
             s["traffic"] = read_traffic(cfg.name, s["call"])
             # the HBM bytes the counters measured per call, over this run's call time
             s["counter_gbs"] = None if s["traffic"] is None else s["traffic"] / (s["per_call_us"] * 1e-6) / 1e9
-            s["counter_mfma_busy"] = read_mfma_busy(cfg.name, s["call"])
+            util, xf = read_mfma(cfg.name, s["call"])
+            # the tool's MFMA utilisation, and the matrix flops it counted over this run's call time
+            s["counter_mfma_util"] = util
+            s["counter_mfma_tflops"] = None if xf is None else xf / (s["per_call_us"] * 1e-6) / 1e12
         return st
 
     def free(self):
