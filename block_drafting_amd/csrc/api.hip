@@ -68,7 +68,8 @@ int inject_kv(const uint16_t* h_target, const uint16_t* w_kv, const uint16_t* k_
     return fail(BD_E_NULL, "inject_kv: a required pointer is NULL");
   if (!aligned16(h_target) || !aligned16(w_kv) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(BD_E_UNSUPPORTED, "inject_kv: H, W and the caches must be 16-byte aligned");
-  const size_t need = inject_kv_workspace_size(M, d_in, L, n_kv, hd);
+  // the bytes this call uses (at most what inject_kv_workspace_size reports)
+  const size_t need = bd::inject_ws_bytes_call(M, d_in, L, n_kv, hd);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(BD_E_WORKSPACE, "inject_kv: workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);

@@ -7,7 +7,10 @@
 
 namespace bd {
 
+// the workspace every call with up to M rows fits in (the size reported to
+// callers), and the part of it a call with exactly M rows uses
 size_t inject_ws_bytes(int M, int d_in, int L, int n_kv, int hd);
+size_t inject_ws_bytes_call(int M, int d_in, int L, int n_kv, int hd);
 hipError_t launch_inject(const uint16_t* h, const uint16_t* w, const uint16_t* gain, const int32_t* row_cu,
                          const int32_t* row_pos0, const int64_t* cache_base, uint16_t* kc, uint16_t* vc,
                          int64_t T_cap, int B, int M, int d_in, int L, int n_kv, int hd, float theta,
@@ -29,6 +32,17 @@ hipError_t launch_verify(const float* zt, const float* zd, const int* dtok, cons
 
 hipError_t launch_commit(const int32_t* tau, int B, int K, int32_t* ctx_len, int32_t* row_pos0, const int32_t* cap,
                          int32_t* done, hipStream_t stream);
+
+// Weight-streaming GEMM (forward.hip): P[s][m][n] = the d_in split s of X . W^T
+// (X [M][Kd], W [N][Kd] bf16, Kd a multiple of 64; P fp32, S splits of
+// steps_per_split 64-wide steps; with S = 1 the product itself).  fg_plan
+// picks the tile shape, split and grid for a shape (split = false: S = 1).
+struct FgPlan {
+  int FN, WMW, S, steps_per_split, MT, G, nwg;
+};
+FgPlan fg_plan(int M, int N, int Kd, bool split = true);
+hipError_t fg_run(const FgPlan& p, const uint16_t* X, const uint16_t* W, float* P, int M, int N, int Kd,
+                  hipStream_t stream);
 
 size_t forward_ws_bytes(int B, int K, int d, int n_q, int n_kv, int hd, int ffn, int max_ctx, int window);
 hipError_t launch_forward(const uint16_t* x_in, int B, int K, int d, int L, int n_q, int n_kv, int hd, int ffn,

@@ -23,6 +23,9 @@
 
 #include <algorithm>
 #include <cmath>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 namespace bd {
 
@@ -262,10 +265,6 @@ __global__ __launch_bounds__(FG_T) void fg_gemm(FgArgs g) {
 
 namespace {
 
-struct FgPlan {
-  int FN, WMW, S, steps_per_split, MT, G, nwg;
-};
-
 int fg_cus() {
   static int cus = [] {
     int dev = 0, n = 0;
@@ -276,6 +275,8 @@ int fg_cus() {
   }();
   return cus;
 }
+
+}  // namespace
 
 // M tile (32 WMW rows), chunk width (at most FN blocks of 32 columns), d_in
 // split S and ranges per plane G of one projection.  Candidates: one chunk per
@@ -288,7 +289,7 @@ int fg_cus() {
 // partials' write and read-back.  Its constants were fitted to timings of
 // every candidate at the drafter's shapes (hidden 4096, MLP 12288, vocabulary
 // 151936, M = 16 .. 512), where its pick is within a few per cent of the best.
-FgPlan fg_plan(int M, int N, int Kd, bool split = true) {
+static FgPlan fg_plan_search(int M, int N, int Kd, bool split) {
   const int cus = fg_cus();
   const double hbm = 5.5e12, cu_load = 40e9, latency = 3e-6, ramp = 1e-6;
   const int WMW = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
@@ -333,11 +334,32 @@ FgPlan fg_plan(int M, int N, int Kd, bool split = true) {
   return best;
 }
 
+// The search above takes tens of microseconds; calls repeat a few shapes, so
+// the plans are kept per (M, N, Kd, split).
+FgPlan fg_plan(int M, int N, int Kd, bool split) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int, bool>, FgPlan> memo;
+  const auto key = std::make_tuple(M, N, Kd, split);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = memo.find(key);
+    if (it != memo.end()) return it->second;
+  }
+  const FgPlan p = fg_plan_search(M, N, Kd, split);
+  std::lock_guard<std::mutex> lock(mu);
+  memo.emplace(key, p);
+  return p;
+}
+
+namespace {
+
 template <int FN, int WMW>
 hipError_t fg_launch_shape(const FgArgs& a, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((fg_gemm<FN, WMW>), dim3(grid), dim3(FG_T), 0, stream, a);
   return hipGetLastError();
 }
+
+}  // namespace
 
 // P = the split partials of X . W^T (with S = 1, the product itself)
 hipError_t fg_run(const FgPlan& p, const uint16_t* X, const uint16_t* W, float* P, int M, int N, int Kd,
@@ -354,7 +376,6 @@ hipError_t fg_run(const FgPlan& p, const uint16_t* X, const uint16_t* W, float* 
   return fg_launch_shape<8, 4>(a, grid, stream);
 }
 
-}  // namespace
 
 // ---------------------------------------------------------------- the consumers
 // Every consumer adds the S split partials of each element in split order, 16

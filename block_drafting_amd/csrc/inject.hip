@@ -477,13 +477,22 @@ static inline size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 struct GemmPlan {
   int bm, bn, bk, S, steps_per_split, tiles;
   bool wide;
+  bool stream;  // the weight-streaming GEMM (fg_run) with plan f
+  FgPlan f;
 };
+
+// Rows up to which the projection runs as the weight-streaming GEMM
+#ifndef BD_INJECT_STREAM_M
+#define BD_INJECT_STREAM_M 128
+#endif
 
 // The fused 256 x 256 projection covers M > 256 when every 256-column tile
 // lies inside one layer's K or V block (n_kv * hd a multiple of 256); its d_in
-// split comes from a cost model of waves and partial traffic.  Otherwise 256 x BD_GEMM_BN
-// tiles (M > 128) or 64 x 128 tiles (small M, weight-bound), split until about
-// BD_GEMM_WGS run, followed by the finish pass.
+// split comes from a cost model of waves and partial traffic.  Up to
+// BD_INJECT_STREAM_M rows the projection is bound by streaming the weights
+// and runs as the library's weight-streaming GEMM (warp-specialised loader
+// waves, a planned d_in split).  Otherwise 256 x BD_GEMM_BN tiles split until
+// about BD_GEMM_WGS run.  Every split is followed by the finish pass.
 static bool wide_fits(int M, int n_kv, int hd) {
   return M > 256 && (hd == 64 || hd == 128) && (size_t(n_kv) * hd) % WBN == 0;
 }
@@ -501,7 +510,7 @@ static int inject_cus() {
 }
 
 static GemmPlan gemm_plan(int M, int N, int Kd, bool wide) {
-  GemmPlan p;
+  GemmPlan p{};
   p.wide = wide;
   if (p.wide) {
     p.bm = WBM; p.bn = WBN; p.bk = WBK;
@@ -523,6 +532,14 @@ static GemmPlan gemm_plan(int M, int N, int Kd, bool wide) {
     }
     p.steps_per_split = (steps + best_S - 1) / best_S;
     p.S = (steps + p.steps_per_split - 1) / p.steps_per_split;
+    return p;
+  }
+  if (M <= BD_INJECT_STREAM_M) {
+    p.stream = true;
+    p.f = fg_plan(M, N, Kd);
+    p.S = p.f.S;
+    p.steps_per_split = p.f.steps_per_split;
+    p.bm = p.bn = p.bk = p.tiles = 0;
     return p;
   }
   const bool big = M > 128 && N % BD_GEMM_BN == 0;
@@ -562,6 +579,11 @@ static size_t ws_bytes_exact(int M, int d_in, int N, int n_kv, int hd) {
   GemmPlan p = gemm_plan(M, N, d_in, wide);
   if (wide && p.S == 1) return wide_layout(M).total;
   return al(size_t(p.S) * M * N * 4);
+}
+
+size_t inject_ws_bytes_call(int M, int d_in, int L, int n_kv, int hd) {
+  if (M <= 0) return 0;
+  return ws_bytes_exact(M, d_in, L * 2 * n_kv * hd, n_kv, hd);
 }
 
 // The size reported covers every call with up to M rows (the unsplit wide
@@ -612,7 +634,10 @@ hipError_t launch_inject(const uint16_t* h, const uint16_t* w, const uint16_t* g
     else hipLaunchKernelGGL(ik_proj<64>, grid, dim3(WNT), 0, stream, a);
     if (p.S == 1) return hipGetLastError();
   }
-  if (!wide) {
+  if (!wide && p.stream) {
+    const hipError_t e = fg_run(p.f, h, w, static_cast<float*>(ws), M, N, d_in, stream);
+    if (e != hipSuccess) return e;
+  } else if (!wide) {
     GemmArgs g;
     g.A = h; g.Bw = w; g.P = static_cast<float*>(ws);
     g.M = M; g.N = N; g.Kd = d_in; g.S = p.S; g.steps_per_split = p.steps_per_split;

@@ -88,6 +88,9 @@ const char* blockdraft_last_error(void);
  * k_cache, v_cache  device bf16 [L, T_cap, n_kv, hd], updated in place; a row
  *             whose slot falls outside [0, T_cap) is skipped.
  * Supported: hd in {64, 128}; d_in a positive multiple of 64; 1 <= n_kv <= 64.
+ * Workspace: inject_kv_workspace_size(M, ...) bytes, 16-byte aligned, serve
+ * every call with up to M rows; a call returns BD_E_WORKSPACE only when the
+ * workspace is smaller than the part of it that call uses.
  * ------------------------------------------------------------------------ */
 size_t inject_kv_workspace_size(int32_t M, int32_t d_in, int32_t L, int32_t n_kv, int32_t hd);
 
