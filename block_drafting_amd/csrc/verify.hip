@@ -9,12 +9,14 @@
 // batched verification can flip near-tied tokens, hence the fixed reduction
 // orders here and the ratio / margin diagnostics.
 //
-// Pass 1 (vb_stats) streams every logits row once, split in chunks of 8192:
-// per chunk the maximum and its lowest index, the sum of exp((z - max) / T)
-// (fp32 lanes, fp64 across lanes) and, under top-k, the chunk's k best
-// (value desc, index asc).  Greedy and top-k: pass 2 (vb_decide, one
-// workgroup per request) merges the chunks of its rows, applies the filters,
-// runs the accept chain and draws over the filtered support.  Full-vocabulary
+// Pass 1 streams every logits row once, in chunks of 8192, with persistent
+// workgroups that each take an equal run of (row, chunk) pairs and write one
+// record per row they touch: vb_stats_stream the maximum and its lowest
+// index and the sum of exp((z - max) / T) (fp32 lanes, fp64 across lanes),
+// vb_topk_stream under top-k the k best (value desc, index asc).  Greedy and
+// top-k: pass 2 (vb_decide, one workgroup per request, after vb_merge_rows
+// under top-k) merges the records of its rows, applies the filters, runs the
+// accept chain and draws over the filtered support.  Full-vocabulary
 // sampling needs the chosen row pair once more: there pass 2
 // (vb_decide_sums, one workgroup per (chunk, request)) merges the request's
 // rows and runs the accept chain in every workgroup, then sums the draw
@@ -47,7 +49,6 @@ constexpr int PICK_FAST_NCH = 64;          // chunks whose run sums the draw kee
 #endif
 #define BD_STATS_OCC __attribute__((amdgpu_waves_per_eu(BD_STATS_WPE)))
 constexpr int STATS_GRID = BD_STATS_GRID;
-constexpr int CAND_PER_WAVE = 64;
 
 enum { JOB_NONE = 0, JOB_RESID = 1, JOB_BONUS = 2 };
 
@@ -353,180 +354,284 @@ __global__ __launch_bounds__(VT) BD_STATS_OCC void vb_stats_stream(VerifyArgs a)
 }
 
 // -------------------------------------------------------------------------
-// Pass 1, top-k form: one chunk per workgroup; besides the maximum (and the
-// sum when asked) it finds the chunk's k best (value desc, index asc).
+// Pass 1, streaming top-k form: a persistent workgroup walks its run of (row,
+// chunk) pairs as the streaming form does, in half chunks (16 logits per
+// thread, the next half's loads in flight).  Each wave keeps, for the row it
+// is in, a bound and an LDS list of its logits that beat it, with no barrier
+// inside the row: at the row's first half chunk of the run the bound is the
+// k-th largest of the wave's 64 lane maxima (k of its logits are at least that
+// large, so each of the wave's own k best, value desc and index asc, is too).
+// Every half chunk appends the wave's logits that beat the bound.  When the
+// list would overflow (or holds 2k entries still under that first bound) the
+// list's k best replace it and the k-th of them becomes the bound (strict from
+// then on: later logits have larger indices, so an equal value comes after
+// it); a half chunk that still does not fit falls back to k rounds of a wave
+// argmax over the wave's own logits of it.  The row's k best are among the
+// union of the waves' own k best: at the row's last half chunk of the run wave
+// 0 selects them from the four lists for the record, whose first entry is
+// also the record's maximum and lowest-index argmax.
 // -------------------------------------------------------------------------
+constexpr int TKW_CAP = 256;       // list entries per wave (values and indices: 8 KB per workgroup)
+constexpr int TKW_Q = TKW_CAP / 64;
+constexpr int HPT = VPT / 2;       // logits per thread of a half chunk
+constexpr int HCH = VCH / 2;       // logits of a half chunk
+
+// the logits of the half chunk at `start` (thread t: slot s < HPT at
+// start + slot_offset(s, t)); slots past the row re-read its first logit
 template <bool VEC>
-__global__ __launch_bounds__(VT) void vb_stats(VerifyArgs a) {
-  __shared__ float s_v[4];
-  __shared__ int s_i[4];
-  __shared__ double s_d[4];
-  __shared__ float s_cv[4 * CAND_PER_WAVE];
-  __shared__ int s_ci[4 * CAND_PER_WAVE];
-  __shared__ int s_cn[4];
-  __shared__ int s_over;
-  __shared__ uint32_t s_kk[4 * 64];  // per wave: its k largest lane-maximum keys
-  __shared__ uint32_t s_tk;
+__device__ __forceinline__ void load_half(const float* __restrict__ row, int start, int V, int t, float (&x)[HPT]) {
+  if (VEC) {
+#pragma unroll
+    for (int j = 0; j < HPT / 4; ++j) {
+      const int e = start + 4 * (j * VT + t);
+      const float4 f = ld_stream(row + (e < V ? e : 0));
+      x[4 * j] = f.x; x[4 * j + 1] = f.y; x[4 * j + 2] = f.z; x[4 * j + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < HPT; ++j) {
+      const int e = start + j * VT + t;
+      x[j] = row[e < V ? e : 0];
+    }
+  }
+}
 
+// The k best (value desc, index asc) of up to 64 Q entries held in the
+// wave's registers (empty entries: index INT32_MAX), by the whole wave: the
+// k-th largest value key T by a bitwise search (one ballot count per bit and
+// register), then the entries with key >= T (ties at T included) staged in
+// LDS and sorted by a wave bitonic sort.  More than 64 of those (heavy ties)
+// fall back to k rounds of a wave argmax over the registers.  Lane r < k gets
+// pick r (value -inf, index INT32_MAX when there are fewer than k entries).
+// The staging area (64 entries) may be where the entries were loaded from:
+// every lane holds its entries before it is written.
+template <int Q>
+__device__ __forceinline__ void wave_top_k(const float (&v)[Q], const int (&id)[Q], int k, float* stage_v,
+                                           int* stage_i, float& mv, int& mi) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) key[q] = id[q] == INT32_MAX ? 0u : order_key(v[q]);  // real keys are >= 1
+  uint32_t T = 0;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = T | (1u << bit);
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) n += __popcll(__ballot(key[q] >= c));
+    if (n >= k) T = c;
+  }
+  if (T == 0) T = 1;  // fewer than k entries: all of them
+  int m = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) m += __popcll(__ballot(key[q] >= T));
+  mv = -INFINITY;
+  mi = INT32_MAX;
+  if (m <= 64) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int off = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const bool p = key[q] >= T;
+      const unsigned long long msk = __ballot(p);
+      const int pos = off + __builtin_amdgcn_mbcnt_hi(unsigned(msk >> 32), __builtin_amdgcn_mbcnt_lo(unsigned(msk), 0u));
+      if (p) { stage_v[pos] = v[q]; stage_i[pos] = id[q]; }
+      off += __popcll(msk);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float sv = lane < m ? stage_v[lane] : -INFINITY;
+    int si = lane < m ? stage_i[lane] : INT32_MAX;
+    wave_sort_best_first(sv, si);
+    if (lane < k) { mv = sv; mi = si; }
+    return;
+  }
+  float pv = INFINITY;
+  int pi = -1;
+  for (int r = 0; r < k; ++r) {
+    float cv = -INFINITY;
+    int ci = INT32_MAX;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if ((pi < 0 || better(pv, pi, v[q], id[q])) && better(v[q], id[q], cv, ci)) { cv = v[q]; ci = id[q]; }
+    wave_argmax(cv, ci);
+    if (ci == INT32_MAX) break;
+    if (lane == r) { mv = cv; mi = ci; }
+    pv = cv;
+    pi = ci;
+  }
+}
+
+struct TopkState {
+  int cnt;     // entries of the wave's list
+  float tv;    // bound: a logit is a candidate when v > tv (strict) or v >= tv
+  int strict;
+};
+
+// the wave's list replaced by its k best, best first; the k-th becomes the
+// (strict) bound when there were at least k entries
+__device__ __forceinline__ void topk_trim(TopkState& st, float* lv, int* li, int k) {
+  const int lane = threadIdx.x & 63;
+  float v[TKW_Q];
+  int id[TKW_Q];
+#pragma unroll
+  for (int q = 0; q < TKW_Q; ++q) {
+    const int j = lane + 64 * q;
+    v[q] = j < st.cnt ? lv[j] : -INFINITY;
+    id[q] = j < st.cnt ? li[j] : INT32_MAX;
+  }
+  float mv;
+  int mi;
+  wave_top_k<TKW_Q>(v, id, k, lv, li, mv, mi);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int kept = st.cnt < k ? st.cnt : k;
+  if (lane < kept) { lv[lane] = mv; li[lane] = mi; }
+  if (st.cnt >= k) {
+    st.tv = lane_value(mv, k - 1);
+    st.strict = 1;
+  }
+  st.cnt = kept;
+}
+
+// Appends the wave's logits of the half chunk that beat the bound to its
+// list (one ballot per slot; a slot no lane hits costs one compare).  Entries
+// past the capacity are not written; returns false when some did not fit.
+template <bool VEC, bool STRICT, bool FULL>
+__device__ __forceinline__ bool topk_append(const VerifyArgs& a, TopkState& st, const float (&x)[HPT], int start,
+                                            float* lv, int* li) {
+  const int t = threadIdx.x;
+  int base = st.cnt;
+#pragma unroll
+  for (int s = 0; s < HPT; ++s) {
+    const int e = start + slot_offset<VEC>(s, t);
+    const bool hit = (STRICT ? x[s] > st.tv : x[s] >= st.tv) && (FULL || e < a.V);
+    const unsigned long long m = __ballot(hit);
+    if (m) {
+      const int pos = base + __builtin_amdgcn_mbcnt_hi(unsigned(m >> 32), __builtin_amdgcn_mbcnt_lo(unsigned(m), 0u));
+      if (hit && pos < TKW_CAP) { lv[pos] = x[s]; li[pos] = e; }
+      base += __popcll(m);
+    }
+  }
+  st.cnt = base < TKW_CAP ? base : TKW_CAP;
+  return base <= TKW_CAP;
+}
+
+template <bool VEC>
+__device__ __forceinline__ bool topk_append(const VerifyArgs& a, TopkState& st, const float (&x)[HPT], int start,
+                                            float* lv, int* li) {
+  if (start + HCH <= a.V)
+    return st.strict ? topk_append<VEC, true, true>(a, st, x, start, lv, li)
+                     : topk_append<VEC, false, true>(a, st, x, start, lv, li);
+  return st.strict ? topk_append<VEC, true, false>(a, st, x, start, lv, li)
+                   : topk_append<VEC, false, false>(a, st, x, start, lv, li);
+}
+
+template <bool VEC>
+__device__ __forceinline__ void topk_half(const VerifyArgs& a, TopkState& st, const float (&x)[HPT], int start,
+                                          bool first, bool last, size_t slot, float* s_bv, int* s_bi, int* s_cnt) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int row = blockIdx.x / a.nch;
-  const int c = blockIdx.x - row * a.nch;
-  const int start = c * VCH;
-  const float* zr = row_ptr(a, row);
-
-  float x[VPT];
-  load_chunk<VEC>(zr, start, a.V, t, x);
-
-  float bv = -INFINITY;
-  int bi = INT32_MAX;
+  const int k = a.topk;
+  float* lv = s_bv + w * TKW_CAP;
+  int* li = s_bi + w * TKW_CAP;
+  if (first) {
+    float lm = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < VPT; ++s) {
-    int e = start + slot_offset<VEC>(s, t);
-    if (e < a.V && (x[s] > bv || bi == INT32_MAX)) { bv = x[s]; bi = e; }
+    for (int s = 0; s < HPT; ++s) lm = (start + slot_offset<VEC>(s, t) < a.V) ? fmaxf(lm, x[s]) : lm;
+    st.cnt = 0;
+    st.tv = key_value(wave_nth_key(order_key(lm), k));
+    st.strict = 0;
   }
-  float lane_best = bv;
-  block_argmax(bv, bi, s_v, s_i);
-  const size_t rc = size_t(row) + blockIdx.x;  // record slot (cpw = 1)
-  if (t == 0) { a.ws.cmax[rc] = bv; a.ws.carg[rc] = bi; }
-
-  if (a.need_sum) {
-    double sum = 0.0;
-    if (bi != INT32_MAX && bv != -INFINITY) {
-      float part = 0.f;
-#pragma unroll
-      for (int s = 0; s < VPT; ++s) {
-        const float p = exp2_hw((x[s] - bv) * a.c2);
-        part += (start + slot_offset<VEC>(s, t) < a.V) ? p : 0.f;
-      }
-      sum = double(part);
-    }
-    sum = block_sum_f64(sum, s_d);
-    if (t == 0) a.ws.csum[rc] = sum;
-  }
-
-  if (a.topk > 0) {
-    const int k = a.topk;
-    // The chunk's k-th largest lane maximum bounds its k best from below (k
-    // elements are at least that large).  Each wave finds its own k-th
-    // largest lane maximum by a bitwise search over order-preserving keys and
-    // hands its k lane maxima at or above it to wave 0, which takes the k-th
-    // largest of those 4k: the chunk's k largest lane maxima are among them.
-    {
-      const uint32_t kb = order_key(lane_best);
-      const uint32_t tw = wave_nth_key(kb, k);
-      const bool p = kb >= tw;  // at least k lanes
-      const unsigned long long m = __ballot(p);
-      const int pos = __builtin_amdgcn_mbcnt_hi(unsigned(m >> 32), __builtin_amdgcn_mbcnt_lo(unsigned(m), 0u));
-      if (p && pos < k) s_kk[w * 64 + pos] = kb;
-    }
-    if (t == 0) s_over = 0;
-    __syncthreads();
-    if (w == 0) {
-      uint32_t k4[4];
-#pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) k4[w2] = lane < k ? s_kk[w2 * 64 + lane] : 0u;  // key 0: no element
-      uint32_t T = 0;
-#pragma unroll
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = T | (1u << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) cnt += __popcll(__ballot(k4[w2] >= cand));
-        if (cnt >= k) T = cand;
-      }
-      if (lane == 0) s_tk = T;
-    }
-    __syncthreads();
-    const float thr = key_value(s_tk);
-    // candidates: elements at or above the bound, appended per wave by a
-    // ballot per slot (at most CAND_PER_WAVE per wave)
-    int total = 0;
-#pragma unroll
-    for (int s = 0; s < VPT; ++s) {
-      const int e = start + slot_offset<VEC>(s, t);
-      const bool p = (e < a.V) & (x[s] >= thr);
-      const unsigned long long m = __ballot(p);
-      if (m) {
-        const int pos = total + __builtin_amdgcn_mbcnt_hi(unsigned(m >> 32), __builtin_amdgcn_mbcnt_lo(unsigned(m), 0u));
-        if (p && pos < CAND_PER_WAVE) { s_cv[w * CAND_PER_WAVE + pos] = x[s]; s_ci[w * CAND_PER_WAVE + pos] = e; }
-        total += __popcll(m);
-      }
-    }
-    if (lane == 0) s_cn[w] = total;
-    if (total > CAND_PER_WAVE && lane == 0) s_over = 1;
-    __syncthreads();
-    float* ov = a.ws.ctv + rc * k;
-    int* oi = a.ws.cti + rc * k;
-    const int n0 = s_cn[0], n01 = n0 + s_cn[1], n012 = n01 + s_cn[2], n_all = n012 + s_cn[3];
-    if (!s_over && n_all <= 64) {
-      // wave 0 sorts all candidates best first (empty lanes last) and keeps k
-      if (w == 0) {
-        float v = -INFINITY;
-        int id = INT32_MAX;
-        if (lane < n_all) {
-          const int ww = (lane >= n0) + (lane >= n01) + (lane >= n012);
-          const int off = lane - (ww == 0 ? 0 : ww == 1 ? n0 : ww == 2 ? n01 : n012);
-          v = s_cv[ww * CAND_PER_WAVE + off];
-          id = s_ci[ww * CAND_PER_WAVE + off];
-        }
-        wave_sort_best_first(v, id);
-        if (lane < k) { ov[lane] = v; oi[lane] = id; }
-      }
-    } else if (!s_over) {
-      // more than 64 in all (k near 64): each wave sorts its own list, then
-      // wave 0 takes the k best by a 4-way merge (lane q < 4 holding list q's
-      // head, the round's winner advancing)
-      float v = -INFINITY;
-      int id = INT32_MAX;
-      if (lane < s_cn[w]) { v = s_cv[w * CAND_PER_WAVE + lane]; id = s_ci[w * CAND_PER_WAVE + lane]; }
-      wave_sort_best_first(v, id);
-      __syncthreads();
-      s_cv[w * CAND_PER_WAVE + lane] = v;  // sorted, empty entries last
-      s_ci[w * CAND_PER_WAVE + lane] = id;
-      __syncthreads();
-      if (w == 0) {
-        int hq = 0;
-        float hv = lane < 4 ? s_cv[lane * CAND_PER_WAVE] : -INFINITY;
-        int hi = lane < 4 ? s_ci[lane * CAND_PER_WAVE] : INT32_MAX;
-        float ov_l = -INFINITY;
-        int oi_l = INT32_MAX;
-        for (int r = 0; r < k; ++r) {
-          float bv = hv;
-          int bi = hi;
-          wave_argmax(bv, bi);
-          if (lane == r) { ov_l = bv; oi_l = bi; }
-          if (bi != INT32_MAX && hi == bi) {  // indices are distinct: one lane wins
-            ++hq;
-            hv = hq < CAND_PER_WAVE ? s_cv[lane * CAND_PER_WAVE + hq] : -INFINITY;
-            hi = hq < CAND_PER_WAVE ? s_ci[lane * CAND_PER_WAVE + hq] : INT32_MAX;
-          }
-        }
-        if (lane < k) { ov[lane] = ov_l; oi[lane] = oi_l; }
-      }
-    } else {
-      // exact fallback: k rounds, each taking the best element strictly
-      // after the previous pick in (value desc, index asc) order
+  const int cnt0 = st.cnt;
+  if (!topk_append<VEC>(a, st, x, start, lv, li)) {
+    // the half chunk did not fit: its entries are dropped, the list trimmed
+    // to its k best (a stricter bound), and the half chunk appended again
+    st.cnt = cnt0;
+    topk_trim(st, lv, li, k);
+    const int cnt1 = st.cnt;
+    if (!topk_append<VEC>(a, st, x, start, lv, li)) {
+      // still too many: the wave's own k best of the half chunk, k rounds
+      // of a wave argmax
+      st.cnt = cnt1;
       float pv = INFINITY;
       int pi = -1;
       for (int r = 0; r < k; ++r) {
         float cv = -INFINITY;
         int ci = INT32_MAX;
 #pragma unroll
-        for (int s = 0; s < VPT; ++s) {
-          int e = start + slot_offset<VEC>(s, t);
-          if (e < a.V && (pi < 0 || better(pv, pi, x[s], e)) && better(x[s], e, cv, ci)) {
-            cv = x[s]; ci = e;
-          }
+        for (int s = 0; s < HPT; ++s) {
+          const int e = start + slot_offset<VEC>(s, t);
+          if (e < a.V && (pi < 0 || better(pv, pi, x[s], e)) && better(x[s], e, cv, ci)) { cv = x[s]; ci = e; }
         }
-        block_argmax(cv, ci, s_v, s_i);
-        if (t == 0) { ov[r] = cv; oi[r] = ci; }
-        if (ci == INT32_MAX) {
-          for (int r2 = r + 1 + t; r2 < k; r2 += VT) { ov[r2] = -INFINITY; oi[r2] = INT32_MAX; }
-          break;
-        }
-        pv = cv; pi = ci;
+        wave_argmax(cv, ci);
+        if (ci == INT32_MAX) break;
+        if (lane == 0) { lv[st.cnt] = cv; li[st.cnt] = ci; }
+        ++st.cnt;
+        pv = cv;
+        pi = ci;
       }
     }
+  } else if (!st.strict && st.cnt > 2 * k) {
+    // the first bound is loose: once the list holds 2k the k-th best becomes
+    // the bound
+    topk_trim(st, lv, li, k);
+  }
+  if (last) {
+    // the record: each wave's k best, then the k best of those four lists
+    topk_trim(st, lv, li, k);
+    if (lane == 0) s_cnt[w] = st.cnt;
+    __syncthreads();
+    if (w == 0) {
+      float v[VT / 64];
+      int id[VT / 64];
+#pragma unroll
+      for (int q = 0; q < VT / 64; ++q) {
+        const bool ok = lane < s_cnt[q];
+        v[q] = ok ? s_bv[q * TKW_CAP + lane] : -INFINITY;
+        id[q] = ok ? s_bi[q * TKW_CAP + lane] : INT32_MAX;
+      }
+      float mv;
+      int mi;
+      wave_top_k<VT / 64>(v, id, k, s_bv, s_bi, mv, mi);
+      if (lane < k) { a.ws.ctv[slot * k + lane] = mv; a.ws.cti[slot * k + lane] = mi; }
+      if (lane == 0) { a.ws.cmax[slot] = mv; a.ws.carg[slot] = mi; }
+    }
+    __syncthreads();
+  }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(VT) BD_STATS_OCC void vb_topk_stream(VerifyArgs a) {
+  __shared__ float s_bv[(VT / 64) * TKW_CAP];
+  __shared__ int s_bi[(VT / 64) * TKW_CAP];
+  __shared__ int s_cnt[VT / 64];
+  const int t = threadIdx.x, w = blockIdx.x;
+  const long long total = (long long)a.n_rows * a.nch;
+  const long long x0 = (long long)w * a.cpw;
+  const long long x1 = min(total, x0 + a.cpw);
+  if (x0 >= x1) return;
+  // half chunks h = 2 x + half of the chunks x in [x0, x1)
+  const long long h0 = 2 * x0, h1 = 2 * x1;
+  TopkState st{0, -INFINITY, 0};
+  float xa[HPT], xb[HPT];
+  auto rowp = [&](long long h) { return row_ptr(a, int((h >> 1) / a.nch)); };
+  auto hstart = [&](long long h) { return int((h >> 1) % a.nch) * VCH + int(h & 1) * HCH; };
+  auto is_first = [&](long long h) { return (h & 1) == 0 && (h == h0 || (h >> 1) % a.nch == 0); };
+  auto is_last = [&](long long h) { return (h & 1) == 1 && (h + 1 == h1 || ((h >> 1) + 1) % a.nch == 0); };
+  auto slot = [&](long long h) { return size_t((h >> 1) / a.nch) + size_t(w); };
+  // two half chunks per iteration (h0 and h1 are even): register double buffer
+  load_half<VEC>(rowp(h0), hstart(h0), a.V, t, xa);
+  for (long long h = h0; h < h1; h += 2) {
+    load_half<VEC>(rowp(h + 1), hstart(h + 1), a.V, t, xb);
+    topk_half<VEC>(a, st, xa, hstart(h), is_first(h), false, slot(h), s_bv, s_bi, s_cnt);
+    // the look-ahead past the run re-reads its last half chunk (in bounds, never consumed)
+    const long long hn = h + 2 < h1 ? h + 2 : h + 1;
+    load_half<VEC>(rowp(hn), hstart(hn), a.V, t, xa);
+    topk_half<VEC>(a, st, xb, hstart(h + 1), false, is_last(h + 1), slot(h + 1), s_bv, s_bi, s_cnt);
   }
 }
 
@@ -1480,9 +1585,9 @@ static VerifyLayout verify_layout(int B, int n_trows, int V, int top_k, bool bet
   const size_t nch = (size_t(V) + VCH - 1) / VCH;
   const size_t rows = 2 * size_t(n_trows) - size_t(B);
   const size_t n_draft = size_t(n_trows) - size_t(B);
-  // record slots: row + workgroup; the top-k pass uses rows * nch workgroups,
-  // the streaming pass at most max(rows * nch, STATS_GRID)
-  const size_t rc = rows + (rows * nch > size_t(STATS_GRID) ? rows * nch : size_t(STATS_GRID));
+  // record slots: row + workgroup, with at most min(rows * nch, STATS_GRID)
+  // workgroups in pass 1
+  const size_t rc = rows + (rows * nch < size_t(STATS_GRID) ? rows * nch : size_t(STATS_GRID));
   const size_t k = top_k > 0 ? size_t(top_k) : 0;
   size_t o = 0;
   L.cmax = o; o += al(rc * 4);
@@ -1553,10 +1658,14 @@ hipError_t launch_verify(const float* zt, const float* zd, const int* dtok, cons
   const bool vec = (V & 3) == 0;
   const long long work = (long long)a.n_rows * a.nch;
   if (k > 0) {
-    // top-k: one chunk per workgroup
-    a.cpw = 1;
-    if (vec) hipLaunchKernelGGL(vb_stats<true>, dim3(unsigned(work)), dim3(VT), 0, stream, a);
-    else hipLaunchKernelGGL(vb_stats<false>, dim3(unsigned(work)), dim3(VT), 0, stream, a);
+    // top-k (sampling only, so no sums are needed): persistent workgroups
+    // with equal runs of chunks, as below
+    long long cpw = (work + STATS_GRID - 1) / STATS_GRID;
+    if (cpw < 1) cpw = 1;
+    a.cpw = int(cpw);
+    const unsigned grid = unsigned((work + cpw - 1) / cpw);
+    if (vec) hipLaunchKernelGGL(vb_topk_stream<true>, dim3(grid), dim3(VT), 0, stream, a);
+    else hipLaunchKernelGGL(vb_topk_stream<false>, dim3(grid), dim3(VT), 0, stream, a);
   } else {
     // at most STATS_GRID persistent workgroups with equal runs of chunks
     long long cpw = (work + STATS_GRID - 1) / STATS_GRID;

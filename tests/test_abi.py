@@ -223,9 +223,9 @@ def test_select_block_validation_codes(lib):
 def test_noalloc_verify_size_limit_on_the_host(lib):
     # the size check comes before any device call, so it runs without a GPU
     F = ctypes.c_float
-    need = lib.verify_block_workspace_size(256, 15, 151936, 64)
+    need = lib.verify_block_workspace_size(1024, 15, 151936, 64)
     assert need > bd.NOALLOC_SCRATCH_BYTES
-    st = lib.verify_block_noalloc(1 << 20, 1 << 20, 1 << 20, 1 << 20, 256, 15, 151936, F(1.0), 64, F(1.0),
+    st = lib.verify_block_noalloc(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1024, 15, 151936, F(1.0), 64, F(1.0),
                                   1 << 20, 1 << 20, None, None, None, None, None)
     assert st == bd.BD_E_WORKSPACE
     assert "static array" in bd.last_error()

@@ -60,7 +60,7 @@ def test_noalloc_matches_workspace_call_twice(first, second):
 def test_noalloc_rejects_calls_beyond_the_scratch_size():
     import block_drafting_amd as bd
     say("noalloc size limit")
-    B, G, V, k = 256, 15, 151936, 64
+    B, G, V, k = 1024, 15, 151936, 64
     need = bd.verify_block_workspace_size(B, G, V, k)
     assert need > bd.NOALLOC_SCRATCH_BYTES
     dev = "cuda"
