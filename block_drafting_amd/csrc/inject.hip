@@ -483,7 +483,7 @@ struct GemmPlan {
 
 // Rows up to which the projection runs as the weight-streaming GEMM
 #ifndef BD_INJECT_STREAM_M
-#define BD_INJECT_STREAM_M 128
+#define BD_INJECT_STREAM_M 256
 #endif
 
 // The fused 256 x 256 projection covers M > 256 when every 256-column tile

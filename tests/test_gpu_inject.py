@@ -71,8 +71,18 @@ def test_ragged_requests_large_positions():
     run_case(3, 4, 128, 1024, [5, 0, 70, 1], [0, 3, 32000, 32767 - 1], 2)
 
 
-def test_m_above_128_uses_big_tiles():
-    run_case(2, 8, 128, 512, [150, 150], [100, 0], 3)
+def test_m_above_256_without_whole_head_tiles_uses_big_tiles():
+    """M = 300 with 3 KV heads of 128 (n_kv * hd = 384: the 256-column tiles
+    would straddle heads, so not the fused wide kernel): 256-row split tiles
+    and the finish pass."""
+    run_case(2, 3, 128, 512, [150, 150], [100, 0], 3)
+
+
+def test_m_up_to_256_streams_the_weights():
+    """M = 200 and M = 256 (the largest): the weight-streaming GEMM with its
+    d_in split and the finish pass."""
+    run_case(2, 8, 128, 1024, [120, 80], [100, 0], 12)
+    run_case(1, 4, 64, 640, [16] * 16, list(range(0, 1600, 100)), 13)
 
 
 def test_wide_tiles_two_m_tiles_one_step_splits():
