@@ -46,10 +46,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+# the sources each call's kernels are built from (a committed counter
+# measurement counts only while their hash is unchanged)
 KERNEL_SOURCES = {
-    "inject_kv": "block_drafting_amd/csrc/inject.hip",
-    "draft_block_attn": "block_drafting_amd/csrc/attn.hip",
-    "verify_block": "block_drafting_amd/csrc/verify.hip",
+    "inject_kv": ("block_drafting_amd/csrc/inject.hip", "block_drafting_amd/csrc/forward.hip",
+                  "block_drafting_amd/csrc/bd_gemm.hpp", "block_drafting_amd/csrc/bd_common.hpp"),
+    "draft_block_attn": ("block_drafting_amd/csrc/attn.hip", "block_drafting_amd/csrc/bd_common.hpp"),
+    "verify_block": ("block_drafting_amd/csrc/verify.hip", "block_drafting_amd/csrc/bd_common.hpp"),
 }
 
 
@@ -72,9 +75,13 @@ def parse():
     return ap.parse_args()
 
 
-def source_sha(path: str) -> str:
-    with open(os.path.join(ROOT, path), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_sha(paths) -> str:
+    """sha256[:16] of the named source files, concatenated in order."""
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(config: str, call: str):

@@ -32,28 +32,24 @@ cycles of the dispatch times the SIMD count) and MfmaFlopsBF16 (bf16 matrix
 flops executed); bench.py divides the latter by the call's time.
 """
 import csv
-import hashlib
 import os
 import statistics
 import sys
 from collections import Counter, defaultdict
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+from bench import KERNEL_SOURCES, source_sha  # noqa: E402
 
-# call -> (kernel name prefix, kernel source); the source hash ties a measured
-# figure to the code it was measured on
+# call -> the name prefixes of its kernels in the round (the weight-streaming
+# GEMM runs the projection of up to 256 rows; nothing else in a round uses it)
 CALLS = {
-    "inject_kv": ("bd::ik_", "block_drafting_amd/csrc/inject.hip"),
-    "draft_block_attn": ("bd::attn_", "block_drafting_amd/csrc/attn.hip"),
-    "verify_block": ("bd::vb_", "block_drafting_amd/csrc/verify.hip"),
+    "inject_kv": ("bd::ik_", "bd::fg_gemm"),
+    "draft_block_attn": ("bd::attn_",),
+    "verify_block": ("bd::vb_",),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_KIB = 262144.0  # the calibration copy: 256 MiB read and 256 MiB written
-
-
-def source_sha(path):
-    with open(os.path.join(ROOT, path), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def short(name):
@@ -73,8 +69,8 @@ def short(name):
 
 
 def call_of(name):
-    for call, (prefix, _) in CALLS.items():
-        if name.startswith(prefix):
+    for call, prefixes in CALLS.items():
+        if name.startswith(prefixes):
             return call
     return None
 
@@ -148,8 +144,9 @@ def traffic(config, d):
              f"{cf:.4f}; WRITE_SIZE {wc['WRITE_SIZE']:.1f} KiB -> factor {cw:.4f}",
              "# dispatches from the first attention launch on; bytes_per_call = sum over the call's kernels of "
              "(FETCH_SIZE * fetch factor + WRITE_SIZE * write factor) * 1024, each kernel averaged over its "
-             "dispatches at its most frequent grid; source_sha = sha256[:16] of the kernel source measured"]
-    for call, (_, src) in CALLS.items():
+             "dispatches at its most frequent grid; source_sha = sha256[:16] of the kernel sources measured"]
+    for call in CALLS:
+        src = KERNEL_SOURCES[call]
         if call not in kf or call not in kw:
             continue
         tot, parts = 0.0, []
@@ -176,7 +173,8 @@ def mfma(config, d):
              "cycles x SIMDs) of the call's matrix kernels, weighted by their MFMA instructions; exec_flops = bf16 "
              "matrix flops executed per call (MfmaFlopsBF16, 512 per counted operation), summed over the call's "
              "kernels"]
-    for call, (_, src) in CALLS.items():
+    for call in CALLS:
+        src = KERNEL_SOURCES[call]
         flops = util_w = n_w = 0.0
         parts = []
         for k, g, _ in kk.get(call, []):
