@@ -182,6 +182,49 @@ def test_topk_with_tied_logits():
         compare(o, g, u, greedy=False, label=f"topk ties k={k}", zt=zt, zd=zd, T=1.0, k=k, p=p)
 
 
+def structured_rows(kind, n, V, rng):
+    """n rows of one kind: 0 ascending, 1 constant, 2 finite at 7 places only
+    (-inf elsewhere), 3 descending."""
+    if kind == 0:
+        z = np.tile(np.linspace(-3.0, 3.0, V, dtype=np.float32), (n, 1))
+    elif kind == 1:
+        z = np.full((n, V), 0.25, np.float32)
+    elif kind == 2:
+        z = np.full((n, V), -np.inf, np.float32)
+        for r in range(n):
+            z[r, rng.choice(V, 7, replace=False)] = rng.standard_normal(7).astype(np.float32)
+    else:
+        z = np.tile(np.linspace(3.0, -3.0, V, dtype=np.float32), (n, 1))
+    return z + (rng.standard_normal((n, V)).astype(np.float32) * 1e-3 if kind in (0, 3) else 0)
+
+
+def test_topk_structured_rows_every_path():
+    """Rows that drive the streaming top-k statistics through its rare paths,
+    at a size where each workgroup walks several chunks: ascending logits (every
+    half chunk beats the bound: list trims, undone half chunks and the k-round
+    fallback), constant logits (every logit ties with the bound: the lowest
+    indices are kept), fewer finite logits than k (-inf elsewhere), and
+    descending logits (nothing after the first chunk)."""
+    rng = np.random.default_rng(31)
+    B, G, V = 32, 3, 151936
+    zt = np.empty((B, G + 1, V), np.float32)
+    zd = np.empty((B, G, V), np.float32)
+    for b in range(B):
+        zt[b] = structured_rows(b % 4, G + 1, V, rng)
+        zd[b] = structured_rows(b % 4, G, V, rng)
+    u = rng.random((B, G + 1, 2), dtype=np.float32)
+    for k, p in ((20, 0.95), (64, 1.0)):
+        # drafted tokens the drafter could draw: among its own k best
+        dt = np.empty((B, G), np.int32)
+        for b in range(B):
+            for i in range(G):
+                dt[b, i] = ov.row_order(zd[b, i])[rng.integers(0, min(k, 7))]
+        say(f"top-k structured rows k={k} p={p}")
+        o = oracle_verify(zt, zd, dt, u, 1.0, k, p)
+        g = run_gpu(zt, zd, dt, u, 1.0, k, p)
+        compare(o, g, u, greedy=False, label=f"topk structured k={k}", zt=zt, zd=zd, T=1.0, k=k, p=p)
+
+
 @pytest.mark.parametrize("T,k,p", [(0.0, 0, 1.0), (1.0, 0, 1.0), (0.8, 20, 0.95)])
 def test_probabilities_within_1e5(T, k, p):
     say(f"probs T={T} k={k}")
