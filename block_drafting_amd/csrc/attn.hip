@@ -104,6 +104,7 @@ __device__ __forceinline__ int req_tiles(const AttnArgs& a, int b) {
 
 constexpr int TMIN = 4;     // fewest tiles a workgroup takes
 constexpr int MAXSEG = 64;  // partial records one merge may combine
+constexpr int MGRP = 8;     // records whose loads the merge keeps in flight together
 
 // Shared schedule: every workgroup (and the merge) derives the same tile
 // prefix over requests from ctx_len: item i = b * n_kv + g owns global tiles
@@ -536,11 +537,16 @@ __global__ __launch_bounds__(64 * NW) BD_ATTN_OCC(NW) void attn_partial(AttnArgs
 
 // One workgroup per (item, 32-row wave block): the records' (max, normaliser)
 // pairs are read in parallel into LDS, each row's weights 2^(m_s - M) / L
-// follow, then the weighted sum of the records in their stored (accumulator)
-// order, with the loads of four records in flight together, transposed through
-// LDS so the bf16 rows leave as whole rows.
+// follow (the rows' records shared out over the threads), then the weighted
+// sum of the records in their stored (accumulator) order, with the loads of
+// eight records in flight together (a small batch spreads an item over many
+// workgroups: 32 records at batch 1), transposed through LDS so the bf16 rows
+// leave whole.
 template <int HD>
 __global__ __launch_bounds__(MT) void attn_merge(AttnArgs a) {
+  constexpr int TPR = MT / 32;       // threads per row in the weight pass
+  constexpr int NP = 32 * HD / 8;    // 16-byte pieces of a record's row block
+  constexpr int PPT = NP / MT;
   extern __shared__ int s_pref[];
   __shared__ float2 s_ml[MAXSEG * 32];                                  // [record][row]
   __shared__ float s_f[MAXSEG * 32];                                    // [record][row]
@@ -562,16 +568,23 @@ __global__ __launch_bounds__(MT) void attn_merge(AttnArgs a) {
     s_ml[e] = *reinterpret_cast<const float2*>(a.wml + ((slot0 + s) * a.Rp + 32 * wb + r) * 2);
   }
   __syncthreads();
-  if (t < 32) {
+  {
+    // TPR threads per row (consecutive lanes), each taking every TPR-th
+    // record; the partial maxima and sums are combined across them
+    const int r = t / TPR, q = t % TPR;
     float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, s_ml[s * 32 + t].x);
+    for (int s = q; s < ns; s += TPR) M = fmaxf(M, s_ml[s * 32 + r].x);
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
     float L = 0.f;
-    for (int s = 0; s < ns; ++s) L += s_ml[s * 32 + t].y * exp2f(s_ml[s * 32 + t].x - M);
+    for (int s = q; s < ns; s += TPR) L += s_ml[s * 32 + r].y * exp2f(s_ml[s * 32 + r].x - M);
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) L += __shfl_xor(L, o);
     const float inv = 1.f / L;
     // records hold O_s / l_s: weight l_s 2^(m_s - M) / L
-    for (int s = 0; s < ns; ++s) s_f[s * 32 + t] = s_ml[s * 32 + t].y * exp2f(s_ml[s * 32 + t].x - M) * inv;
-    if (t < nr && a.lse) {
-      const int row = 32 * wb + t;
+    for (int s = q; s < ns; s += TPR) s_f[s * 32 + r] = s_ml[s * 32 + r].y * exp2f(s_ml[s * 32 + r].x - M) * inv;
+    if (q == 0 && r < nr && a.lse) {
+      const int row = 32 * wb + r;
       const int i = row / a.group, hh = row - i * a.group;
       a.lse[(size_t(b) * a.K + i) * a.n_q + g * a.group + hh] = ok ? (M + log2f(L)) * 0.6931471805599453f : NAN;
     }
@@ -579,7 +592,6 @@ __global__ __launch_bounds__(MT) void attn_merge(AttnArgs a) {
   __syncthreads();
   // 16 bytes p of a record: (d, rp, lane) -> row lane % 32, dims
   // 32 d + 16 rp + 4 (lane / 32) .. + 3 and the same + 8
-  constexpr int NP = 32 * HD / 8, PPT = NP / MT;
   const uint16_t* base = a.wo + (slot0 * (a.Rp / 32) + wb) * (32 * HD);
   const size_t rstride = size_t(a.Rp) * HD;  // elements between consecutive records
   float o[PPT][8];
@@ -587,17 +599,17 @@ __global__ __launch_bounds__(MT) void attn_merge(AttnArgs a) {
   for (int k = 0; k < PPT; ++k)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[k][e] = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += 4) {
-    uint4 v[4][PPT];
+  for (int s0 = 0; s0 < ns; s0 += MGRP) {
+    uint4 v[MGRP][PPT];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < MGRP; ++u) {
       const int s = min(s0 + u, ns - 1);  // a repeated record gets weight 0
 #pragma unroll
       for (int k = 0; k < PPT; ++k)
         v[u][k] = *reinterpret_cast<const uint4*>(base + s * rstride + size_t(t + k * MT) * 8);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < MGRP; ++u) {
 #pragma unroll
       for (int k = 0; k < PPT; ++k) {
         const int rr = (t + k * MT) & 31;
@@ -631,6 +643,113 @@ __global__ __launch_bounds__(MT) void attn_merge(AttnArgs a) {
     const int i = row / a.group, hh = row - i * a.group;
     const size_t oidx = (size_t(b) * a.K + i) * a.n_q + g * a.group + hh;
     *reinterpret_cast<uint4*>(a.out + oidx * HD + c8) = *reinterpret_cast<const uint4*>(&s_o[rr * (HD + 8) + c8]);
+  }
+}
+
+// The same merge split over the head dimension, for few (item, row block)
+// pairs (a small batch, whose items each span many workgroups: 32 records at
+// batch 1): one workgroup per (item, 32-row block, 32-dimension group), whose
+// threads take one 16-byte piece of the group each, in RS record phases
+// (phase r adds records r, r + RS, ...; the phases are added in order through
+// LDS at the end).  Each workgroup then reads a quarter of the records' bytes
+// (at hd 128) with as many loads in flight, so four times the CUs share them.
+template <int HD>
+__global__ __launch_bounds__(MT) void attn_merge_split(AttnArgs a) {
+  constexpr int TPR = MT / 32;       // threads per row in the weight pass
+  constexpr int NPD = 32 * 32 / 8;   // pieces of a 32-dimension group of a row block: 128
+  constexpr int RS = MT / NPD;       // record phases
+  static_assert(RS >= 1 && MT % NPD == 0, "merge shape");
+  extern __shared__ int s_pref[];
+  __shared__ float2 s_ml[MAXSEG * 32];                                  // [record][row]
+  __shared__ float s_f[MAXSEG * 32];                                    // [record][row]
+  __shared__ float s_red[(RS - 1) * NPD * 8 + 1];                      // later phases' sums
+  __shared__ __attribute__((aligned(16))) uint16_t s_o[32 * (32 + 8)];  // bf16 row slices
+  const int item = blockIdx.x, wb = blockIdx.y, dg = blockIdx.z, t = threadIdx.x;
+  const int b = item / a.n_kv, g = item - b * a.n_kv;
+  const Sched sc = build_sched(a, s_pref);
+  const int nt = s_pref[b + 1] - s_pref[b];
+  const int item_s = a.n_kv * s_pref[b] + g * nt;
+  const int w0 = sched_owner(sc, item_s), w1 = sched_owner(sc, item_s + nt - 1);
+  const int ns = min(w1 - w0 + 1, MAXSEG);
+  int64_t cbase;
+  int lo, hi;
+  const bool ok = visible(a, b, cbase, lo, hi) && w1 - w0 + 1 <= MAXSEG;
+  const size_t slot0 = size_t(item) + w0;
+  const int nr = min(32, a.R - 32 * wb);
+  for (int e = t; e < ns * 32; e += MT) {
+    const int s = e >> 5, r = e & 31;
+    s_ml[e] = *reinterpret_cast<const float2*>(a.wml + ((slot0 + s) * a.Rp + 32 * wb + r) * 2);
+  }
+  __syncthreads();
+  {
+    const int r = t / TPR, q = t % TPR;
+    float M = -INFINITY;
+    for (int s = q; s < ns; s += TPR) M = fmaxf(M, s_ml[s * 32 + r].x);
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float L = 0.f;
+    for (int s = q; s < ns; s += TPR) L += s_ml[s * 32 + r].y * exp2f(s_ml[s * 32 + r].x - M);
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) L += __shfl_xor(L, o);
+    const float inv = 1.f / L;
+    for (int s = q; s < ns; s += TPR) s_f[s * 32 + r] = s_ml[s * 32 + r].y * exp2f(s_ml[s * 32 + r].x - M) * inv;
+    if (dg == 0 && q == 0 && r < nr && a.lse) {
+      const int row = 32 * wb + r;
+      const int i = row / a.group, hh = row - i * a.group;
+      a.lse[(size_t(b) * a.K + i) * a.n_q + g * a.group + hh] = ok ? (M + log2f(L)) * 0.6931471805599453f : NAN;
+    }
+  }
+  __syncthreads();
+  // piece pp of the group (pieces (d, rp, lane) with d = dg: 2 x 64)
+  const int pp = t % NPD, ph = t / NPD;
+  const int rr = pp & 31;
+  const uint16_t* base = a.wo + (slot0 * (a.Rp / 32) + wb) * (32 * HD) + size_t(dg * NPD + pp) * 8;
+  const size_t rstride = size_t(a.Rp) * HD;
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  for (int s0 = ph; s0 < ns; s0 += RS * MGRP) {
+    uint4 v[MGRP];
+#pragma unroll
+    for (int u = 0; u < MGRP; ++u) v[u] = *reinterpret_cast<const uint4*>(base + min(s0 + u * RS, ns - 1) * rstride);
+#pragma unroll
+    for (int u = 0; u < MGRP; ++u) {
+      const int s = s0 + u * RS;
+      const float f = s < ns ? s_f[s * 32 + rr] : 0.f;
+      const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] += bf16_to_f32(uint16_t(wd[e] & 0xffffu)) * f;
+        o[2 * e + 1] += bf16_to_f32(uint16_t(wd[e] >> 16)) * f;
+      }
+    }
+  }
+  if (ph > 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_red[((ph - 1) * NPD + pp) * 8 + e] = o[e];
+  }
+  __syncthreads();
+  if (ph == 0) {
+    for (int q = 1; q < RS; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] += s_red[((q - 1) * NPD + pp) * 8 + e];
+    const int lane = pp & 63, rp = pp >> 6;
+    const int dim = 16 * rp + 4 * (lane >> 5);  // within the group
+    const uint2 lo4 = ok ? make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]))
+                         : make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
+    const uint2 hi4 = ok ? make_uint2(pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]))
+                         : make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
+    *reinterpret_cast<uint2*>(&s_o[rr * 40 + dim]) = lo4;
+    *reinterpret_cast<uint2*>(&s_o[rr * 40 + dim + 8]) = hi4;
+  }
+  __syncthreads();
+  // the group's 32 dimensions of each row: 64 bytes, 16 per thread
+  for (int e = t; e < nr * 4; e += MT) {
+    const int r2 = e >> 2, c8 = (e & 3) * 8;
+    const int row = 32 * wb + r2;
+    const int i = row / a.group, hh = row - i * a.group;
+    const size_t oidx = (size_t(b) * a.K + i) * a.n_q + g * a.group + hh;
+    *reinterpret_cast<uint4*>(a.out + oidx * HD + 32 * dg + c8) = *reinterpret_cast<const uint4*>(&s_o[r2 * 40 + c8]);
   }
 }
 
@@ -708,7 +827,12 @@ static void run_attn(AttnArgs& a, size_t pref_bytes, hipStream_t stream) {
     case 3: run_partial<HD, 3>(a, pref_bytes, stream); break;
     default: run_partial<HD, 4>(a, pref_bytes, stream); break;
   }
-  hipLaunchKernelGGL(attn_merge<HD>, dim3(a.B * a.n_kv, a.Rp / 32), dim3(MT), pref_bytes, stream, a);
+  // few (item, row block) pairs: split each over its 32-dimension groups
+  if (a.B * a.n_kv * (a.Rp / 32) < device_cus())
+    hipLaunchKernelGGL(attn_merge_split<HD>, dim3(a.B * a.n_kv, a.Rp / 32, HD / 32), dim3(MT), pref_bytes, stream,
+                       a);
+  else
+    hipLaunchKernelGGL(attn_merge<HD>, dim3(a.B * a.n_kv, a.Rp / 32), dim3(MT), pref_bytes, stream, a);
 }
 
 hipError_t launch_attn(const uint16_t* q, const uint16_t* kb, const uint16_t* vb, const uint16_t* kc,
