@@ -49,7 +49,7 @@ constexpr int MT = 256;  // threads of a merge workgroup
 #endif
 // stages of the partial kernel's LDS tile ring (S - 1 tiles in flight)
 #ifndef BD_ATTN_STAGES
-#define BD_ATTN_STAGES 3
+#define BD_ATTN_STAGES 2
 #endif
 #define BD_ATTN_OCC(NW) __attribute__((amdgpu_waves_per_eu(NW == 1 ? 1 : BD_ATTN_WPE)))
 
