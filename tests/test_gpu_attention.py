@@ -101,13 +101,21 @@ def test_window_never_reads_outside():
     check(q, kb, vb, kc, vc, base, ctx, W, label="window")
 
 
-def test_invalid_request_metadata_gives_nan_not_fault():
-    q, kb, vb, kc, vc, base, ctx, T = case(3, 16, 32, 8, 128, [100, 200, 300], 7)
+@pytest.mark.parametrize("B,n_q,n_kv", [(3, 32, 8), (80, 16, 4)])
+def test_invalid_request_metadata_gives_nan_not_fault(B, n_q, n_kv):
+    """A request whose context length lies beyond max_ctx and the cache gets
+    NaN outputs and lse; the others are finite.  Few (item, row block) pairs
+    take the merge split over dimension groups (3 requests x 8 heads x 2 row
+    blocks), many the one workgroup per pair merge (80 x 4 x 2 = 640)."""
+    rng = np.random.default_rng(7)
+    ctx0 = rng.integers(50, 350, B)
+    q, kb, vb, kc, vc, base, ctx, T = case(B, 16, n_q, n_kv, 128, ctx0, 7)
     bad = ctx.copy()
     bad[1] = 10_000  # beyond max_ctx and beyond the cache
-    go, _ = run_gpu(q, kb, vb, kc, vc, base, bad, 0, max_ctx=400)
-    assert np.isnan(go[1]).all()
-    assert np.isfinite(go[0]).all() and np.isfinite(go[2]).all()
+    go, gl = run_gpu(q, kb, vb, kc, vc, base, bad, 0, max_ctx=400)
+    assert np.isnan(go[1]).all() and np.isnan(gl[1]).all()
+    keep = np.arange(B) != 1
+    assert np.isfinite(go[keep]).all() and np.isfinite(gl[keep]).all()
 
 
 def test_deterministic_run_to_run():
