@@ -384,41 +384,96 @@ struct FinishArgs {
   double inv_freq[64];
 };
 
-__global__ __launch_bounds__(256) void ik_finish(FinishArgs f) {
-  const int m = blockIdx.x, l = blockIdx.y, t = threadIdx.x;
-  // request of this row
-  if (f.B <= 0 || m >= f.row_cu[f.B]) return;
+// A thread item is eight values of one (row, layer): a K item holds dims d0..d0+3
+// and hd/2+d0..hd/2+d0+3 of one head (the rotary pairs), a V item eight
+// consecutive columns; either is two float4 per split.  The K and V items of the
+// row run side by side, every split's loads of an item are issued before the
+// first is added (in split order), and the row's request is looked up while
+// they are in flight.
+constexpr int FIN_SG = 4;  // splits whose loads are in flight together
+
+struct FinRow {
+  bool valid;
+  int pos;
+  int64_t slot;
+};
+
+// request, position and cache slot of row m (uniform); row_cu is non-decreasing
+__device__ __forceinline__ FinRow fin_lookup(const FinishArgs& f, int m) {
+  FinRow r{false, 0, 0};
+  if (f.B <= 0 || m >= f.row_cu[f.B]) return r;
   int lo = 0, hi = f.B - 1;
   while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
+    const int mid = (lo + hi + 1) >> 1;
     if (f.row_cu[mid] <= m) lo = mid; else hi = mid - 1;
   }
-  const int b = lo;
-  const int j = m - f.row_cu[b];
-  const int pos = f.row_pos0[b] + j;
-  const int64_t slot = f.cache_base[b] + pos;
-  if (j < 0 || slot < 0 || slot >= f.T_cap) return;
+  const int j = m - f.row_cu[lo];
+  r.pos = f.row_pos0[lo] + j;
+  r.slot = f.cache_base[lo] + r.pos;
+  r.valid = j >= 0 && r.slot >= 0 && r.slot < f.T_cap;
+  return r;
+}
 
+// One item (thread it of the row's 2 n_kv hd / 8): loads every split, then adds
+// them in split order and writes the eight outputs.  FIRST: the row lookup runs
+// between the first splits' loads and their use (it precedes every store of the
+// kernel, so its reads are scalar and do not wait for the vector loads).
+template <bool FIRST>
+__device__ __forceinline__ void fin_item(const FinishArgs& f, int m, int l, int it, FinRow& row) {
   const int hd = f.hd, half = hd >> 1;
-  const int tph = hd / 8;  // threads per K head (4 + 4 dims each)
-  const int n_items_k = f.n_kv * tph;
-  const int n_items_v = f.n_kv * hd / 8;
-  const size_t kcol0 = size_t(l) * 2 * f.n_kv * hd;
-  const size_t vcol0 = kcol0 + size_t(f.n_kv) * hd;
+  const int tph = hd / 8;                 // K items per head
+  const int n_items_k = f.n_kv * tph;     // as many V items (n_kv * hd / 8)
   const size_t MN = size_t(f.M) * f.N;
-  const float* prow = f.P + size_t(m) * f.N;
-
-  for (int it = t; it < n_items_k; it += 256) {
-    const int head = it / tph, jj = it - head * tph;
-    const int d0 = 4 * jj;  // dims d0..d0+3 and half+d0..half+d0+3
-    const float* p0 = prow + kcol0 + size_t(head) * hd;
-    float xa[4] = {0.f, 0.f, 0.f, 0.f}, xb[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < f.S; ++s) {
-      const float4 va = *reinterpret_cast<const float4*>(p0 + s * MN + d0);
-      const float4 vb = *reinterpret_cast<const float4*>(p0 + s * MN + half + d0);
-      xa[0] += va.x; xa[1] += va.y; xa[2] += va.z; xa[3] += va.w;
-      xb[0] += vb.x; xb[1] += vb.y; xb[2] += vb.z; xb[3] += vb.w;
+  const float* prow = f.P + size_t(m) * f.N + size_t(l) * 2 * f.n_kv * hd;  // the layer's K columns, then V
+  const bool act = it < 2 * n_items_k;
+  const bool isk = it < n_items_k;
+  int head = 0, d0 = 0, off0 = 0, off1 = 0;
+  if (isk) {
+    head = it / tph;
+    d0 = 4 * (it - head * tph);
+    off0 = head * hd + d0;
+    off1 = off0 + half;
+  } else {
+    off0 = f.n_kv * hd + (it - n_items_k) * 8;
+    off1 = off0 + 4;
+  }
+  float xa[4] = {0.f, 0.f, 0.f, 0.f}, xb[4] = {0.f, 0.f, 0.f, 0.f};
+  double fr[4] = {0.0, 0.0, 0.0, 0.0};
+  uint16_t ga[4] = {0, 0, 0, 0}, gb[4] = {0, 0, 0, 0};
+  for (int s0 = 0; s0 < f.S; s0 += FIN_SG) {
+    float4 va[FIN_SG], vb[FIN_SG];
+#pragma unroll
+    for (int u = 0; u < FIN_SG; ++u) {
+      va[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      vb[u] = va[u];
     }
+#pragma unroll
+    for (int u = 0; u < FIN_SG; ++u)
+      if (s0 + u < f.S && act) {
+        va[u] = *reinterpret_cast<const float4*>(prow + (s0 + u) * MN + off0);
+        vb[u] = *reinterpret_cast<const float4*>(prow + (s0 + u) * MN + off1);
+      }
+    if (s0 == 0 && isk) {
+      // the item's rotary frequencies and gains, in flight with the partials
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        fr[c] = kernarg_elem<double>(offsetof(FinishArgs, inv_freq), d0 + c);
+        if (f.gain) {
+          ga[c] = f.gain[l * hd + d0 + c];
+          gb[c] = f.gain[l * hd + half + d0 + c];
+        }
+      }
+    }
+    if (FIRST && s0 == 0) row = fin_lookup(f, m);
+#pragma unroll
+    for (int u = 0; u < FIN_SG; ++u)
+      if (s0 + u < f.S) {
+        xa[0] += va[u].x; xa[1] += va[u].y; xa[2] += va[u].z; xa[3] += va[u].w;
+        xb[0] += vb[u].x; xb[1] += vb[u].y; xb[2] += vb[u].z; xb[3] += vb[u].w;
+      }
+  }
+  if (!row.valid || !act) return;
+  if (isk) {
     float ss = 0.f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) ss += xa[c] * xa[c] + xb[c] * xb[c];
@@ -427,37 +482,31 @@ __global__ __launch_bounds__(256) void ik_finish(FinishArgs f) {
     uint16_t oa[4], ob[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int i = d0 + c;
-      float ga = 1.f, gb = 1.f;
-      if (f.gain) {
-        ga = bf16_to_f32(f.gain[l * hd + i]);
-        gb = bf16_to_f32(f.gain[l * hd + half + i]);
-      }
-      const float a = xa[c] * inv * ga, bb = xb[c] * inv * gb;
-      // angle pos * theta^(-2i/hd) in fp64, reduced in fp64
+      const float gxa = f.gain ? bf16_to_f32(ga[c]) : 1.f, gxb = f.gain ? bf16_to_f32(gb[c]) : 1.f;
+      const float a = xa[c] * inv * gxa, bb = xb[c] * inv * gxb;
+      // angle pos * theta^(-2i/hd), i = d0 + c, in fp64, reduced in fp64
       float sn, cs;
-      sincos_angle(double(pos) * kernarg_elem<double>(offsetof(FinishArgs, inv_freq), i), &sn, &cs);
+      sincos_angle(double(row.pos) * fr[c], &sn, &cs);
       oa[c] = f32_to_bf16(a * cs - bb * sn);
       ob[c] = f32_to_bf16(bb * cs + a * sn);
     }
-    uint16_t* kd = f.kc + ((size_t(l) * f.T_cap + slot) * f.n_kv + head) * hd;
+    uint16_t* kd = f.kc + ((size_t(l) * f.T_cap + row.slot) * f.n_kv + head) * hd;
     *reinterpret_cast<uint2*>(kd + d0) = make_uint2(oa[0] | (uint32_t(oa[1]) << 16), oa[2] | (uint32_t(oa[3]) << 16));
     *reinterpret_cast<uint2*>(kd + half + d0) = make_uint2(ob[0] | (uint32_t(ob[1]) << 16), ob[2] | (uint32_t(ob[3]) << 16));
+  } else {
+    uint16_t* vd = f.vc + (size_t(l) * f.T_cap + row.slot) * f.n_kv * hd + (off0 - f.n_kv * hd);
+    *reinterpret_cast<uint4*>(vd) = make_uint4(pack_bf16x2(xa[0], xa[1]), pack_bf16x2(xa[2], xa[3]),
+                                               pack_bf16x2(xb[0], xb[1]), pack_bf16x2(xb[2], xb[3]));
   }
-  for (int it = t; it < n_items_v; it += 256) {
-    const int c0 = it * 8;  // column within this layer's V block
-    const float* p0 = prow + vcol0 + c0;
-    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < f.S; ++s) {
-      const float4 va = *reinterpret_cast<const float4*>(p0 + s * MN);
-      const float4 vb = *reinterpret_cast<const float4*>(p0 + s * MN + 4);
-      x[0] += va.x; x[1] += va.y; x[2] += va.z; x[3] += va.w;
-      x[4] += vb.x; x[5] += vb.y; x[6] += vb.z; x[7] += vb.w;
-    }
-    uint16_t* vd = f.vc + (size_t(l) * f.T_cap + slot) * f.n_kv * hd + c0;
-    *reinterpret_cast<uint4*>(vd) = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
-                                               pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
-  }
+}
+
+__global__ __launch_bounds__(256) void ik_finish(FinishArgs f) {
+  const int m = blockIdx.x, l = blockIdx.y, t = threadIdx.x;
+  FinRow row;
+  fin_item<true>(f, m, l, t, row);
+  if (!row.valid) return;
+  const int n_items = 2 * f.n_kv * (f.hd / 8);
+  for (int base = 256; base < n_items; base += 256) fin_item<false>(f, m, l, base + t, row);
 }
 
 // ---------------------------------------------------------------- host side

@@ -85,6 +85,14 @@ def test_m_up_to_256_streams_the_weights():
     run_case(1, 4, 64, 640, [16] * 16, list(range(0, 1600, 100)), 13)
 
 
+def test_finish_rows_wider_than_one_workgroup():
+    """n_kv * hd above 1024 (more K and V items per row than the finish pass's
+    256 threads): 24 heads of 128 at M = 32 (weight-streaming GEMM, long d_in
+    split) and 12 heads of 128 at M = 300 (256-column tiles, split)."""
+    run_case(1, 24, 128, 8192, [16, 16], [5, 900], 14)
+    run_case(1, 12, 128, 1024, [200, 100], [0, 3000], 15)
+
+
 def test_wide_tiles_two_m_tiles_one_step_splits():
     """M = 700: three 256-row tiles of the wide kernel, the last ragged; d_in =
     128 gives two 64-wide steps, split one per workgroup, then the finish pass."""
