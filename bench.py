@@ -484,6 +484,14 @@ def next_rows(a, cfg, r, bd, torch, dev, stream, q, kb, vb, kc, vc, cache_base, 
     ex["select_block"] = select_block(cfg, bd, torch, dev, stream, zd)
     ex["overlap"] = overlap_rounds(cfg, r, bd, torch, dev, q, kb, vb, zt, zd, dtok, uni)
     ex["inject_prefill"] = inject_prefill(cfg, r, bd, torch, dev, stream)
+    # the same at the other batches' context sums: 8 x 32768 rows at d_in 25600,
+    # and the 128 lognormal contexts (about 411k rows)
+    import workloads as wl
+    ex["inject_prefill_other"] = {}
+    for name in ("27b-long", "sweep-b128"):
+        c2 = wl.CONFIGS[name]
+        ex["inject_prefill_other"][name] = inject_prefill(c2, wl.make_round(c2, parts=("inject",)), bd, torch, dev,
+                                                          stream)
     ex["draft_pass"] = draft_pass(cfg, r, bd, torch, dev, stream, kc, vc, cache_base, ctx_len, max_ctx)
     ex["library_gemm"] = library_gemm(cfg, r, bd, torch, dev, stream, kc, vc, cache_base, ctx_len)
     ex["stream_reference"] = stream_reference(torch, dev, stream)
@@ -627,7 +635,11 @@ def inject_prefill(cfg, r, bd, torch, dev, stream):
     M = int(r.ctx_len.astype(np.int64).sum())
     gen = torch.Generator(device=dev)
     gen.manual_seed(11)
-    h = torch.randn((M, cfg.d_in), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+    h = torch.empty((M, cfg.d_in), dtype=torch.int16, device=dev)
+    step = (1 << 28) // cfg.d_in  # drawn in row slices: no full-size float32 copy
+    for i in range(0, M, step):
+        n = min(step, M - i)
+        h[i:i + n] = torch.randn((n, cfg.d_in), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
     i16 = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev)
     w, g = i16(r.w_bits), i16(r.k_norm_bits)
     cu = torch.from_numpy(np.concatenate([[0], np.cumsum(r.ctx_len.astype(np.int64))]).astype(np.int32)).to(dev)

@@ -207,21 +207,35 @@ def test_full_size_sweep_round_sampled_rows():
     _full_size_sampled_rows("sweep-b128", [0, 511, 512, 1000, 1535, 1536, 2047])
 
 
-def test_prefill_scale_materialization_sampled_rows():
+def device_bf16_normal(M, d, seed):
+    """[M, d] standard normal bf16 (as int16 bits) drawn on the device in row
+    slices, so no full-size float32 copy is ever held."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    h = torch.empty((M, d), dtype=torch.int16, device="cuda")
+    step = max(1, (1 << 28) // d)
+    for i in range(0, M, step):
+        n = min(step, M - i)
+        h[i:i + n] = torch.randn((n, d), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+    return h
+
+
+@pytest.mark.parametrize("name", ["qwen3-8b", "27b-long", "sweep-b128"])
+def test_prefill_scale_materialization_sampled_rows(name):
     """Immediate materialization of a whole context batch (NEXT row): every
-    request's context at once, M = sum of the 8B round's context lengths
-    (about 74k rows) in one call; the oracle checks 12 sampled rows."""
+    request's context at once, M = the sum of the workload's context lengths
+    in one call (about 74k rows for the 8B round's batch, 262k for the 27B
+    batch at d_in 25600, 411k for the batch of 128 lognormal contexts); the
+    oracle checks 12 sampled rows."""
     import block_drafting_amd as bd
-    cfg = wl.CONFIGS["qwen3-8b"]
+    cfg = wl.CONFIGS[name]
     r = wl.make_round(cfg, parts=("inject",), random_gains=True)
     ctx = r.ctx_len.astype(np.int64)
     M = int(ctx.sum())
     row_cu = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)
     pos0 = np.zeros(cfg.B, np.int32)
-    say(f"prefill-scale inject M={M}")
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(11)
-    h = torch.randn((M, cfg.d_in), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+    say(f"prefill-scale inject {name} M={M} d_in={cfg.d_in}")
+    h = device_bf16_normal(M, cfg.d_in, 11)
     kc = torch.full((cfg.L, r.T_cap, cfg.n_kv, cfg.hd), SENTINEL, dtype=torch.int16, device="cuda")
     vc = torch.full_like(kc, SENTINEL)
     bd.inject_kv(h, cuda_bits(r.w_bits), cuda_bits(r.k_norm_bits), torch.from_numpy(row_cu).cuda(),
@@ -245,3 +259,5 @@ def test_prefill_scale_materialization_sampled_rows():
         ev = rel_err(bits_to_f64(gv[l]), ov_[l])
         say(f"  layer {l}: K rel err {ek:.2e}  V rel err {ev:.2e}")
         assert ek <= TOL and ev <= TOL
+    del h, kc, vc
+    torch.cuda.empty_cache()
