@@ -51,7 +51,9 @@ __global__ __launch_bounds__(256) void read_stream(const float4* __restrict__ bu
 // heads of 256 B, the cache row of one position).  MODE 0: tile j is the 8 KB
 // at j * 8 KB (contiguous); MODE 1: one head's 256 B of 32 consecutive rows,
 // tiles head-major (the attention kernel's items); MODE 2: the same tiles with
-// the heads interleaved (tile j: row block j / 8, head j % 8).
+// the heads interleaved (tile j: row block j / 8, head j % 8); MODE 3: tile j
+// is the 8 KB at (j mod 256) * 8 KB, so every tile comes from the same 2 MB,
+// which stays in each XCD's L2 (the rate an L2-resident operand reaches LDS).
 template <int L, int A>
 __device__ __forceinline__ void wait_ring(int ahead) {
   if constexpr (A == 0) {
@@ -74,6 +76,8 @@ __global__ __launch_bounds__(64) void tile_ring(const uint8_t* K, const uint8_t*
     size_t base;
     if (MODE == 0) {
       base = size_t(j) * 8192;
+    } else if (MODE == 3) {
+      base = size_t(j % 256) * 8192;
     } else {
       const int g = MODE == 1 ? j / nkt : j % 8, kt = MODE == 1 ? j % nkt : j / 8;
       base = size_t(kt) * 32 * 2048 + size_t(g) * 256;
@@ -81,12 +85,12 @@ __global__ __launch_bounds__(64) void tile_ring(const uint8_t* K, const uint8_t*
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       // MODE 0: 1 KB contiguous; else rows 4 i .. 4 i + 3 of the head, 16 lanes each
-      const uint32_t vo = MODE == 0 ? uint32_t(i * 1024 + lane * 16) : uint32_t((4 * i + lane / 16) * 2048 + (lane % 16) * 16);
+      const uint32_t vo = MODE == 0 || MODE == 3 ? uint32_t(i * 1024 + lane * 16) : uint32_t((4 * i + lane / 16) * 2048 + (lane % 16) * 16);
       dma16(K + base, vo, r0 + st * 16384 + i * 1024);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t vo = MODE == 0 ? uint32_t(i * 1024 + lane * 16) : uint32_t((4 * i + lane / 16) * 2048 + (lane % 16) * 16);
+      const uint32_t vo = MODE == 0 || MODE == 3 ? uint32_t(i * 1024 + lane * 16) : uint32_t((4 * i + lane / 16) * 2048 + (lane % 16) * 16);
       dma16(V + base, vo, r0 + st * 16384 + 8192 + i * 1024);
     }
   };
@@ -194,6 +198,17 @@ int main() {
     run(tile_ring<1, 5>, cus, "ring_head_256B");
     run(tile_ring<2, 5>, cus, "ring_head_cycle");
     run(tile_ring<1, 3>, 3 * cus, "ring_head_256B_x3");
+    // L2-resident tiles: 512 tiles of 16 KB per workgroup from the first 2 MB
+    auto run_l2 = [&](auto kern, int G, const char* name) {
+      const int nt = 512 * G;
+      const double b = double(nt) * 16384;
+      const double us = time_us([&] { hipLaunchKernelGGL(kern, dim3(G), dim3(64), 0, 0, K, V, T, nt); });
+      CHECK(hipGetLastError());
+      std::printf("%-19s bytes %.0f  us %.1f  TB/s %.2f  GB/s per CU %.1f  (grid %d)\n", name, b, us, b / us / 1e6,
+                  b / us / 1e3 / cus, G);
+    };
+    run_l2(tile_ring<3, 5>, cus, "ring_l2_1wave");
+    run_l2(tile_ring<3, 3>, 3 * cus, "ring_l2_3waves");
     CHECK(hipFree(K));
     CHECK(hipFree(V));
   }
