@@ -44,6 +44,23 @@ __global__ __launch_bounds__(256) void read_stream(const float4* __restrict__ bu
   if (acc == -1.25e-30f) sink[0] = acc;  // never true for the data written below
 }
 
+// The same loads, every workgroup reading the first `span` float4 (2 MB, held in
+// each XCD's L2) over and over: the rate an L2-resident operand reaches
+// registers, against the LDS-direct rate of the rings below.
+__global__ __launch_bounds__(256) void read_l2(const float4* __restrict__ buf, int span, int iters, float* sink) {
+  const int t = threadIdx.x;
+  const int off = (blockIdx.x * 4096) % span;  // spread the workgroups' starting points
+  float acc = 0.f;
+  for (int it = 0; it < iters; ++it) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = buf[(off + it * 1024 + u * 256 + t) % span];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc += v[u].x + v[u].y + v[u].z + v[u].w;
+  }
+  if (acc == -1.25e-30f) sink[0] = acc;
+}
+
 // ------------------------------------------------------------ LDS-direct tile rings
 // One wave per workgroup streams tiles of 16 KB (8 KB of K, 8 KB of V, 16 loads
 // of 1 KB) into an S-stage LDS ring with global_load_lds, as the attention
@@ -175,6 +192,14 @@ int main() {
     CHECK(hipGetLastError());
     std::printf("read_stream_nt      bytes %.0f  us %.1f  TB/s %.2f\n", bytes, tn, bytes / tn / 1e6);
     std::printf("read_stream_plain   bytes %.0f  us %.1f  TB/s %.2f\n", bytes, tp, bytes / tp / 1e6);
+    for (int wpc : {4, 8}) {
+      const int G2 = wpc * cus / 4, span = 1 << 17, iters = 2048;  // 2 MB; 8 MB per workgroup
+      const double b2 = double(G2) * iters * 1024 * 16;
+      const double t2 = time_us([&] { hipLaunchKernelGGL(read_l2, dim3(G2), dim3(256), 0, 0, buf, span, iters, sink); });
+      CHECK(hipGetLastError());
+      std::printf("read_l2_w%-10d bytes %.0f  us %.1f  TB/s %.2f  GB/s per CU %.1f\n", wpc, b2, t2, b2 / t2 / 1e6,
+                  b2 / t2 / 1e3 / cus);
+    }
     CHECK(hipFree(buf));
   }
 
