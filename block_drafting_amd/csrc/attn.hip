@@ -102,7 +102,7 @@ __device__ __forceinline__ int req_tiles(const AttnArgs& a, int b) {
   return (hi - lo + TK - 1) / TK + a.nbt;
 }
 
-constexpr int TMIN = 4;     // fewest tiles a workgroup takes
+constexpr int TMIN = 2;     // fewest tiles a workgroup takes (small problems: more, shorter runs)
 constexpr int MAXSEG = 64;  // partial records one merge may combine
 constexpr int MGRP = 8;     // records whose loads the merge keeps in flight together
 
