@@ -57,6 +57,10 @@ static_assert(WFN == 4, "a wave spans 128 columns");
 #ifndef BD_GEMM_WIDE_SW
 #define BD_GEMM_WIDE_SW 2
 #endif
+// Split workgroups grouped by d_in range per XCD (1) or launched as (tile, split) (0)
+#ifndef BD_GEMM_XCD_MAP
+#define BD_GEMM_XCD_MAP 1
+#endif
 constexpr int WBK = BD_GEMM_WIDE_BK, WSA = BD_GEMM_WIDE_SA, WSW = BD_GEMM_WIDE_SW;
 static_assert(WSW >= WSA && WSA >= 2, "ring depths");
 constexpr int WA_BYTES = WBM * WBK * 2;
@@ -191,16 +195,16 @@ __device__ __forceinline__ void proj_epilogue(const ProjArgs& a, floatx16 (&acc)
   }
 }
 
+// One 256 x 256 output tile over one d_in range (split), from the workgroup's
+// LDS rings; the caller's rings are free on entry and free again on return
+// once the workgroup has passed a barrier.
 template <int HD>
-__global__ __launch_bounds__(WNT) void ik_proj(ProjArgs g) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ringA[WSA * WA_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t ringW[WSW * WW_BYTES];
+__device__ __forceinline__ void proj_tile(const ProjArgs& g, int tile, int split, uint8_t* ringA, uint8_t* ringW) {
   constexpr int P = WBK / 8;
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w / WNWN, wn = w % WNWN;
   const int lr = lane & 31, h = lane >> 5;
-  const int tile = blockIdx.x, split = blockIdx.y;
   const int tm = tile / g.tiles_n, tn = tile - tm * g.tiles_n;
   const int m0 = tm * WBM, n0 = tn * WBN;
   const int step0 = split * g.steps_per_split;
@@ -347,6 +351,71 @@ __global__ __launch_bounds__(WNT) void ik_proj(ProjArgs g) {
   if (t < HD / 2) lds_f[t] = kernarg_elem<double>(offsetof(ProjArgs, inv_freq), t);
   __syncthreads();
   proj_epilogue<HD>(g, acc, n0, wn, lane, rslot, rpos, lds_g, lds_f);
+}
+
+template <int HD>
+__global__ __launch_bounds__(WNT) void ik_proj(ProjArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ringA[WSA * WA_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ringW[WSW * WW_BYTES];
+#if BD_GEMM_XCD_MAP
+  // launch index L sits on XCD L mod 8; the workgroups run in the order
+  // (split, column tile) major, row tile minor, and XCD x takes the x-th
+  // eighth of that order, so its workgroups share few H blocks (one d_in
+  // range) and each W block between the row tiles
+  const int tiles_m = (g.M + WBM - 1) / WBM;
+  const int total = tiles_m * g.tiles_n * g.S;
+  const int per_x = (total + 7) / 8;
+  const int q = (blockIdx.x & 7) * per_x + (blockIdx.x >> 3);
+  if (q >= total) return;
+  const int sc = q / tiles_m;
+  proj_tile<HD>(g, (q % tiles_m) * g.tiles_n + sc % g.tiles_n, sc / g.tiles_n, ringA, ringW);
+#else
+  proj_tile<HD>(g, blockIdx.x, blockIdx.y, ringA, ringW);
+#endif
+}
+
+// Persistent form of the unsplit projection (many tiles per CU, e.g. a whole
+// prefill's rows): one workgroup per CU walks its tiles.  The grid is a
+// multiple of 8, and launch index w is taken to sit on XCD w mod 8 (the
+// dispatcher's round-robin; any other placement gives the same results, only
+// less L2 reuse).  The tiles form super-tiles of SM row tiles x SN column
+// tiles, one tile per workgroup of an XCD; XCD x takes super-tiles x, x + 8,
+// x + 16, ... in row-major order, so the workgroups of one XCD work on one
+// super-tile at a time and share its SM H row blocks and SN W column blocks in
+// their L2.
+#ifndef BD_PERSIST_SN
+#define BD_PERSIST_SN 8
+#endif
+struct PersistPlan {
+  int SM, SN, n_sm, n_sn;
+};
+
+__device__ __forceinline__ PersistPlan persist_plan(const ProjArgs& g) {
+  PersistPlan p;
+  const int n_loc = gridDim.x >> 3;
+  p.SN = (n_loc % BD_PERSIST_SN == 0) ? BD_PERSIST_SN : n_loc;
+  p.SM = n_loc / p.SN;
+  const int tiles_m = (g.M + WBM - 1) / WBM;
+  p.n_sm = (tiles_m + p.SM - 1) / p.SM;
+  p.n_sn = (g.tiles_n + p.SN - 1) / p.SN;
+  return p;
+}
+
+template <int HD>
+__global__ __launch_bounds__(WNT) void ik_proj_persist(ProjArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ringA[WSA * WA_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ringW[WSW * WW_BYTES];
+  const PersistPlan p = persist_plan(g);
+  const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int tiles_m = (g.M + WBM - 1) / WBM;
+  for (int s = x; s < p.n_sm * p.n_sn; s += 8) {
+    const int tm = (s / p.n_sn) * p.SM + j / p.SN;
+    const int tn = (s % p.n_sn) * p.SN + j % p.SN;
+    if (tm < tiles_m && tn < g.tiles_n) {
+      proj_tile<HD>(g, tm * g.tiles_n + tn, 0, ringA, ringW);
+      __syncthreads();  // the epilogue's use of the rings ends before the next tile's loads
+    }
+  }
 }
 
 // Before an unsplit projection: the cache slot (-1: not written) and absolute
@@ -530,6 +599,11 @@ struct GemmPlan {
   FgPlan f;
 };
 
+// The persistent form of the unsplit projection (1) or one workgroup per tile (0)
+#ifndef BD_INJECT_PERSIST
+#define BD_INJECT_PERSIST 1
+#endif
+
 // Rows up to which the projection runs as the weight-streaming GEMM
 #ifndef BD_INJECT_STREAM_M
 #define BD_INJECT_STREAM_M 256
@@ -679,8 +753,17 @@ hipError_t launch_inject(const uint16_t* h, const uint16_t* w, const uint16_t* g
     } else {
       a.part = static_cast<float*>(ws);
     }
-    if (hd == 128) hipLaunchKernelGGL(ik_proj<128>, grid, dim3(WNT), 0, stream, a);
-    else hipLaunchKernelGGL(ik_proj<64>, grid, dim3(WNT), 0, stream, a);
+    // more unsplit tiles than CUs: the persistent form, one workgroup per CU
+    // (the grid a multiple of 8 for its XCD placement)
+    const int pgrid = inject_cus() / 8 * 8;
+    if (BD_INJECT_PERSIST && p.S == 1 && pgrid >= 8 && p.tiles > inject_cus()) {
+      if (hd == 128) hipLaunchKernelGGL(ik_proj_persist<128>, dim3(pgrid), dim3(WNT), 0, stream, a);
+      else hipLaunchKernelGGL(ik_proj_persist<64>, dim3(pgrid), dim3(WNT), 0, stream, a);
+    } else {
+      const dim3 g1 = BD_GEMM_XCD_MAP ? dim3((p.tiles * p.S + 7) / 8 * 8) : grid;
+      if (hd == 128) hipLaunchKernelGGL(ik_proj<128>, g1, dim3(WNT), 0, stream, a);
+      else hipLaunchKernelGGL(ik_proj<64>, g1, dim3(WNT), 0, stream, a);
+    }
     if (p.S == 1) return hipGetLastError();
   }
   if (!wide && p.stream) {

@@ -119,6 +119,19 @@ def test_wide_unsplit_fused_epilogue_hd64():
     run_case(2, 4, 64, 64, [40, 400], [3, 0], 11, gains=False)
 
 
+def test_wide_persistent_many_tiles_hd128():
+    """M = 4300 rows x 4096 outputs at d_in = 128: 17 x 16 = 272 unsplit tiles,
+    more than the CUs, so the persistent projection walks its XCD super-tiles
+    (full 8-column super-tiles, a last row tile 204 rows deep)."""
+    run_case(2, 8, 128, 128, [2000, 2300], [0, 30000], 12)
+
+
+def test_wide_persistent_narrow_hd64():
+    """The persistent projection with two column tiles (super-tiles mostly
+    empty) and 129 row tiles, hd = 64, one step of d_in, three ragged requests."""
+    run_case(1, 4, 64, 64, [20000, 12900, 77], [5, 0, 40000], 13)
+
+
 def test_no_gains_hd64():
     run_case(2, 3, 64, 640, [40, 9], [7, 1000], 4, gains=False)
 
