@@ -114,18 +114,31 @@ constexpr int MGRP = 8;     // records whose loads the merge keeps in flight tog
 // Measured: weighting the shares (e.g. more work for the workgroups placed
 // first on a CU, whose older waves win the issue arbitration) does not help,
 // since a CU's workgroups share its bandwidth.
+//
+// Head-synchronous form (BD_ATTN_HEADSYNC): every KV head's items form their
+// own sequence of T1 = sum_b nt_b tiles (requests in order), cut the same way
+// for all heads: workgroup w serves head w mod n_kv in group w / n_kv, and
+// group j takes tiles [floor(j T1 / ge1), floor((j + 1) T1 / ge1)) of its
+// head's sequence (ge1 groups).  The n_kv workgroups of a group read the same
+// cache rows' heads at about the same time.  Records: head g, request b, group
+// j at slot g (B + ge1) + b + j.
+#ifndef BD_ATTN_HEADSYNC
+#define BD_ATTN_HEADSYNC 1
+#endif
 struct Sched {
-  int total;  // all tiles
+  int total;  // all tiles (head-synchronous: tiles of one head's sequence)
   int ge;     // workgroups with work
+  int ge1;    // head-synchronous: groups of n_kv workgroups
 };
 
+// first tile of workgroup w (head-synchronous: of group w, in its head's sequence)
 __device__ __forceinline__ int sched_start(const Sched& s, int w) {
-  return int((long long)s.total * w / s.ge);
+  return int((long long)s.total * w / (BD_ATTN_HEADSYNC ? s.ge1 : s.ge));
 }
 
-// workgroup holding global tile x: the last w with start(w) <= x
+// workgroup (head-synchronous: group) holding tile x: the last w with start(w) <= x
 __device__ __forceinline__ int sched_owner(const Sched& s, int x) {
-  return int((((long long)x + 1) * s.ge - 1) / s.total);
+  return int((((long long)x + 1) * (BD_ATTN_HEADSYNC ? s.ge1 : s.ge) - 1) / s.total);
 }
 
 __device__ Sched build_sched(const AttnArgs& a, int* s_pref /* [B + 1] */) {
@@ -140,18 +153,30 @@ __device__ Sched build_sched(const AttnArgs& a, int* s_pref /* [B + 1] */) {
   __syncthreads();
   Sched s;
   // values read from LDS are the same in every lane: keep them in scalar registers
+#if BD_ATTN_HEADSYNC
+  s.total = __builtin_amdgcn_readfirstlane(s_pref[a.B]);
+  // every share at least tmin tiles (fewer groups for small problems); the
+  // host makes the grid at least n_kv
+  const int gmax = a.grid / a.n_kv;
+  s.ge1 = (long long)s.total >= (long long)gmax * a.tmin ? gmax : (s.total / a.tmin > 1 ? s.total / a.tmin : 1);
+  s.ge = s.ge1 * a.n_kv;
+#else
   s.total = __builtin_amdgcn_readfirstlane(a.n_kv * s_pref[a.B]);
   // every share at least tmin tiles (fewer workgroups for small problems)
   s.ge = (long long)s.total >= (long long)a.grid * a.tmin ? a.grid : (s.total / a.tmin > 1 ? s.total / a.tmin : 1);
+  s.ge1 = 0;
+#endif
   return s;
 }
 
-// request holding global tile x (binary search over the prefix)
+// request holding global tile x (head-synchronous: tile x of a head's
+// sequence), by a binary search over the prefix
 __device__ __forceinline__ int find_req(const AttnArgs& a, const int* s_pref, int x) {
+  const int f = BD_ATTN_HEADSYNC ? 1 : a.n_kv;
   int lo = 0, hi = a.B - 1;
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
-    if (a.n_kv * s_pref[mid] <= x) lo = mid; else hi = mid - 1;
+    if (f * s_pref[mid] <= x) lo = mid; else hi = mid - 1;
   }
   return lo;
 }
@@ -211,23 +236,56 @@ __device__ __forceinline__ void cur_item(const AttnArgs& a, const int* s_pref, C
   c.nctx = ok ? hi - lo : 0;
 }
 
-__device__ __forceinline__ void cur_init(const AttnArgs& a, const int* s_pref, Cur& c, int x) {
+// cursor at tile x (head-synchronous: tile x of head g's sequence)
+__device__ __forceinline__ void cur_init(const AttnArgs& a, const int* s_pref, Cur& c, int x, int g) {
   c.b = __builtin_amdgcn_readfirstlane(find_req(a, s_pref, x));
+#if BD_ATTN_HEADSYNC
+  c.g = g;
+  c.ti = x - __builtin_amdgcn_readfirstlane(s_pref[c.b]);
+#else
+  (void)g;
   const int nt = __builtin_amdgcn_readfirstlane(s_pref[c.b + 1] - s_pref[c.b]);
   const int r = x - a.n_kv * __builtin_amdgcn_readfirstlane(s_pref[c.b]);
   c.g = r / nt;
   c.ti = r - c.g * nt;
+#endif
   cur_item(a, s_pref, c);
 }
 
 __device__ __forceinline__ void cur_next(const AttnArgs& a, const int* s_pref, Cur& c) {
   if (++c.ti < c.nt) return;
   c.ti = 0;
-  if (++c.g == a.n_kv) {
-    c.g = 0;
+  if (BD_ATTN_HEADSYNC || ++c.g == a.n_kv) {
+    if (!BD_ATTN_HEADSYNC) c.g = 0;
     if (++c.b >= a.B) return;  // past the last tile: never read
   }
   cur_item(a, s_pref, c);
+}
+
+// record slot of the cursor's item in workgroup wg
+__device__ __forceinline__ size_t rec_slot(const AttnArgs& a, const Sched& sc, int b, int g, int wg) {
+#if BD_ATTN_HEADSYNC
+  return size_t(g) * (a.B + sc.ge1) + b + wg / a.n_kv;
+#else
+  (void)sc;
+  return size_t(b) * a.n_kv + g + wg;
+#endif
+}
+
+// first record slot and record count of item (b, g)
+__device__ __forceinline__ void item_records(const AttnArgs& a, const Sched& sc, const int* s_pref, int b, int g,
+                                             size_t& slot0, int& nrec) {
+  const int nt = s_pref[b + 1] - s_pref[b];
+#if BD_ATTN_HEADSYNC
+  const int s0 = s_pref[b];
+  const int w0 = sched_owner(sc, s0), w1 = sched_owner(sc, s0 + nt - 1);
+  slot0 = size_t(g) * (a.B + sc.ge1) + b + w0;
+#else
+  const int s0 = a.n_kv * s_pref[b] + g * nt;
+  const int w0 = sched_owner(sc, s0), w1 = sched_owner(sc, s0 + nt - 1);
+  slot0 = size_t(b) * a.n_kv + g + w0;
+#endif
+  nrec = w1 - w0 + 1;
 }
 
 // first K and V rows of the cursor's tile; returns its number of keys (>= 1)
@@ -427,8 +485,9 @@ __global__ __launch_bounds__(64 * NW) BD_ATTN_OCC(NW) void attn_partial(AttnArgs
   const Sched sc = build_sched(a, s_pref);
   const int wg = blockIdx.x;
   if (wg >= sc.ge) return;
-  const int x0 = sched_start(sc, wg);
-  const int x_end = sched_start(sc, wg + 1);
+  const int sw = BD_ATTN_HEADSYNC ? wg / a.n_kv : wg;  // share index (head-synchronous: group)
+  const int x0 = sched_start(sc, sw);
+  const int x_end = sched_start(sc, sw + 1);
   if (x0 >= x_end) return;
   const bool full_wave = (NI % NW == 0) || w < NI % NW;  // issues LMAX loads per tile
   const uint32_t ring0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring)));
@@ -437,7 +496,7 @@ __global__ __launch_bounds__(64 * NW) BD_ATTN_OCC(NW) void attn_partial(AttnArgs
   IssuePlan<HD, NW> plan;
   plan_init<HD, NW>(plan, a.n_kv * HD * 2, w, lane);
   Cur ic, cc;
-  cur_init(a, s_pref, ic, x0);
+  cur_init(a, s_pref, ic, x0, wg % a.n_kv);
   cc = ic;
 #pragma unroll
   for (int s = 0; s < S - 1; ++s) {
@@ -514,7 +573,7 @@ __global__ __launch_bounds__(64 * NW) BD_ATTN_OCC(NW) void attn_partial(AttnArgs
       // fp32) in accumulator order, so each store is one contiguous KB: the
       // 16 bytes (d, rp, lane) hold dims 32 d + 16 rp + 4 h .. + 3 and
       // 32 d + 16 rp + 8 + 4 h .. + 3 of row lr
-      const size_t slot = size_t(cc.b) * a.n_kv + cc.g + wg;
+      const size_t slot = rec_slot(a, sc, cc.b, cc.g, wg);
       const float l = l_run + __shfl_xor(l_run, 32);
       const float il = l > 0.f ? 1.f / l : 0.f;  // l = 0: no key of this segment was visible
       uint16_t* o = a.wo + (slot * (a.Rp / 32) + w) * (32 * HD);
@@ -554,14 +613,13 @@ __global__ __launch_bounds__(MT) void attn_merge(AttnArgs a) {
   const int item = blockIdx.x, wb = blockIdx.y, t = threadIdx.x;
   const int b = item / a.n_kv, g = item - b * a.n_kv;
   const Sched sc = build_sched(a, s_pref);
-  const int nt = s_pref[b + 1] - s_pref[b];
-  const int item_s = a.n_kv * s_pref[b] + g * nt;
-  const int w0 = sched_owner(sc, item_s), w1 = sched_owner(sc, item_s + nt - 1);
-  const int ns = min(w1 - w0 + 1, MAXSEG);
+  size_t slot0;
+  int nrec;
+  item_records(a, sc, s_pref, b, g, slot0, nrec);
+  const int ns = min(nrec, MAXSEG);
   int64_t cbase;
   int lo, hi;
-  const bool ok = visible(a, b, cbase, lo, hi) && w1 - w0 + 1 <= MAXSEG;
-  const size_t slot0 = size_t(item) + w0;
+  const bool ok = visible(a, b, cbase, lo, hi) && nrec <= MAXSEG;
   const int nr = min(32, a.R - 32 * wb);  // valid rows of this block
   for (int e = t; e < ns * 32; e += MT) {
     const int s = e >> 5, r = e & 31;
@@ -667,14 +725,13 @@ __global__ __launch_bounds__(MT) void attn_merge_split(AttnArgs a) {
   const int item = blockIdx.x, wb = blockIdx.y, dg = blockIdx.z, t = threadIdx.x;
   const int b = item / a.n_kv, g = item - b * a.n_kv;
   const Sched sc = build_sched(a, s_pref);
-  const int nt = s_pref[b + 1] - s_pref[b];
-  const int item_s = a.n_kv * s_pref[b] + g * nt;
-  const int w0 = sched_owner(sc, item_s), w1 = sched_owner(sc, item_s + nt - 1);
-  const int ns = min(w1 - w0 + 1, MAXSEG);
+  size_t slot0;
+  int nrec;
+  item_records(a, sc, s_pref, b, g, slot0, nrec);
+  const int ns = min(nrec, MAXSEG);
   int64_t cbase;
   int lo, hi;
-  const bool ok = visible(a, b, cbase, lo, hi) && w1 - w0 + 1 <= MAXSEG;
-  const size_t slot0 = size_t(item) + w0;
+  const bool ok = visible(a, b, cbase, lo, hi) && nrec <= MAXSEG;
   const int nr = min(32, a.R - 32 * wb);
   for (int e = t; e < ns * 32; e += MT) {
     const int s = e >> 5, r = e & 31;
@@ -774,6 +831,7 @@ static int attn_grid(int B, int n_kv, int max_ctx, int window) {
   const int tmin = attn_tmin(max_ctx, window);
   long long g = (tiles + tmin - 1) / tmin;
   if (g > PARTIAL_GRID) g = PARTIAL_GRID;
+  if (g < n_kv) g = n_kv;  // head-synchronous schedule: one group at least
   if (g < 1) g = 1;
   return int(g);
 }
