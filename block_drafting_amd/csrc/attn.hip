@@ -39,10 +39,12 @@ constexpr int TK = 32;   // keys per tile
 constexpr int MT = 256;  // threads of a merge workgroup
 
 // Register budget of the persistent partial kernel (waves per SIMD it must
-// allow); its grid is the number of workgroups resident at once (CUs x
-// workgroups per CU from the occupancy query), at most BD_ATTN_GRID.
+// allow); its grid is at most the number of workgroups resident at once (CUs x
+// workgroups per CU from the occupancy query) and at most BD_ATTN_GRID: three
+// workgroups per CU of 256 (measured at the 8B round: 68.0 us per call against
+// 71.8 us with all four that fit, 76 us with two).
 #ifndef BD_ATTN_GRID
-#define BD_ATTN_GRID 2048
+#define BD_ATTN_GRID 768
 #endif
 #ifndef BD_ATTN_WPE
 #define BD_ATTN_WPE 2
