@@ -76,6 +76,7 @@ struct AttnArgs {
   float* lse;
   uint16_t* wo;  // [items + grid][Rp / 32][HD / 32][2][64 lanes][8] partial O / l (bf16)
   float* wml;  // [items + grid][Rp][2]  running max (exp2 domain), normaliser
+  int2* ihdr;  // [items] first record slot and record count of each item
 };
 
 // visible context of request b, or ok = false when its metadata is invalid
@@ -511,6 +512,7 @@ __global__ __launch_bounds__(64 * NW) BD_ATTN_OCC(NW) void attn_partial(AttnArgs
   bf16x8 qf[HD / 16];
   floatx16 acc[HD / 32];
   float m_run = -INFINITY, l_run = 0.f;
+  bool first_seg = false;  // the current segment starts at the item's first tile
   int stage = 0;
   int ready = x0 - 1;  // tiles up to here are known to be in LDS
   for (int x = x0; x < x_end; ++x) {
@@ -530,6 +532,7 @@ __global__ __launch_bounds__(64 * NW) BD_ATTN_OCC(NW) void attn_partial(AttnArgs
       for (int d = 0; d < HD / 32; ++d) acc[d] = floatx16{};
       m_run = -INFINITY;
       l_run = 0.f;
+      first_seg = cc.ti == 0;
     }
     // refill the stage that every wave finished with before the barrier
     if (x + S - 1 < x_end) {
@@ -590,6 +593,13 @@ __global__ __launch_bounds__(64 * NW) BD_ATTN_OCC(NW) void attn_partial(AttnArgs
                          pk_bf16(c[r0 + 4] * il, c[r0 + 5] * il), pk_bf16(c[r0 + 6] * il, c[r0 + 7] * il));
         }
       if (h == 0) *reinterpret_cast<float2*>(a.wml + (slot * a.Rp + row) * 2) = make_float2(m_run, l);
+      if (first_seg && t == 0) {
+        // the item's first record is this one: its slot and record count for the merge
+        size_t s0;
+        int nrec;
+        item_records(a, sc, s_pref, cc.b, cc.g, s0, nrec);
+        a.ihdr[size_t(cc.b) * a.n_kv + cc.g] = make_int2(int(s0), nrec);
+      }
     }
     cur_next(a, s_pref, cc);
     stage = stage == S - 1 ? 0 : stage + 1;
@@ -614,16 +624,33 @@ __global__ __launch_bounds__(MT) void attn_merge(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_o[32 * (HD + 8)];  // bf16 rows
   const int item = blockIdx.x, wb = blockIdx.y, t = threadIdx.x;
   const int b = item / a.n_kv, g = item - b * a.n_kv;
-  const Sched sc = build_sched(a, s_pref);
-  size_t slot0;
-  int nrec;
-  item_records(a, sc, s_pref, b, g, slot0, nrec);
+  const int2 ih = a.ihdr[item];  // written by the partial kernel
+  const size_t slot0 = size_t(ih.x);
+  const int nrec = ih.y;
   const int ns = min(nrec, MAXSEG);
   int64_t cbase;
   int lo, hi;
   const bool ok = visible(a, b, cbase, lo, hi) && nrec <= MAXSEG;
   const int nr = min(32, a.R - 32 * wb);  // valid rows of this block
-  for (int e = t; e < ns * 32; e += MT) {
+  // 16 bytes p of a record: (d, rp, lane) -> row lane % 32, dims
+  // 32 d + 16 rp + 4 (lane / 32) .. + 3 and the same + 8
+  const uint16_t* base = a.wo + (slot0 * (a.Rp / 32) + wb) * (32 * HD);
+  const size_t rstride = size_t(a.Rp) * HD;  // elements between consecutive records
+  // the (max, normaliser) pairs and the first MGRP records' pieces, all in flight together
+  uint4 v[MGRP][PPT];
+  {
+    const int s = t >> 5, r = t & 31;
+    const float2 ml0 = *reinterpret_cast<const float2*>(a.wml + ((slot0 + min(s, ns - 1)) * a.Rp + 32 * wb + r) * 2);
+#pragma unroll
+    for (int u = 0; u < MGRP; ++u) {
+      const int su = min(u, ns - 1);  // a repeated record gets weight 0
+#pragma unroll
+      for (int k = 0; k < PPT; ++k)
+        v[u][k] = *reinterpret_cast<const uint4*>(base + su * rstride + size_t(t + k * MT) * 8);
+    }
+    if (t < ns * 32) s_ml[t] = ml0;
+  }
+  for (int e = t + MT; e < ns * 32; e += MT) {
     const int s = e >> 5, r = e & 31;
     s_ml[e] = *reinterpret_cast<const float2*>(a.wml + ((slot0 + s) * a.Rp + 32 * wb + r) * 2);
   }
@@ -650,23 +677,20 @@ __global__ __launch_bounds__(MT) void attn_merge(AttnArgs a) {
     }
   }
   __syncthreads();
-  // 16 bytes p of a record: (d, rp, lane) -> row lane % 32, dims
-  // 32 d + 16 rp + 4 (lane / 32) .. + 3 and the same + 8
-  const uint16_t* base = a.wo + (slot0 * (a.Rp / 32) + wb) * (32 * HD);
-  const size_t rstride = size_t(a.Rp) * HD;  // elements between consecutive records
   float o[PPT][8];
 #pragma unroll
   for (int k = 0; k < PPT; ++k)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[k][e] = 0.f;
   for (int s0 = 0; s0 < ns; s0 += MGRP) {
-    uint4 v[MGRP][PPT];
+    if (s0 > 0) {
 #pragma unroll
-    for (int u = 0; u < MGRP; ++u) {
-      const int s = min(s0 + u, ns - 1);  // a repeated record gets weight 0
+      for (int u = 0; u < MGRP; ++u) {
+        const int s = min(s0 + u, ns - 1);  // a repeated record gets weight 0
 #pragma unroll
-      for (int k = 0; k < PPT; ++k)
-        v[u][k] = *reinterpret_cast<const uint4*>(base + s * rstride + size_t(t + k * MT) * 8);
+        for (int k = 0; k < PPT; ++k)
+          v[u][k] = *reinterpret_cast<const uint4*>(base + s * rstride + size_t(t + k * MT) * 8);
+      }
     }
 #pragma unroll
     for (int u = 0; u < MGRP; ++u) {
@@ -726,10 +750,9 @@ __global__ __launch_bounds__(MT) void attn_merge_split(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_o[32 * (32 + 8)];  // bf16 row slices
   const int item = blockIdx.x, wb = blockIdx.y, dg = blockIdx.z, t = threadIdx.x;
   const int b = item / a.n_kv, g = item - b * a.n_kv;
-  const Sched sc = build_sched(a, s_pref);
-  size_t slot0;
-  int nrec;
-  item_records(a, sc, s_pref, b, g, slot0, nrec);
+  const int2 ih = a.ihdr[item];  // written by the partial kernel
+  const size_t slot0 = size_t(ih.x);
+  const int nrec = ih.y;
   const int ns = min(nrec, MAXSEG);
   int64_t cbase;
   int lo, hi;
@@ -868,7 +891,7 @@ size_t attn_ws_bytes(int B, int K, int n_q, int n_kv, int hd, int max_ctx, int w
   if (B <= 0) return 0;
   const size_t Rp = (size_t(K) * (n_q / n_kv) + 31) / 32 * 32;
   const size_t slots = size_t(B) * n_kv + attn_grid(B, n_kv, max_ctx, window);
-  return al(slots * Rp * hd * 2) + al(slots * Rp * 2 * 4);
+  return al(slots * Rp * hd * 2) + al(slots * Rp * 2 * 4) + al(size_t(B) * n_kv * 8);
 }
 
 // one partial-kernel variant: NW = ceil(R / 32) waves of 32 query rows
@@ -917,6 +940,7 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* kb, const uint16_t* vb
   const size_t slots = size_t(B) * n_kv + a.grid;
   a.wo = static_cast<uint16_t*>(ws);
   a.wml = reinterpret_cast<float*>(static_cast<char*>(ws) + al(slots * Rp * hd * 2));
+  a.ihdr = reinterpret_cast<int2*>(static_cast<char*>(ws) + al(slots * Rp * hd * 2) + al(slots * Rp * 2 * 4));
   const size_t pref_bytes = size_t(B + 1) * sizeof(int);
   if (hd == 128) run_attn<128>(a, pref_bytes, stream);
   else run_attn<64>(a, pref_bytes, stream);
