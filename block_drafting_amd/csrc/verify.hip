@@ -724,7 +724,17 @@ __device__ void merge_row(const VerifyArgs& a, int row, int lane, float* s_v = n
     double* kp = a.ws.rkp + size_t(row) * TOPK_MAX;
     float kv_lane = -INFINITY;  // lane r keeps the r-th kept value
     int kept = 0;
-    if (s_v && nrec <= 64) {
+    if (ncand <= 64) {
+      // every candidate in one lane: the k best are the first k lanes after a
+      // wave-wide bitonic sort (value desc, index asc; empty entries, index
+      // INT32_MAX, sort last)
+      float sv = -INFINITY;
+      int si = INT32_MAX;
+      if (lane < ncand) { sv = cv[lane]; si = ci[lane]; }
+      wave_sort_best_first(sv, si);
+      kept = __popcll(__ballot(lane < k && si != INT32_MAX));
+      if (lane < kept) { kv_lane = sv; ki[lane] = si; }
+    } else if (s_v && nrec <= 64) {
       // the chunk lists are sorted best first: a k-way merge, lane l holding
       // list l's head and the round's winner advancing (the lists staged in
       // LDS, loaded eight per lane at a time)
