@@ -229,26 +229,27 @@ CAUSAL, PER_QUERY = 1, 2
 
 
 def _segment_starts_at_last_tile(ctx, K, n_kv, window=0, per_query=False):
-    """Items (b, g) one of whose partial segments holds only the item's last
-    tile, under the kernel's schedule (equal shares of the flattened tiles,
-    at least 4 tiles and at most 64 workgroups per item, grid at most 2048):
-    there a causal block gives rows that see no key of the segment."""
+    """Requests b (every KV head alike) one of whose partial segments holds only
+    the item's last tile, under the kernel's head-synchronous schedule (each
+    head's items form one sequence of tiles, cut into equal group shares of at
+    least 2 tiles, at most 64 groups per item, grid at most 768 and at least
+    n_kv): there a causal block gives rows that see no key of the segment."""
     TK = 32
     vis = window if (window > 0 and max(ctx) > window) else max(ctx)
     nt_max = (vis + TK - 1) // TK + 2
-    tmin = max(4, (nt_max + 61) // 62)
-    grid = max(1, min(2048, -(-len(ctx) * n_kv * nt_max // tmin)))
+    tmin = max(2, (nt_max + 61) // 62)
+    grid = max(n_kv, min(768, -(-len(ctx) * n_kv * nt_max // tmin)), 1)
     nts = []
     for c in ctx:
         w_lo = c + 1 - window if per_query else c - window
         lo = w_lo if (window > 0 and w_lo > 0) else 0
         nts.append((c - lo + TK - 1) // TK + (K + TK - 1) // TK)
     pref = np.concatenate([[0], np.cumsum(nts)])
-    total = n_kv * int(pref[-1])
-    ge = grid if total >= grid * tmin else max(1, total // tmin)
-    starts = {total * w // ge for w in range(ge)}
-    return [(b, g) for b, nt in enumerate(nts) for g in range(n_kv)
-            if nt > 1 and n_kv * pref[b] + g * nt + nt - 1 in starts]
+    total = int(pref[-1])
+    gmax = grid // n_kv
+    groups = gmax if total >= gmax * tmin else max(1, total // tmin)
+    starts = {total * j // groups for j in range(groups)}
+    return [b for b, nt in enumerate(nts) if nt > 1 and int(pref[b]) + nt - 1 in starts]
 
 
 @pytest.mark.parametrize("flags", [CAUSAL, PER_QUERY, CAUSAL | PER_QUERY])
