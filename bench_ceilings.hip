@@ -70,7 +70,11 @@ __global__ __launch_bounds__(256) void read_l2(const float4* __restrict__ buf, i
 // tiles head-major (the attention kernel's items); MODE 2: the same tiles with
 // the heads interleaved (tile j: row block j / 8, head j % 8); MODE 3: tile j
 // is the 8 KB at (j mod 256) * 8 KB, so every tile comes from the same 2 MB,
-// which stays in each XCD's L2 (the rate an L2-resident operand reaches LDS).
+// which stays in each XCD's L2 (the rate an L2-resident operand reaches LDS);
+// MODE 4: workgroup w streams head w mod 8 of its group's rows (groups of 8
+// workgroups cut the 32-row blocks into equal runs: the attention kernel's
+// head-synchronous schedule); MODE 5: two adjacent heads (512 B) of 16 rows per
+// tile, groups of 4 workgroups.
 template <int L, int A>
 __device__ __forceinline__ void wait_ring(int ahead) {
   if constexpr (A == 0) {
@@ -86,12 +90,22 @@ __global__ __launch_bounds__(64) void tile_ring(const uint8_t* K, const uint8_t*
   static_assert(S >= 2 && (S - 2) * 16 < 64, "ring depth");
   __shared__ __attribute__((aligned(1024))) uint8_t ring[S * 16384];
   const int lane = threadIdx.x, G = gridDim.x, w = blockIdx.x;
-  const int j0 = int((long long)ntiles * w / G), j1 = int((long long)ntiles * (w + 1) / G);
+  // modes 4 / 5: groups of 8 (4) workgroups share one range of key tiles
+  const int gs = MODE == 4 ? 8 : MODE == 5 ? 4 : 1;
+  const int nt = MODE == 4 ? T / 32 : MODE == 5 ? T / 16 : ntiles;
+  const int q = w / gs, Q = G / gs;
+  const int j0 = int((long long)nt * q / Q), j1 = int((long long)nt * (q + 1) / Q);
   const uint32_t r0 = __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t(ring)));
   const int nkt = T / 32;
   auto issue = [&](int j, int st) {
     size_t base;
-    if (MODE == 0) {
+    if (MODE == 4) {
+      // head-synchronous: workgroup w streams head w % 8; groups of 8 cut the key tiles
+      base = size_t(j) * 32 * 2048 + size_t(w % 8) * 256;
+    } else if (MODE == 5) {
+      // two heads per workgroup: 16 keys x 512 B per tile buffer
+      base = size_t(j) * 16 * 2048 + size_t(w % 4) * 512;
+    } else if (MODE == 0) {
       base = size_t(j) * 8192;
     } else if (MODE == 3) {
       base = size_t(j % 256) * 8192;
@@ -102,12 +116,16 @@ __global__ __launch_bounds__(64) void tile_ring(const uint8_t* K, const uint8_t*
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       // MODE 0: 1 KB contiguous; else rows 4 i .. 4 i + 3 of the head, 16 lanes each
-      const uint32_t vo = MODE == 0 || MODE == 3 ? uint32_t(i * 1024 + lane * 16) : uint32_t((4 * i + lane / 16) * 2048 + (lane % 16) * 16);
+      const uint32_t vo = MODE == 0 || MODE == 3 ? uint32_t(i * 1024 + lane * 16)
+                        : MODE == 5 ? uint32_t((2 * i + lane / 32) * 2048 + (lane % 32) * 16)
+                                    : uint32_t((4 * i + lane / 16) * 2048 + (lane % 16) * 16);
       dma16(K + base, vo, r0 + st * 16384 + i * 1024);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t vo = MODE == 0 || MODE == 3 ? uint32_t(i * 1024 + lane * 16) : uint32_t((4 * i + lane / 16) * 2048 + (lane % 16) * 16);
+      const uint32_t vo = MODE == 0 || MODE == 3 ? uint32_t(i * 1024 + lane * 16)
+                        : MODE == 5 ? uint32_t((2 * i + lane / 32) * 2048 + (lane % 32) * 16)
+                                    : uint32_t((4 * i + lane / 16) * 2048 + (lane % 16) * 16);
       dma16(V + base, vo, r0 + st * 16384 + 8192 + i * 1024);
     }
   };
@@ -223,6 +241,10 @@ int main() {
     run(tile_ring<1, 5>, cus, "ring_head_256B");
     run(tile_ring<2, 5>, cus, "ring_head_cycle");
     run(tile_ring<1, 3>, 3 * cus, "ring_head_256B_x3");
+    run(tile_ring<4, 5>, cus, "ring_headsync");
+    run(tile_ring<4, 3>, 3 * cus, "ring_headsync_x3");
+    run(tile_ring<5, 5>, cus, "ring_2heads_512B");
+    run(tile_ring<5, 3>, 3 * cus, "ring_2heads_512B_x3");
     // L2-resident tiles: 512 tiles of 16 KB per workgroup from the first 2 MB
     auto run_l2 = [&](auto kern, int G, const char* name) {
       const int nt = 512 * G;
