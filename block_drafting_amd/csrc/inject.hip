@@ -7,13 +7,16 @@
 // result goes straight into the draft KV cache before the draft forward
 // (immediate materialization; the target latents are not kept).
 //
-// Stage 1 (ik_gemm): Y = H . W^T on the gfx950 32x32x16 bf16 MFMA, fp32
-// accumulation, tiles staged in LDS, optional split over d_in; fp32 partial
-// sums go to the workspace.
-// Stage 2 (ik_finish): one workgroup per (row, layer) sums the partials in a
-// fixed order, normalises each K head (RMS over hd, times the gain), rotates
-// the half-split pairs (i, i + hd/2) by pos * theta^(-2i/hd), rounds K and V
-// to bf16 and writes them to the request's cache slot.
+// The projection Y = H . W^T runs on the gfx950 32x32x16 bf16 MFMA with fp32
+// accumulation: 256 x 256 tiles (ik_proj; ik_proj_persist when there are more
+// unsplit tiles than CUs) for more than 256 rows, the weight-streaming GEMM of
+// the drafter forward (fg_run) up to 256 rows, and ik_gemm's smaller tiles when
+// the K/V blocks do not divide into 256 columns.  The epilogue normalises each
+// K head (RMS over hd, times the gain), rotates the half-split pairs
+// (i, i + hd/2) by pos * theta^(-2i/hd), rounds K and V to bf16 and writes them
+// to the request's cache slot: inside ik_proj when its tile needs no split over
+// d_in, otherwise in ik_finish (one workgroup per (row, layer)), which first
+// adds the splits' fp32 partials in a fixed order.
 #include "bd_common.hpp"
 #include "bd_gemm.hpp"
 #include "bd_launch.hpp"
