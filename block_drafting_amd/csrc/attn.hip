@@ -898,7 +898,10 @@ size_t attn_ws_bytes(int B, int K, int n_q, int n_kv, int hd, int max_ctx, int w
 template <int HD, int NW>
 static void run_partial(AttnArgs& a, size_t pref_bytes, hipStream_t stream) {
   const int resident = resident_partial<HD, NW>();
-  if (a.grid > resident) a.grid = resident;
+  // at most the resident workgroups, but never fewer than one group of n_kv
+  // (the head-synchronous schedule needs a workgroup per head; nothing waits on
+  // another workgroup, so workgroups beyond the resident ones simply run later)
+  if (a.grid > resident) a.grid = resident > a.n_kv ? resident : a.n_kv;
   hipLaunchKernelGGL((attn_partial<HD, NW>), dim3(a.grid), dim3(64 * NW), pref_bytes, stream, a);
 }
 
